@@ -1,0 +1,259 @@
+"""CPU oracle for the DeepSeek Sparse Attention forward path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It wraps the plain
+fp64 C implementation in ``dsa_oracle.c`` (built with gcc + OpenMP) and shares
+no code with the HIP library.
+
+Every function takes numpy arrays or CPU torch tensors holding the exact values
+the device receives (bf16 values are widened to float32, which is exact) and
+returns numpy arrays.
+
+Method source: the DeepSeek-V3.2 model documentation page, section "DeepSeek
+Sparse Attention (DSA)" (lightning indexer; top-index_topk token selection;
+MLA over the selected tokens; FP8 indexer behind a Hadamard rotation).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_SO = os.path.join(_HERE, "_dsa_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile dsa_oracle.c into _dsa_oracle.so with gcc (-O2 -fopenmp)."""
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        tmp = _SO + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_SO)
+            P = ctypes.c_void_p
+            I = ctypes.c_int
+            L = ctypes.c_long
+            D = ctypes.c_double
+            lib.orc_num_threads.restype = I
+            lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+            lib.orc_e4m3_decode.restype = D
+            lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+            lib.orc_e4m3_encode.restype = ctypes.c_uint8
+            lib.orc_e4m3_encode_array.argtypes = [L, P, P]
+            lib.orc_e4m3_encode_array.restype = None
+            lib.orc_hadamard_matrix.argtypes = [I, P]
+            lib.orc_rotate.argtypes = [L, I, P, P]
+            lib.orc_rotate_quant.argtypes = [L, I, P, P, P]
+            lib.orc_index_scores.argtypes = [I, I, I, I, I, P, P, P, P, L, P, P]
+            lib.orc_index_scores_fp8.argtypes = [I, I, I, I, I, P, P, P, P, P, P, L, P, P]
+            lib.orc_topk.argtypes = [I, I, I, I, P, L, P, P, P]
+            lib.orc_sparse_mla.argtypes = [I, I, I, I, I, I, I, D, P, P, L, P, P, P, P]
+            lib.orc_masked_dense_mla.argtypes = [I, I, I, I, I, I, I, D, P, P, P, L, P, P, P, P]
+            for f in ("orc_hadamard_matrix", "orc_rotate", "orc_rotate_quant", "orc_index_scores",
+                      "orc_index_scores_fp8", "orc_topk", "orc_sparse_mla", "orc_masked_dense_mla"):
+                getattr(lib, f).restype = None
+            _lib = lib
+    return _lib
+
+
+def _f32(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # torch tensor (CPU)
+        x = x.detach().to("cpu").float().numpy()
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _u8(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().to("cpu")
+        if x.dtype != torch.uint8:
+            x = x.view(torch.uint8)
+        x = x.numpy()
+    return np.ascontiguousarray(x, dtype=np.uint8)
+
+
+def _i32(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").numpy()
+    return np.ascontiguousarray(x, dtype=np.int32)
+
+
+def _rows(rows, n_all):
+    if rows is None:
+        return np.arange(n_all, dtype=np.int64)
+    return np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+# ---------------------------------------------------------------- fp8 codec
+def e4m3_decode(codes) -> np.ndarray:
+    lib = _load()
+    c = _u8(codes)
+    table = np.array([lib.orc_e4m3_decode(i) for i in range(256)], dtype=np.float64)
+    return table[c]
+
+
+def e4m3_encode(y) -> np.ndarray:
+    y = _f32(y)
+    out = np.empty(y.shape, dtype=np.uint8)
+    _load().orc_e4m3_encode_array(y.size, _p(y), _p(out))
+    return out
+
+
+# ------------------------------------------------------------ Hadamard / fp8
+def hadamard(D: int) -> np.ndarray:
+    H = np.empty((D, D), dtype=np.float64)
+    _load().orc_hadamard_matrix(D, _p(H))
+    return H
+
+
+def rotate(x) -> np.ndarray:
+    x = _f32(x)
+    D = x.shape[-1]
+    out = np.empty_like(x)
+    _load().orc_rotate(x.size // D, D, _p(x), _p(out))
+    return out
+
+
+def rotate_quant(x):
+    """Per-row Hadamard rotation + e4m3 quantisation -> (codes uint8, scales f32)."""
+    x = _f32(x)
+    D = x.shape[-1]
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    _load().orc_rotate_quant(x.size // D, D, _p(x), _p(codes), _p(scales))
+    return codes, scales
+
+
+def dequant(codes, scales) -> np.ndarray:
+    """decode(code) * scale in float64 (one scale per row of the last axis)."""
+    return e4m3_decode(codes) * _f32(scales).astype(np.float64)[..., None]
+
+
+# ------------------------------------------------------------------ indexer
+def index_scores(q_idx, w, k_idx, kv_len, rows=None) -> np.ndarray:
+    """q_idx [B,T,H,D], w [B,T,H], k_idx [B,Lmax,D], kv_len [B] -> [n_rows, Lmax] f32."""
+    q = _f32(q_idx)
+    w = _f32(w)
+    k = _f32(k_idx)
+    kl = _i32(kv_len)
+    B, T, H, D = q.shape
+    Lmax = k.shape[1]
+    r = _rows(rows, B * T)
+    out = np.empty((len(r), Lmax), dtype=np.float32)
+    _load().orc_index_scores(B, T, Lmax, H, D, _p(q), _p(w), _p(k), _p(kl), len(r), _p(r), _p(out))
+    return out
+
+
+def index_scores_fp8(q_codes, q_scale, w, k_codes, k_scale, kv_len, rows=None) -> np.ndarray:
+    qc = _u8(q_codes)
+    qs = _f32(q_scale)
+    w = _f32(w)
+    kc = _u8(k_codes)
+    ks = _f32(k_scale)
+    kl = _i32(kv_len)
+    B, T, H, D = qc.shape
+    Lmax = kc.shape[1]
+    r = _rows(rows, B * T)
+    out = np.empty((len(r), Lmax), dtype=np.float32)
+    _load().orc_index_scores_fp8(B, T, Lmax, H, D, _p(qc), _p(qs), _p(w), _p(kc), _p(ks), _p(kl),
+                                 len(r), _p(r), _p(out))
+    return out
+
+
+# -------------------------------------------------------------------- top-k
+def topk(scores, kv_len, T: int, K: int, rows=None) -> np.ndarray:
+    """scores [n_rows, Lmax] for query rows ``rows`` -> idx [n_rows, K] int32 (sorted, -1 padded)."""
+    s = _f32(scores)
+    kl = _i32(kv_len)
+    B = kl.shape[0]
+    Lmax = s.shape[1]
+    r = _rows(rows, B * T)
+    assert s.shape[0] == len(r)
+    idx = np.empty((len(r), K), dtype=np.int32)
+    _load().orc_topk(B, T, Lmax, K, _p(kl), len(r), _p(r), _p(s), _p(idx))
+    return idx
+
+
+# --------------------------------------------------------------- sparse MLA
+def sparse_mla(q, kv, idx, sm_scale: float, rows=None, v_dim: int | None = None):
+    """q [B,T,H,Dqk], kv [B,Lmax,Dqk], idx [n_rows,K] -> (out [n_rows,H,Dv] f64, lse [n_rows,H] f64)."""
+    q = _f32(q)
+    kv = _f32(kv)
+    ix = _i32(idx)
+    B, T, H, Dqk = q.shape
+    Lmax = kv.shape[1]
+    Dv = Dqk if v_dim is None else v_dim
+    r = _rows(rows, B * T)
+    K = ix.shape[-1]
+    ix = ix.reshape(len(r), K)
+    out = np.empty((len(r), H, Dv), dtype=np.float64)
+    lse = np.empty((len(r), H), dtype=np.float64)
+    _load().orc_sparse_mla(B, T, Lmax, H, Dqk, Dv, K, float(sm_scale), _p(q), _p(kv), len(r), _p(r),
+                           _p(ix), _p(out), _p(lse))
+    return out, lse
+
+
+def masked_dense_mla(q, kv, kv_len, idx, sm_scale: float, rows=None, v_dim: int | None = None):
+    """The additive-mask formulation of the same attention (dense logits + 0/-inf mask)."""
+    q = _f32(q)
+    kv = _f32(kv)
+    kl = _i32(kv_len)
+    ix = _i32(idx)
+    B, T, H, Dqk = q.shape
+    Lmax = kv.shape[1]
+    Dv = Dqk if v_dim is None else v_dim
+    r = _rows(rows, B * T)
+    K = ix.shape[-1]
+    ix = ix.reshape(len(r), K)
+    out = np.empty((len(r), H, Dv), dtype=np.float64)
+    lse = np.empty((len(r), H), dtype=np.float64)
+    _load().orc_masked_dense_mla(B, T, Lmax, H, Dqk, Dv, K, float(sm_scale), _p(q), _p(kv), _p(kl),
+                                 len(r), _p(r), _p(ix), _p(out), _p(lse))
+    return out, lse
+
+
+# -------------------------------------------------------------- whole path
+def forward(inp: dict, shape, rows=None) -> dict:
+    """The whole path on the listed query rows.
+
+    ``inp`` holds q_idx, w, k_idx (raw, pre-rotation), q, kv, kv_len.  With an fp8
+    indexer the oracle rotates and quantises q_idx and k_idx itself.  Returns
+    scores [n,Lmax] f32, idx [n,K] i32, out [n,H,Dv] f64, lse [n,H] f64 and, for
+    fp8, the codes and scales it used.
+    """
+    B, T = shape.batch, shape.n_q
+    r = _rows(rows, B * T)
+    res = {}
+    if shape.idx_dtype == "fp8":
+        qc, qs = rotate_quant(inp["q_idx"])
+        kc, ks = rotate_quant(inp["k_idx"])
+        res.update(q_codes=qc, q_scale=qs, k_codes=kc, k_scale=ks)
+        sc = index_scores_fp8(qc, qs, inp["w"], kc, ks, inp["kv_len"], rows=r)
+    else:
+        sc = index_scores(inp["q_idx"], inp["w"], inp["k_idx"], inp["kv_len"], rows=r)
+    idx = topk(sc, inp["kv_len"], T, shape.topk, rows=r)
+    out, lse = sparse_mla(inp["q"], inp["kv"], idx, shape.sm_scale, rows=r, v_dim=shape.v_dim)
+    res.update(scores=sc, idx=idx, out=out, lse=lse, rows=r)
+    return res

@@ -1,0 +1,146 @@
+"""Pins for the oracle's OCP e4m3fn codec and its Hadamard rotation.
+
+The FP8 indexer of the DeepSeek-V3.2 model documentation page ("DeepSeek Sparse
+Attention (DSA)", lightning indexer) rotates q and k by an orthogonal Hadamard
+transform before FP8, which leaves q.k unchanged.  The codec is checked against
+torch's own float8_e4m3fn conversion (a library routine) and against the
+format's definition; the rotation against orthogonality and an independent
+butterfly transform written here.
+"""
+import numpy as np
+import pytest
+import torch
+
+
+def test_decode_all_codes_match_torch(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    ours = orc.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def test_encode_roundtrips_every_finite_code(orc):
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = orc.e4m3_decode(codes).astype(np.float32)
+    assert np.array_equal(orc.e4m3_encode(vals), codes)
+
+
+def _neighbour_probes(orc):
+    pos = orc.e4m3_decode(np.arange(0x7F, dtype=np.uint8))  # 0 .. 448, increasing
+    assert np.all(np.diff(pos) > 0)
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)      # exact in fp32
+    probes = [pos.astype(np.float32), mids,
+              np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(-np.inf))]
+    rng = np.random.default_rng(0)
+    lo = pos[:-1]
+    hi = pos[1:]
+    for _ in range(40):
+        probes.append((lo + (hi - lo) * rng.random(lo.shape)).astype(np.float32))
+    y = np.concatenate(probes)
+    y = y[np.abs(y) <= 448.0]
+    return np.concatenate([y, -y])
+
+
+def test_encode_matches_torch_rne_on_grid_midpoints_and_between(orc):
+    y = _neighbour_probes(orc)
+    ours = orc.e4m3_encode(y)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_encode_matches_torch_on_random_sweep(orc):
+    rng = np.random.default_rng(1)
+    y = (rng.standard_normal(2_000_000) * np.exp(rng.uniform(-12, 6, 2_000_000))).astype(np.float32)
+    y = y[np.abs(y) <= 448.0]
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(orc.e4m3_encode(y), ref)
+
+
+def test_encode_ties_to_even_and_saturates(orc):
+    # 1.0625 lies halfway between 1.0 (mantissa 0, even) and 1.125 (mantissa 1).
+    assert orc.e4m3_encode(np.float32([1.0625]))[0] == 0x38
+    # 1.1875 lies halfway between 1.125 (odd) and 1.25 (even).
+    assert orc.e4m3_encode(np.float32([1.1875]))[0] == 0x3A
+    # half the smallest subnormal rounds to zero (even); just above it rounds up
+    tiny = np.float32(2.0 ** -10)
+    assert orc.e4m3_encode(np.float32([tiny]))[0] == 0x00
+    assert orc.e4m3_encode(np.float32([np.nextafter(tiny, np.float32(1))]))[0] == 0x01
+    big = orc.e4m3_encode(np.float32([449.0, 1e6, -1e30]))
+    assert list(big) == [0x7E, 0x7E, 0xFE]
+    assert orc.e4m3_encode(np.float32([-0.0]))[0] == 0x80
+
+
+@pytest.mark.parametrize("D", [2, 16, 32, 128, 256])
+def test_hadamard_is_orthonormal_and_symmetric(orc, D):
+    H = orc.hadamard(D)
+    assert np.allclose(H @ H.T, np.eye(D), atol=1e-12)
+    assert np.array_equal(H, H.T)
+    assert np.allclose(np.abs(H), D ** -0.5, atol=0)
+    e0 = np.zeros(D)
+    e0[0] = 1
+    assert np.allclose(H @ e0, np.full(D, D ** -0.5), atol=1e-15)
+
+
+def _fwht(x):
+    """Iterative butterfly (natural order), then the 1/sqrt(D) normalisation."""
+    x = np.array(x, dtype=np.float64)
+    D = x.shape[-1]
+    h = 1
+    while h < D:
+        y = x.reshape(*x.shape[:-1], D // (2 * h), 2, h)
+        a = y[..., 0, :].copy()
+        b = y[..., 1, :].copy()
+        y[..., 0, :] = a + b
+        y[..., 1, :] = a - b
+        x = y.reshape(*x.shape[:-1], D)
+        h *= 2
+    return x / np.sqrt(D)
+
+
+def test_rotation_equals_butterfly_transform(orc):
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((300, 128)).astype(np.float32)
+    ours = orc.rotate(x)
+    ref = _fwht(x.astype(np.float64)).astype(np.float32)
+    assert np.allclose(ours, ref, rtol=2.5e-7, atol=1e-12)
+    assert np.mean(ours == ref) > 0.999
+
+
+def test_rotation_leaves_index_scores_unchanged(orc):
+    # Hq . Hk = q . k  (orthogonality): scores on rotated operands equal the plain ones.
+    rng = np.random.default_rng(3)
+    B, T, H, D, L = 1, 16, 8, 128, 64
+    q = (rng.standard_normal((B, T, H, D)) / np.sqrt(D)).astype(np.float32)
+    k = (rng.standard_normal((B, L, D)) / np.sqrt(D)).astype(np.float32)
+    w = (rng.standard_normal((B, T, H)) / np.sqrt(H)).astype(np.float32)
+    kl = np.array([L], dtype=np.int32)
+    plain = orc.index_scores(q, w, k, kl)
+    rot = orc.index_scores(orc.rotate(q), w, orc.rotate(k), kl)
+    fin = np.isfinite(plain)
+    assert np.array_equal(fin, np.isfinite(rot))
+    rel = np.abs(plain[fin] - rot[fin]).max() / np.abs(plain[fin]).max()
+    assert rel < 1e-5
+
+
+def test_rotate_quant_properties(orc):
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((200, 128)) * np.exp(rng.standard_normal((200, 1)))).astype(np.float32)
+    x[7] = 0.0
+    codes, scales = orc.rotate_quant(x)
+    assert codes.dtype == np.uint8 and scales.shape == (200,)
+    assert np.all(codes[7] == 0) and scales[7] == 1.0
+    dec = orc.e4m3_decode(codes)
+    live = np.arange(200) != 7
+    # the largest rotated magnitude lands on +-448
+    assert np.all(np.abs(dec[live]).max(axis=1) == 448.0)
+    xr = orc.rotate(x).astype(np.float64)
+    amax = np.abs(xr).max(axis=1)
+    assert np.array_equal(scales[live], (amax[live] / 448.0).astype(np.float32))
+    # dequantised values are within half an e4m3 step of the rotated ones
+    deq = orc.dequant(codes, scales)
+    err = np.abs(deq - xr)[live]
+    assert np.all(err <= np.maximum(np.abs(xr[live]) * 2.0 ** -4, 2.0 ** -10 * amax[live, None] / 448 * 1.01))

@@ -58,11 +58,11 @@ def _load():
             lib.orc_hadamard_matrix.argtypes = [I, P]
             lib.orc_rotate.argtypes = [L, I, P, P]
             lib.orc_rotate_quant.argtypes = [L, I, P, P, P]
-            lib.orc_index_scores.argtypes = [I, I, I, I, I, P, P, P, P, L, P, P]
-            lib.orc_index_scores_fp8.argtypes = [I, I, I, I, I, P, P, P, P, P, P, L, P, P]
+            lib.orc_index_scores.argtypes = [I, I, I, I, I, P, P, P, P, L, P, I, P]
+            lib.orc_index_scores_fp8.argtypes = [I, I, I, I, I, P, P, P, P, P, P, L, P, I, P]
             lib.orc_topk.argtypes = [I, I, I, I, P, L, P, P, P]
-            lib.orc_sparse_mla.argtypes = [I, I, I, I, I, I, I, D, P, P, L, P, P, P, P]
-            lib.orc_masked_dense_mla.argtypes = [I, I, I, I, I, I, I, D, P, P, P, L, P, P, P, P]
+            lib.orc_sparse_mla.argtypes = [I, I, I, I, I, I, I, D, P, P, L, P, I, P, P, P]
+            lib.orc_masked_dense_mla.argtypes = [I, I, I, I, I, I, I, D, P, P, P, L, P, I, P, P, P]
             for f in ("orc_hadamard_matrix", "orc_rotate", "orc_rotate_quant", "orc_index_scores",
                       "orc_index_scores_fp8", "orc_topk", "orc_sparse_mla", "orc_masked_dense_mla"):
                 getattr(lib, f).restype = None
@@ -152,33 +152,47 @@ def dequant(codes, scales) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ indexer
-def index_scores(q_idx, w, k_idx, kv_len, rows=None) -> np.ndarray:
-    """q_idx [B,T,H,D], w [B,T,H], k_idx [B,Lmax,D], kv_len [B] -> [n_rows, Lmax] f32."""
+def index_scores(q_idx, w, k_idx, kv_len, rows=None, T=None) -> np.ndarray:
+    """q_idx [B,T,H,D], w [B,T,H], k_idx [B,Lmax,D], kv_len [B] -> [n_rows, Lmax] f32.
+
+    With ``T`` given, q_idx [n_rows,H,D] and w [n_rows,H] hold only the listed rows.
+    """
     q = _f32(q_idx)
     w = _f32(w)
     k = _f32(k_idx)
     kl = _i32(kv_len)
-    B, T, H, D = q.shape
+    compact = T is not None
+    B = kl.shape[0]
+    if compact:
+        _, H, D = q.shape
+    else:
+        _, T, H, D = q.shape
     Lmax = k.shape[1]
     r = _rows(rows, B * T)
     out = np.empty((len(r), Lmax), dtype=np.float32)
-    _load().orc_index_scores(B, T, Lmax, H, D, _p(q), _p(w), _p(k), _p(kl), len(r), _p(r), _p(out))
+    _load().orc_index_scores(B, T, Lmax, H, D, _p(q), _p(w), _p(k), _p(kl), len(r), _p(r), int(compact), _p(out))
     return out
 
 
-def index_scores_fp8(q_codes, q_scale, w, k_codes, k_scale, kv_len, rows=None) -> np.ndarray:
+def index_scores_fp8(q_codes, q_scale, w, k_codes, k_scale, kv_len, rows=None, T=None) -> np.ndarray:
+    """fp8 operands (codes + row scales); ``T`` as in index_scores."""
     qc = _u8(q_codes)
     qs = _f32(q_scale)
     w = _f32(w)
     kc = _u8(k_codes)
     ks = _f32(k_scale)
     kl = _i32(kv_len)
-    B, T, H, D = qc.shape
+    compact = T is not None
+    B = kl.shape[0]
+    if compact:
+        _, H, D = qc.shape
+    else:
+        _, T, H, D = qc.shape
     Lmax = kc.shape[1]
     r = _rows(rows, B * T)
     out = np.empty((len(r), Lmax), dtype=np.float32)
     _load().orc_index_scores_fp8(B, T, Lmax, H, D, _p(qc), _p(qs), _p(w), _p(kc), _p(ks), _p(kl),
-                                 len(r), _p(r), _p(out))
+                                 len(r), _p(r), int(compact), _p(out))
     return out
 
 
@@ -197,12 +211,20 @@ def topk(scores, kv_len, T: int, K: int, rows=None) -> np.ndarray:
 
 
 # --------------------------------------------------------------- sparse MLA
-def sparse_mla(q, kv, idx, sm_scale: float, rows=None, v_dim: int | None = None):
-    """q [B,T,H,Dqk], kv [B,Lmax,Dqk], idx [n_rows,K] -> (out [n_rows,H,Dv] f64, lse [n_rows,H] f64)."""
+def sparse_mla(q, kv, idx, sm_scale: float, rows=None, v_dim: int | None = None, T=None):
+    """q [B,T,H,Dqk], kv [B,Lmax,Dqk], idx [n_rows,K] -> (out [n_rows,H,Dv] f64, lse [n_rows,H] f64).
+
+    With ``T`` given, q [n_rows,H,Dqk] holds only the listed rows.
+    """
     q = _f32(q)
     kv = _f32(kv)
     ix = _i32(idx)
-    B, T, H, Dqk = q.shape
+    compact = T is not None
+    B = kv.shape[0]
+    if compact:
+        _, H, Dqk = q.shape
+    else:
+        _, T, H, Dqk = q.shape
     Lmax = kv.shape[1]
     Dv = Dqk if v_dim is None else v_dim
     r = _rows(rows, B * T)
@@ -211,7 +233,7 @@ def sparse_mla(q, kv, idx, sm_scale: float, rows=None, v_dim: int | None = None)
     out = np.empty((len(r), H, Dv), dtype=np.float64)
     lse = np.empty((len(r), H), dtype=np.float64)
     _load().orc_sparse_mla(B, T, Lmax, H, Dqk, Dv, K, float(sm_scale), _p(q), _p(kv), len(r), _p(r),
-                           _p(ix), _p(out), _p(lse))
+                           int(compact), _p(ix), _p(out), _p(lse))
     return out, lse
 
 
@@ -230,30 +252,32 @@ def masked_dense_mla(q, kv, kv_len, idx, sm_scale: float, rows=None, v_dim: int 
     out = np.empty((len(r), H, Dv), dtype=np.float64)
     lse = np.empty((len(r), H), dtype=np.float64)
     _load().orc_masked_dense_mla(B, T, Lmax, H, Dqk, Dv, K, float(sm_scale), _p(q), _p(kv), _p(kl),
-                                 len(r), _p(r), _p(ix), _p(out), _p(lse))
+                                 len(r), _p(r), 0, _p(ix), _p(out), _p(lse))
     return out, lse
 
 
 # -------------------------------------------------------------- whole path
-def forward(inp: dict, shape, rows=None) -> dict:
+def forward(inp: dict, shape, rows=None, compact: bool = False) -> dict:
     """The whole path on the listed query rows.
 
-    ``inp`` holds q_idx, w, k_idx (raw, pre-rotation), q, kv, kv_len.  With an fp8
-    indexer the oracle rotates and quantises q_idx and k_idx itself.  Returns
-    scores [n,Lmax] f32, idx [n,K] i32, out [n,H,Dv] f64, lse [n,H] f64 and, for
-    fp8, the codes and scales it used.
+    ``inp`` holds q_idx, w, k_idx (raw, pre-rotation), q, kv, kv_len.  With
+    ``compact`` the per-query tensors q_idx [n,H_I,D_I], w [n,H_I] and q [n,H,Dqk]
+    hold only the listed rows.  With an fp8 indexer the oracle rotates and
+    quantises q_idx and k_idx itself.  Returns scores [n,Lmax] f32, idx [n,K] i32,
+    out [n,H,Dv] f64, lse [n,H] f64 and, for fp8, the codes and scales it used.
     """
     B, T = shape.batch, shape.n_q
     r = _rows(rows, B * T)
+    Tc = T if compact else None
     res = {}
     if shape.idx_dtype == "fp8":
         qc, qs = rotate_quant(inp["q_idx"])
         kc, ks = rotate_quant(inp["k_idx"])
         res.update(q_codes=qc, q_scale=qs, k_codes=kc, k_scale=ks)
-        sc = index_scores_fp8(qc, qs, inp["w"], kc, ks, inp["kv_len"], rows=r)
+        sc = index_scores_fp8(qc, qs, inp["w"], kc, ks, inp["kv_len"], rows=r, T=Tc)
     else:
-        sc = index_scores(inp["q_idx"], inp["w"], inp["k_idx"], inp["kv_len"], rows=r)
+        sc = index_scores(inp["q_idx"], inp["w"], inp["k_idx"], inp["kv_len"], rows=r, T=Tc)
     idx = topk(sc, inp["kv_len"], T, shape.topk, rows=r)
-    out, lse = sparse_mla(inp["q"], inp["kv"], idx, shape.sm_scale, rows=r, v_dim=shape.v_dim)
+    out, lse = sparse_mla(inp["q"], inp["kv"], idx, shape.sm_scale, rows=r, v_dim=shape.v_dim, T=Tc)
     res.update(scores=sc, idx=idx, out=out, lse=lse, rows=r)
     return res

@@ -118,22 +118,24 @@ void orc_hadamard_matrix(int D, double* H)
             H[(size_t)i * D + j] = (popcount_u32((uint32_t)(i & j)) & 1) ? -s : s;
 }
 
-/* out[r] = fp32(H x[r]) for each row of length D. */
+/* out[r] = fp32(H x[r]) for each row of length D, with H = S / sqrt(D) and S
+ * the +-1 Sylvester matrix: the +-1 product is summed in double, then scaled
+ * once by 1/sqrt(D), so the irrational scale is not rounded into every term. */
 void orc_rotate(long rows, int D, const float* x, float* out)
 {
-    double* H = (double*)malloc(sizeof(double) * (size_t)D * D);
-    orc_hadamard_matrix(D, H);
+    const double scale = 1.0 / sqrt((double)D);
 #pragma omp parallel for schedule(static)
     for (long r = 0; r < rows; ++r) {
         const float* xr = x + (size_t)r * D;
         for (int i = 0; i < D; ++i) {
             double acc = 0.0;
-            for (int j = 0; j < D; ++j)
-                acc += H[(size_t)i * D + j] * (double)xr[j];
-            out[(size_t)r * D + i] = (float)acc;
+            for (int j = 0; j < D; ++j) {
+                int neg = popcount_u32((uint32_t)(i & j)) & 1;
+                acc += neg ? -(double)xr[j] : (double)xr[j];
+            }
+            out[(size_t)r * D + i] = (float)(acc * scale);
         }
     }
-    free(H);
 }
 
 /* Rotate, then quantise each row to e4m3 with one float scale per row:
@@ -172,8 +174,11 @@ void orc_rotate_quant(long rows, int D, const float* x, uint8_t* codes, float* s
 }
 
 /* ------------------------------------------------------------------ */
-/* Row lists.  A "row" is one query (b, t), numbered r = b * T + t.      */
-/* n_rows == 0 with rows == NULL means every row.                       */
+/* Row lists.  A "row" is one query (b, t), numbered r = b * T + t; the  */
+/* i-th listed row is rows[i] (rows == NULL lists every row in order).  */
+/* With compact != 0 the per-query inputs (q, w, codes, scales) hold     */
+/* only the listed rows, the i-th listed row at index i; keys, values and */
+/* kv_len are always whole.                                             */
 /* ------------------------------------------------------------------ */
 
 static long row_at(long i, const long* rows) { return rows ? rows[i] : i; }
@@ -184,7 +189,7 @@ static long row_at(long i, const long* rows) { return rows ? rows[i] : i; }
  *   -inf for s > p.  Accumulated in double, stored as fp32. */
 void orc_index_scores(int B, int T, int Lmax, int H, int D,
                       const float* q, const float* w, const float* k,
-                      const int* kv_len, long n_rows, const long* rows, float* out)
+                      const int* kv_len, long n_rows, const long* rows, int compact, float* out)
 {
     (void)B;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -192,8 +197,9 @@ void orc_index_scores(int B, int T, int Lmax, int H, int D,
         long r = row_at(i, rows);
         long b = r / T, t = r % T;
         long p = (long)kv_len[b] - T + t;
-        const float* qr = q + (size_t)r * H * D;
-        const float* wr = w + (size_t)r * H;
+        long qi = compact ? i : r;
+        const float* qr = q + (size_t)qi * H * D;
+        const float* wr = w + (size_t)qi * H;
         const float* kb = k + (size_t)b * Lmax * D;
         float* o = out + (size_t)i * Lmax;
         for (long s = 0; s < Lmax; ++s) {
@@ -220,7 +226,7 @@ void orc_index_scores(int B, int T, int Lmax, int H, int D,
 void orc_index_scores_fp8(int B, int T, int Lmax, int H, int D,
                           const uint8_t* qc, const float* qs, const float* w,
                           const uint8_t* kc, const float* ks,
-                          const int* kv_len, long n_rows, const long* rows, float* out)
+                          const int* kv_len, long n_rows, const long* rows, int compact, float* out)
 {
     (void)B;
     double table[256];
@@ -231,11 +237,12 @@ void orc_index_scores_fp8(int B, int T, int Lmax, int H, int D,
         long r = row_at(i, rows);
         long b = r / T, t = r % T;
         long p = (long)kv_len[b] - T + t;
+        long qi = compact ? i : r;
         double* qd = (double*)malloc(sizeof(double) * (size_t)H * D);
         for (int h = 0; h < H; ++h)
             for (int d = 0; d < D; ++d)
-                qd[(size_t)h * D + d] = table[qc[((size_t)r * H + h) * D + d]] * (double)qs[(size_t)r * H + h];
-        const float* wr = w + (size_t)r * H;
+                qd[(size_t)h * D + d] = table[qc[((size_t)qi * H + h) * D + d]] * (double)qs[(size_t)qi * H + h];
+        const float* wr = w + (size_t)qi * H;
         float* o = out + (size_t)i * Lmax;
         for (long s = 0; s < Lmax; ++s) {
             if (s > p) {
@@ -311,7 +318,7 @@ void orc_topk(int B, int T, int Lmax, int K, const int* kv_len,
 /* ------------------------------------------------------------------ */
 
 void orc_sparse_mla(int B, int T, int Lmax, int H, int Dqk, int Dv, int K, double sm_scale,
-                    const float* q, const float* kv, long n_rows, const long* rows,
+                    const float* q, const float* kv, long n_rows, const long* rows, int compact,
                     const int* idx, double* out, double* lse)
 {
     (void)B;
@@ -323,7 +330,7 @@ void orc_sparse_mla(int B, int T, int Lmax, int H, int Dqk, int Dv, int K, doubl
         const float* kvb = kv + (size_t)b * Lmax * Dqk;
         double* z = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
         for (int h = 0; h < H; ++h) {
-            const float* qh = q + ((size_t)r * H + h) * Dqk;
+            const float* qh = q + ((size_t)(compact ? i : r) * H + h) * Dqk;
             double* o = out + ((size_t)i * H + h) * Dv;
             double m = -INFINITY;
             for (int j = 0; j < K; ++j) {
@@ -363,7 +370,7 @@ void orc_sparse_mla(int B, int T, int Lmax, int H, int Dqk, int Dv, int K, doubl
  * then a softmax over all of them.  Must agree with orc_sparse_mla. */
 void orc_masked_dense_mla(int B, int T, int Lmax, int H, int Dqk, int Dv, int K, double sm_scale,
                           const float* q, const float* kv, const int* kv_len,
-                          long n_rows, const long* rows, const int* idx,
+                          long n_rows, const long* rows, int compact, const int* idx,
                           double* out, double* lse)
 {
     (void)B;
@@ -383,7 +390,7 @@ void orc_masked_dense_mla(int B, int T, int Lmax, int H, int Dqk, int Dv, int K,
             if (ir[j] >= 0 && ir[j] < n)
                 mask[ir[j]] = 0.0;
         for (int h = 0; h < H; ++h) {
-            const float* qh = q + ((size_t)r * H + h) * Dqk;
+            const float* qh = q + ((size_t)(compact ? i : r) * H + h) * Dqk;
             double* o = out + ((size_t)i * H + h) * Dv;
             double m = -INFINITY;
             for (long s = 0; s < n; ++s) {

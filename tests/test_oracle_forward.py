@@ -80,3 +80,16 @@ def test_golden_fixture_tiny(orc):
         assert sorted(res["idx"][i][res["idx"][i] >= 0].tolist()) == g["idx_sorted"][str(r)]
         assert np.allclose(res["lse"][i], g["lse"][str(r)], rtol=0, atol=1e-12)
         assert np.allclose(res["out"][i].sum(axis=-1), g["out_rowsum"][str(r)], rtol=0, atol=1e-12)
+
+
+def test_compact_rows_equal_full_rows(orc):
+    # compact inputs (only the listed query rows) give the same results as full inputs
+    wl = get("tiny_f32").replace(batch=2, max_kv=300, kv_len=280)
+    inp = make_inputs(wl)
+    rows = [3, 255, 256, 400, 511]
+    full = orc.forward(inp, wl, rows=rows)
+    flat = lambda t: t.reshape(wl.rows, *t.shape[2:])[rows]
+    cin = dict(inp, q_idx=flat(inp["q_idx"]), w=flat(inp["w"]), q=flat(inp["q"]))
+    comp = orc.forward(cin, wl, rows=rows, compact=True)
+    for k in ("scores", "idx", "out", "lse"):
+        assert np.array_equal(full[k], comp[k]), k

@@ -1,0 +1,248 @@
+"""DSA forward throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode_32k|prefill_32k|decode_128k_fp8|...]
+
+A step is one dsa_forward call (fp8 workloads: q rotation + quantisation,
+index scores, top-k, sparse MLA) over one batch of synthetic inputs already
+resident in HBM.  Decode workloads alternate between two independent input
+sets so that consecutive steps cannot be served from the 256 MB Infinity Cache.
+After the timed forward loop, a second timed loop calls the stage entry points
+(same launch configurations) with HIP events between them to get per-kernel
+durations; the dominant kernel is reported against its roofline.  The CPU
+oracle is timed on a bounded sample of the same workload on the host cores.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA fwd queries/sec at L=32K/128K + % of MFMA peak / HBM GB/s"
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+DEFAULT_STEPS = {"decode_32k": 100, "decode_128k_fp8": 100, "prefill_32k": 10, "prefill_4k": 50, "tiny_f32": 100}
+
+
+def algorithmic(wl) -> dict:
+    """Work the method must do per forward, stage by stage (masked work not counted)."""
+    B, T, L, K = wl.batch, wl.n_q, wl.kv_len, wl.topk
+    HI, DI, H, Dqk, Dv = wl.idx_heads, wl.idx_dim, wl.heads, wl.qk_dim, wl.v_dim
+    ib = 1 if wl.idx_dtype == "fp8" else (4 if wl.idx_dtype == "f32" else 2)
+    mb = 4 if wl.mla_dtype == "f32" else 2
+    pairs = 0      # causal (query, key) pairs scored
+    sel = 0        # selected (query, key) pairs attended
+    for t in range(T):
+        n = L - T + t + 1
+        pairs += n
+        sel += min(K, n)
+    pairs *= B
+    sel *= B
+    key_bytes = B * L * DI * ib + (B * L * 4 if wl.idx_dtype == "fp8" else 0)
+    idx_flops = 2.0 * pairs * HI * DI
+    idx_bytes = key_bytes + B * T * HI * (DI * ib + 4 + (4 if wl.idx_dtype == "fp8" else 0)) + pairs * 4
+    topk_bytes = pairs * 4 + B * T * K * 4
+    mla_flops = 2.0 * sel * H * (Dqk + Dv)
+    gather = sel * Dqk * mb if T == 1 else B * L * Dqk * mb  # prefill rows come from L2 after first touch
+    mla_bytes = gather + B * T * H * (Dqk * mb + Dv * mb + 4) + sel * 4
+    return dict(indexer=dict(flops=idx_flops, bytes=idx_bytes), topk=dict(flops=0.0, bytes=topk_bytes),
+                mla=dict(flops=mla_flops, bytes=mla_bytes))
+
+
+def dominant(wl, stage_us: dict) -> tuple[str, dict]:
+    """The longest stage and its roofline object."""
+    alg = algorithmic(wl)
+    name = max(("indexer", "topk", "mla"), key=lambda k: stage_us.get(k, 0.0))
+    us = stage_us[name]
+    a = alg[name]
+    dt = wl.idx_dtype if name == "indexer" else wl.mla_dtype
+    ai = a["flops"] / max(a["bytes"], 1.0)
+    ridge = PEAK_TFLOPS.get(dt, PEAK_TFLOPS["bf16"]) * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if name != "topk" and ai > ridge:
+        achieved = a["flops"] / (us * 1e-6) / 1e12
+        peak = PEAK_TFLOPS[dt]
+        return name, {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                      "work_per_launch": a["flops"], "avg_launch_us": round(us, 2)}
+    achieved = a["bytes"] / (us * 1e-6) / 1e9
+    return name, {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                  "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                  "work_per_launch": a["bytes"], "avg_launch_us": round(us, 2)}
+
+
+class Case:
+    """Device inputs, outputs and workspace of one workload."""
+
+    def __init__(self, dsa, wl, seed, torch):
+        from workloads import make_inputs
+        self.wl = wl
+        self.shape = dsa.DsaShape.of(wl)
+        inp = make_inputs(wl, device="cuda", seed=seed)
+        self.inp = inp
+        self.k_idx, self.k_scale = inp["k_idx"], None
+        if wl.idx_dtype == "fp8":
+            self.k_idx, self.k_scale = dsa.rotate_quant_fp8(inp["k_idx"])
+            del inp["k_idx"]
+            q_codes, q_scale = dsa.rotate_quant_fp8(inp["q_idx"])
+            self.q_codes, self.q_scale = q_codes, q_scale
+        dev = "cuda"
+        B, T = wl.batch, wl.n_q
+        self.idx = torch.empty((B, T, wl.topk), dtype=torch.int32, device=dev)
+        mdt = torch.float32 if wl.mla_dtype == "f32" else torch.bfloat16
+        self.out = torch.empty((B, T, wl.heads, wl.v_dim), dtype=mdt, device=dev)
+        self.lse = torch.empty((B, T, wl.heads), dtype=torch.float32, device=dev)
+        self.ws = torch.empty((dsa.forward_workspace_size(self.shape),), dtype=torch.uint8, device=dev)
+        self.scores = None
+
+    def forward(self, dsa):
+        i = self.inp
+        dsa.forward(self.shape, i["q_idx"], i["w"], self.k_idx, i["q"], i["kv"], i["kv_len"], k_scale=self.k_scale,
+                    idx_out=self.idx, out=self.out, lse=self.lse, workspace=self.ws)
+
+
+def time_forward(dsa, torch, cases, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for s in range(warmup):
+        cases[s % len(cases)].forward(dsa)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    t0 = time.perf_counter()
+    for s in range(steps):
+        cases[s % len(cases)].forward(dsa)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_stages(dsa, torch, cases, steps):
+    """Per-stage durations through the stage entry points (events on the launch stream)."""
+    stream = torch.cuda.current_stream()
+    wl = cases[0].wl
+    sh = cases[0].shape
+    B, T, Lmax = wl.batch, wl.n_q, wl.max_kv
+    if wl.n_q > 1 and B * T * Lmax * 4 > (6 << 30):
+        return None  # the stage API writes the whole masked score matrix; skip huge prefill shapes
+    for c in cases:
+        if c.scores is None:
+            c.scores = torch.empty((B, T, Lmax), dtype=torch.float32, device="cuda")
+        c.mla_ws = torch.empty((max(dsa.sparse_mla_workspace_size(sh), 1),), dtype=torch.uint8, device="cuda")
+    names = ["indexer", "topk", "mla"]
+    acc = {n: 0.0 for n in names}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for rep in range(steps + 2):
+        c = cases[rep % len(cases)]
+        i = c.inp
+        qi = c.q_codes if wl.idx_dtype == "fp8" else i["q_idx"]
+        ev[0].record(stream)
+        dsa.index_scores(sh, qi, i["w"], c.k_idx, i["kv_len"], q_scale=getattr(c, "q_scale", None),
+                         k_scale=c.k_scale, scores=c.scores)
+        ev[1].record(stream)
+        dsa.topk(sh, c.scores, i["kv_len"], idx=c.idx)
+        ev[2].record(stream)
+        dsa.sparse_mla_fwd(sh, i["q"], i["kv"], c.idx, i["kv_len"], out=c.out, lse=c.lse, workspace=c.mla_ws)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        if rep >= 2:
+            for k, n in enumerate(names):
+                acc[n] += ev[k].elapsed_time(ev[k + 1]) * 1000.0
+    return {n: acc[n] / steps for n in names}
+
+
+def cpu_baseline(wl, budget_rows: int | None = None) -> dict:
+    """The oracle, as it stands, on a bounded sample of the workload (host cores)."""
+    import numpy as np
+
+    import oracle
+    from workloads import make_inputs
+    oracle.build()
+    threads = oracle.num_threads()
+    if wl.n_q == 1:
+        n = budget_rows or min(wl.batch, max(2, threads))
+        seqs = list(range(n))
+        sub = wl.replace(batch=n)
+        inp = make_inputs(sub, seqs=seqs)
+        rows = list(range(n))
+        t0 = time.perf_counter()
+        oracle.forward(inp, sub, rows=rows)
+        dt = time.perf_counter() - t0
+        sample = f"{n} of {wl.batch} sequences (one decode query each, full {wl.kv_len}-token context)"
+    else:
+        n = budget_rows or max(2, threads)
+        rng = np.random.default_rng(0)
+        rows = sorted(rng.choice(wl.rows, size=n, replace=False).tolist())
+        inp = make_inputs(wl)
+        flat = lambda t: t.reshape(wl.rows, *t.shape[2:])[rows]
+        cin = dict(inp, q_idx=flat(inp["q_idx"]), w=flat(inp["w"]), q=flat(inp["q"]))
+        t0 = time.perf_counter()
+        oracle.forward(cin, wl, rows=rows, compact=True)
+        dt = time.perf_counter() - t0
+        sample = f"{n} uniformly drawn query rows of {wl.rows}"
+    return {"value": round(len(rows) / dt, 3), "unit": "queries/s", "cores": min(threads, len(rows)),
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 2)}
+
+
+def run(args) -> dict:
+    import torch
+
+    import sparse_attention_09_amd as dsa
+    from workloads import get
+
+    wl = get(args.workload)
+    steps = args.steps if args.steps is not None else DEFAULT_STEPS.get(wl.name, 20)
+    warmup = args.warmup
+    n_sets = 2 if wl.n_q == 1 else 1
+    cases = [Case(dsa, wl, seed, torch) for seed in range(n_sets)]
+    torch.cuda.synchronize()
+    ms, wall = time_forward(dsa, torch, cases, steps, warmup)
+    queries = wl.batch * wl.n_q
+    res = {
+        "metric": METRIC, "value": round(queries / (ms * 1e-3), 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.mla_dtype if wl.idx_dtype != "fp8" else "fp8+bf16",
+        "data": "synthetic (seeded Gaussian, DeepSeek-V3.2 shapes)",
+        "config": {"workload": wl.name, "batch": wl.batch, "queries_per_seq": wl.n_q, "context": wl.kv_len,
+                   "index_heads": wl.idx_heads, "index_dim": wl.idx_dim, "topk": wl.topk, "heads": wl.heads,
+                   "qk_dim": wl.qk_dim, "v_dim": wl.v_dim, "idx_dtype": wl.idx_dtype, "mla_dtype": wl.mla_dtype,
+                   "input_sets": n_sets},
+        "wall_s": round(wall, 4),
+    }
+    if not args.no_stages:
+        st = time_stages(dsa, torch, cases, max(5, min(steps, 50)))
+        if st is not None:
+            res["stages_us"] = {k: round(v, 2) for k, v in st.items()}
+            _, roof = dominant(wl, st)
+            res["roofline"] = roof
+    del cases
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_32k")
+    ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    print(json.dumps(run(args)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

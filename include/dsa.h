@@ -1,0 +1,166 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek Sparse Attention forward path.
+ *
+ * What it computes (DeepSeek-V3.2 model documentation page, section "DeepSeek
+ * Sparse Attention (DSA)"):
+ *   1. lightning indexer: an index score between each query and every previous
+ *      key of a single-head index-key cache of width index_head_dim (item 1 and
+ *      the paragraph on the indexer key cache).  Score form:
+ *          I[t,s] = sum_h w[t,h] * relu(q_idx[t,h,:] . k_idx[s,:]);
+ *      with an FP8 indexer both operands are e4m3 codes of Hadamard-rotated
+ *      vectors with one fp32 scale per row (the rotation is orthogonal, so the
+ *      scores are those of the unrotated vectors up to quantisation);
+ *   2. fine-grained token selection: each query keeps its top index_topk
+ *      tokens (item 2);
+ *   3. MLA attention only over the selected tokens (item 2), in absorbed-latent
+ *      form: one latent row [c_kv (v_dim) | k_rope] per token is the key of all
+ *      heads and its first v_dim columns are the value; the output is the
+ *      v_dim-wide latent per head plus its log-sum-exp.
+ * Each layer runs its own indexer (the page's note on per-layer indexers): the
+ * library keeps no state between calls.
+ *
+ * Conventions shared by every entry point
+ *   - Sequence b holds kv_len[b] tokens (device int32 array); its T queries are
+ *     its last T tokens: query t sits at position p(t) = L_b - T + t with
+ *     L_b = min(kv_len[b], max_kv), and sees keys s = 0 .. p(t), itself included.
+ *     A row with p(t) < 0 sees nothing (scores all -inf, indices all -1,
+ *     output 0, lse -inf).  kv_len is not read on the host.
+ *   - Tensors are dense, row-major, innermost dimension contiguous, with base
+ *     pointers aligned to 16 bytes.  Every pointer except the shape is a device
+ *     pointer.  The caller allocates and owns every buffer, the workspace
+ *     included; the library allocates nothing and holds no state.
+ *   - Every call only enqueues work on `stream` and returns; it never waits.
+ *     Argument errors are found on the host before anything is enqueued and
+ *     return a negative status with nothing written.  A failed launch returns
+ *     DSA_ERR_HIP.  Two calls may share a workspace only if they are ordered.
+ *   - bf16 is the 16-bit brain float; fp8 is the OCP E4M3FN format (bias 7,
+ *     largest finite 448, no infinities).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA_F32 = 0,
+    DSA_BF16 = 1,
+    DSA_FP8_E4M3 = 2
+} dsa_dtype;
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_NULL = -1,        /* a required pointer is NULL                         */
+    DSA_ERR_SHAPE = -2,       /* a size is <= 0 or inconsistent (e.g. T > max_kv)    */
+    DSA_ERR_DTYPE = -3,       /* dtype value or combination not accepted             */
+    DSA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                    */
+    DSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required             */
+    DSA_ERR_UNSUPPORTED = -6, /* valid but not built (a head width, a head count)    */
+    DSA_ERR_HIP = -7          /* the HIP runtime reported an error on launch         */
+} dsa_status;
+
+/* Problem description.  Dtype fields hold dsa_dtype values. */
+typedef struct {
+    int32_t batch;      /* B  sequences                                             */
+    int32_t n_q;        /* T  queries per sequence (1 for decode)                   */
+    int32_t max_kv;     /* L_max  cache capacity (rows of k_idx / kv per sequence)  */
+    int32_t idx_heads;  /* H_I  index_n_heads, 1..64                                */
+    int32_t idx_dim;    /* D_I  index_head_dim                                      */
+    int32_t topk;       /* K  index_topk, 1..4096                                   */
+    int32_t heads;      /* H  MLA query heads, >= 1                                 */
+    int32_t qk_dim;     /* D_qk = kv_lora_rank + qk_rope_head_dim (key width)       */
+    int32_t v_dim;      /* D_v  = kv_lora_rank (value = first D_v columns of a row) */
+    float sm_scale;     /* softmax scale applied to q . k; no default               */
+    int32_t idx_dtype;  /* DSA_F32 | DSA_BF16 | DSA_FP8_E4M3                         */
+    int32_t mla_dtype;  /* DSA_F32 | DSA_BF16                                        */
+} dsa_shape;
+
+/*
+ * Supported sizes (anything else returns DSA_ERR_UNSUPPORTED):
+ *   indexer  idx_dtype F32: idx_dim in {32, 64, 128};  BF16 / FP8: idx_dim = 128;
+ *            idx_heads 1..64 (padded internally to 16 or 64).
+ *   MLA      (mla_dtype, qk_dim, v_dim) in {(F32, 80, 64), (BF16, 576, 512),
+ *            (BF16, 192, 128)}; any heads >= 1 (padded to groups of 16).
+ *   top-k    topk <= 4096, max_kv <= 1 << 20.
+ */
+
+/* Lightning-indexer scores.
+ *   q_idx  [B,T,H_I,D_I]  idx_dtype (fp8: e4m3 codes, uint8)
+ *   q_scale[B,T,H_I] f32  fp8 only: dequantisation scale of each q_idx row (else NULL)
+ *   w      [B,T,H_I] f32  per-head weights of the head sum
+ *   k_idx  [B,L_max,D_I]  idx_dtype (fp8: codes)
+ *   k_scale[B,L_max] f32  fp8 only: scale of each k_idx row (else NULL)
+ *   kv_len [B] int32
+ *   scores [B,T,L_max] f32 out: I[t,s] for s <= p(t), -inf for every other s.
+ * fp8: I[t,s] = k_scale[s] * sum_h w[t,h] q_scale[t,h] relu(code(q_h) . code(k_s)). */
+dsa_status dsa_index_scores(const dsa_shape* shape, const void* q_idx, const float* q_scale,
+                            const float* w, const void* k_idx, const float* k_scale,
+                            const int32_t* kv_len, float* scores, hipStream_t stream);
+
+/* Per-query top-k (page item 2).
+ *   scores [B,T,L_max] f32 (only s <= p(t) is read), kv_len [B] int32
+ *   idx    [B,T,K] int32 out: the k_eff = min(K, p(t)+1) positions with the
+ *          largest scores, ties broken towards the smaller position, written in
+ *          ascending position order, followed by K - k_eff entries of -1.
+ *          -0.0 counts as equal to +0.0; NaN scores are not supported.
+ *   workspace / ws_bytes: at least dsa_topk_workspace_size(shape) bytes. */
+size_t dsa_topk_workspace_size(const dsa_shape* shape);
+dsa_status dsa_topk(const dsa_shape* shape, const float* scores, const int32_t* kv_len,
+                    int32_t* idx, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Sparse absorbed-latent MLA over given index sets (page item 2).
+ *   q   [B,T,H,D_qk]  mla_dtype    kv [B,L_max,D_qk] mla_dtype
+ *   idx [B,T,K] int32: entries outside [0, L_b) are skipped; duplicates count twice
+ *   out [B,T,H,D_v] mla_dtype out: sum_j softmax_j(z) kv[idx_j, :D_v] with
+ *       z_j = sm_scale * q . kv[idx_j]
+ *   lse [B,T,H] f32 out (may be NULL): natural-log log-sum-exp of z
+ *   A (b,t) with no valid entry gets out = 0 and lse = -inf.
+ *   workspace / ws_bytes: at least dsa_sparse_mla_workspace_size(shape) bytes. */
+size_t dsa_sparse_mla_workspace_size(const dsa_shape* shape);
+dsa_status dsa_sparse_mla_fwd(const dsa_shape* shape, const void* q, const void* kv,
+                              const int32_t* idx, const int32_t* kv_len, void* out, float* lse,
+                              void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Per-row Hadamard rotation + e4m3 quantisation (the FP8 indexer's operand
+ * preparation, page item 1):  x' = H x with H the Sylvester Hadamard matrix
+ * scaled by 1/sqrt(dim), rounded to fp32; amax = max|x'|; if amax == 0 the codes
+ * are 0 and the scale 1, else codes = e4m3_rne(fp32(x' * fp32(448 / amax))) and
+ * scale = fp32(amax / 448).
+ *   x      [rows, dim]  x_dtype (DSA_F32 or DSA_BF16), dim a power of two, 16..256
+ *   codes  [rows, dim]  uint8 out;  scales [rows] f32 out. */
+dsa_status dsa_rotate_quant_fp8(int64_t rows, int32_t dim, const void* x, int32_t x_dtype,
+                                uint8_t* codes, float* scales, hipStream_t stream);
+
+/* The whole path: (fp8 only) rotate + quantise q_idx, index scores, top-k,
+ * sparse MLA.
+ *   q_idx  [B,T,H_I,D_I]: idx_dtype for F32/BF16; for FP8 it is the unrotated
+ *          BF16 query, rotated and quantised inside the call
+ *   w, kv_len, q, kv as above; k_idx / k_scale as in dsa_index_scores (for FP8
+ *   the ready e4m3 cache and its row scales, e.g. from dsa_rotate_quant_fp8)
+ *   idx_out [B,T,K] int32 out, or NULL to keep the selection in the workspace
+ *   out, lse as in dsa_sparse_mla_fwd.
+ *   workspace (256-byte aligned): dsa_forward_workspace_size(shape) bytes run
+ *   every query in one pass; any size >= dsa_forward_min_workspace_size(shape)
+ *   works, the queries then being processed in the largest chunk of
+ *   ceil(T / 2^k) queries whose buffers fit. */
+size_t dsa_forward_workspace_size(const dsa_shape* shape);
+size_t dsa_forward_min_workspace_size(const dsa_shape* shape);
+dsa_status dsa_forward(const dsa_shape* shape, const void* q_idx, const float* w,
+                       const void* k_idx, const float* k_scale, const void* q, const void* kv,
+                       const int32_t* kv_len, int32_t* idx_out, void* out, float* lse,
+                       void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Static text for a status value. */
+const char* dsa_status_string(dsa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,10 @@
+"""MI355X-native DeepSeek Sparse Attention (DSA) forward path.
+
+The compute lives in libdsa.so (hand-written HIP for gfx950 behind the C ABI in
+include/dsa.h); this package is its thin Python binding.
+"""
+from ._lib import (  # noqa: F401
+    BF16, F32, FP8_E4M3, LIB_PATH, DsaError, DsaShape, forward, forward_min_workspace_size,
+    forward_workspace_size, index_scores, lib, rotate_quant_fp8, sparse_mla_fwd, sparse_mla_workspace_size, topk,
+    topk_workspace_size,
+)

@@ -1,0 +1,362 @@
+// dsa_api.hip -- C ABI of the DSA forward path (declared in include/dsa.h).
+//
+// Host side only: argument validation (before anything is enqueued), workspace
+// carving, query chunking for long prefill and the launch sequence of the
+// gfx950 kernels.  Nothing here computes any step of the method.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "dsa.h"
+#include "dsa_kernels.h"
+
+#define DSA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxTopk = 4096;
+constexpr int kMaxKv = 1 << 20;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+dsa_status check_common(const dsa_shape* s)
+{
+    if (!s) return DSA_ERR_NULL;
+    if (s->batch <= 0 || s->n_q <= 0 || s->max_kv <= 0) return DSA_ERR_SHAPE;
+    if (s->n_q > s->max_kv) return DSA_ERR_SHAPE;
+    if (s->max_kv > kMaxKv) return DSA_ERR_UNSUPPORTED;
+    return DSA_OK;
+}
+
+dsa_status check_indexer_shape(const dsa_shape* s)
+{
+    if (s->idx_heads <= 0 || s->idx_dim <= 0) return DSA_ERR_SHAPE;
+    if (s->idx_dtype != DSA_F32 && s->idx_dtype != DSA_BF16 && s->idx_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
+    if (!dsa::indexer_supported(s->idx_dtype, s->idx_dim, s->idx_heads)) return DSA_ERR_UNSUPPORTED;
+    return DSA_OK;
+}
+
+dsa_status check_topk_shape(const dsa_shape* s)
+{
+    if (s->topk <= 0) return DSA_ERR_SHAPE;
+    if (s->topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
+    return DSA_OK;
+}
+
+dsa_status check_mla_shape(const dsa_shape* s)
+{
+    if (s->heads <= 0 || s->qk_dim <= 0 || s->v_dim <= 0 || s->topk <= 0) return DSA_ERR_SHAPE;
+    if (s->v_dim > s->qk_dim) return DSA_ERR_SHAPE;
+    if (!isfinite(s->sm_scale)) return DSA_ERR_SHAPE;
+    if (s->mla_dtype != DSA_F32 && s->mla_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (s->topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
+    if (!dsa::mla_supported(s->mla_dtype, s->qk_dim, s->v_dim)) return DSA_ERR_UNSUPPORTED;
+    return DSA_OK;
+}
+
+dsa_status ptr_ok(const void* p, size_t align)
+{
+    if (!p) return DSA_ERR_NULL;
+    if (!aligned(p, align)) return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+#define DSA_TRY(x)                        \
+    do {                                  \
+        dsa_status st_ = (x);             \
+        if (st_ != DSA_OK) return st_;    \
+    } while (0)
+
+dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+dsa::IndexerArgs indexer_args(const dsa_shape* s, const void* q, const float* qs, const float* w, const void* k,
+                              const float* ks, const int32_t* kv_len, float* scores, int t_begin, int t_count,
+                              int fill)
+{
+    dsa::IndexerArgs a;
+    a.B = s->batch;
+    a.T = s->n_q;
+    a.Lmax = s->max_kv;
+    a.H = s->idx_heads;
+    a.D = s->idx_dim;
+    a.t_begin = t_begin;
+    a.t_count = t_count;
+    a.q = q;
+    a.q_scale = qs;
+    a.w = w;
+    a.k = k;
+    a.k_scale = ks;
+    a.kv_len = kv_len;
+    a.scores = scores;
+    a.ld_t = s->max_kv;
+    a.ld_b = (long long)t_count * s->max_kv;
+    a.fill = fill;
+    return a;
+}
+
+dsa::TopkArgs topk_args(const dsa_shape* s, const float* scores, const int32_t* kv_len, int32_t* idx, int t_begin,
+                        int t_count)
+{
+    dsa::TopkArgs a;
+    a.B = s->batch;
+    a.T = s->n_q;
+    a.Lmax = s->max_kv;
+    a.K = s->topk;
+    a.t_begin = t_begin;
+    a.t_count = t_count;
+    a.scores = scores;
+    a.ld_t = s->max_kv;
+    a.ld_b = (long long)t_count * s->max_kv;
+    a.kv_len = kv_len;
+    a.idx = idx;
+    return a;
+}
+
+dsa::MlaArgs mla_args(const dsa_shape* s, const void* q, const void* kv, const int32_t* idx, const int32_t* kv_len,
+                      void* out, float* lse, float* part, int t_begin, int t_count, int n_split)
+{
+    dsa::MlaArgs a;
+    a.B = s->batch;
+    a.T = s->n_q;
+    a.Lmax = s->max_kv;
+    a.H = s->heads;
+    a.Dqk = s->qk_dim;
+    a.Dv = s->v_dim;
+    a.K = s->topk;
+    a.t_begin = t_begin;
+    a.t_count = t_count;
+    a.sm_scale = s->sm_scale;
+    a.q = q;
+    a.kv = kv;
+    a.idx = idx;
+    a.kv_len = kv_len;
+    a.out = out;
+    a.lse = lse;
+    a.part = part;
+    a.n_split = n_split;
+    return a;
+}
+
+size_t mla_ws(const dsa_shape* s, int t_count)
+{
+    const int ns = dsa::mla_split_count(s->batch, t_count, s->heads, s->topk);
+    return dsa::mla_partial_bytes(s->batch, t_count, s->heads, s->v_dim, ns);
+}
+
+// Workspace layout of dsa_forward for a query chunk of tc rows.
+struct FwdLayout {
+    size_t qcodes = 0, qscale = 0, idx = 0, scores = 0, part = 0, total = 0;
+};
+
+FwdLayout fwd_layout(const dsa_shape* s, int tc, bool own_idx)
+{
+    FwdLayout l;
+    size_t off = 0;
+    const size_t BT = (size_t)s->batch * s->n_q;
+    if (s->idx_dtype == DSA_FP8_E4M3) {
+        l.qcodes = off;
+        off += align_up(BT * s->idx_heads * s->idx_dim);
+        l.qscale = off;
+        off += align_up(BT * s->idx_heads * sizeof(float));
+    }
+    if (own_idx) {
+        l.idx = off;
+        off += align_up(BT * s->topk * sizeof(int32_t));
+    }
+    l.scores = off;
+    off += align_up((size_t)s->batch * tc * s->max_kv * sizeof(float));
+    l.part = off;
+    off += align_up(mla_ws(s, tc));
+    l.total = off;
+    return l;
+}
+
+dsa_status check_forward_shape(const dsa_shape* s)
+{
+    DSA_TRY(check_common(s));
+    DSA_TRY(check_indexer_shape(s));
+    DSA_TRY(check_topk_shape(s));
+    DSA_TRY(check_mla_shape(s));
+    return DSA_OK;
+}
+
+// Query-chunk candidates: T, ceil(T/2), ceil(T/4), ..., 1.  The workspace of a
+// chunk is not monotone in its size (smaller chunks split the index list more),
+// so the smallest workspace is the minimum over the candidates.
+int next_chunk(int tc) { return tc <= 1 ? 0 : (tc + 1) / 2; }
+
+size_t min_forward_ws(const dsa_shape* s, bool own_idx)
+{
+    size_t best = (size_t)-1;
+    for (int tc = s->n_q; tc > 0; tc = next_chunk(tc)) {
+        const size_t w = fwd_layout(s, tc, own_idx).total;
+        if (w < best) best = w;
+    }
+    return best;
+}
+
+}  // namespace
+
+DSA_EXPORT const char* dsa_status_string(dsa_status st)
+{
+    switch (st) {
+        case DSA_OK: return "ok";
+        case DSA_ERR_NULL: return "a required pointer is NULL";
+        case DSA_ERR_SHAPE: return "invalid or inconsistent sizes";
+        case DSA_ERR_DTYPE: return "dtype value or combination not accepted";
+        case DSA_ERR_ALIGN: return "pointer not aligned";
+        case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+        case DSA_ERR_UNSUPPORTED: return "sizes valid but not supported by the built kernels";
+        case DSA_ERR_HIP: return "HIP runtime error on launch";
+    }
+    return "unknown status";
+}
+
+DSA_EXPORT dsa_status dsa_index_scores(const dsa_shape* s, const void* q_idx, const float* q_scale, const float* w,
+                                       const void* k_idx, const float* k_scale, const int32_t* kv_len,
+                                       float* scores, hipStream_t stream)
+{
+    DSA_TRY(check_common(s));
+    DSA_TRY(check_indexer_shape(s));
+    DSA_TRY(ptr_ok(q_idx, 16));
+    DSA_TRY(ptr_ok(k_idx, 16));
+    DSA_TRY(ptr_ok(w, 4));
+    DSA_TRY(ptr_ok(kv_len, 4));
+    DSA_TRY(ptr_ok(scores, 4));
+    if (s->idx_dtype == DSA_FP8_E4M3) {
+        DSA_TRY(ptr_ok(q_scale, 4));
+        DSA_TRY(ptr_ok(k_scale, 4));
+    }
+    const dsa::IndexerArgs a =
+        indexer_args(s, q_idx, q_scale, w, k_idx, k_scale, kv_len, scores, 0, s->n_q, /*fill=*/1);
+    return hip_status(dsa::launch_indexer(s->idx_dtype, a, stream));
+}
+
+DSA_EXPORT size_t dsa_topk_workspace_size(const dsa_shape* s)
+{
+    if (check_common(s) != DSA_OK || check_topk_shape(s) != DSA_OK) return 0;
+    return dsa::topk_workspace_bytes(s->batch, s->n_q, s->max_kv, s->topk);
+}
+
+DSA_EXPORT dsa_status dsa_topk(const dsa_shape* s, const float* scores, const int32_t* kv_len, int32_t* idx,
+                               void* workspace, size_t ws_bytes, hipStream_t stream)
+{
+    DSA_TRY(check_common(s));
+    DSA_TRY(check_topk_shape(s));
+    DSA_TRY(ptr_ok(scores, 4));
+    DSA_TRY(ptr_ok(kv_len, 4));
+    DSA_TRY(ptr_ok(idx, 4));
+    const size_t need = dsa::topk_workspace_bytes(s->batch, s->n_q, s->max_kv, s->topk);
+    if (need > 0 && (!workspace || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+    const dsa::TopkArgs a = topk_args(s, scores, kv_len, idx, 0, s->n_q);
+    return hip_status(dsa::launch_topk(a, stream));
+}
+
+DSA_EXPORT size_t dsa_sparse_mla_workspace_size(const dsa_shape* s)
+{
+    if (check_common(s) != DSA_OK || check_mla_shape(s) != DSA_OK) return 0;
+    return mla_ws(s, s->n_q);
+}
+
+DSA_EXPORT dsa_status dsa_sparse_mla_fwd(const dsa_shape* s, const void* q, const void* kv, const int32_t* idx,
+                                         const int32_t* kv_len, void* out, float* lse, void* workspace,
+                                         size_t ws_bytes, hipStream_t stream)
+{
+    DSA_TRY(check_common(s));
+    DSA_TRY(check_mla_shape(s));
+    DSA_TRY(ptr_ok(q, 16));
+    DSA_TRY(ptr_ok(kv, 16));
+    DSA_TRY(ptr_ok(idx, 4));
+    DSA_TRY(ptr_ok(kv_len, 4));
+    DSA_TRY(ptr_ok(out, 16));
+    if (lse && !aligned(lse, 4)) return DSA_ERR_ALIGN;
+    const int ns = dsa::mla_split_count(s->batch, s->n_q, s->heads, s->topk);
+    const size_t need = dsa::mla_partial_bytes(s->batch, s->n_q, s->heads, s->v_dim, ns);
+    if (need > 0) {
+        if (!workspace || ws_bytes < need) return DSA_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return DSA_ERR_ALIGN;
+    }
+    const dsa::MlaArgs a = mla_args(s, q, kv, idx, kv_len, out, lse, (float*)workspace, 0, s->n_q, ns);
+    return hip_status(dsa::launch_mla(s->mla_dtype, a, stream));
+}
+
+DSA_EXPORT dsa_status dsa_rotate_quant_fp8(int64_t rows, int32_t dim, const void* x, int32_t x_dtype,
+                                           uint8_t* codes, float* scales, hipStream_t stream)
+{
+    if (rows <= 0 || dim <= 0) return DSA_ERR_SHAPE;
+    if (x_dtype != DSA_F32 && x_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (dim < 16 || dim > 256 || (dim & (dim - 1)) != 0) return DSA_ERR_UNSUPPORTED;
+    DSA_TRY(ptr_ok(x, 4));
+    DSA_TRY(ptr_ok(codes, 1));
+    DSA_TRY(ptr_ok(scales, 4));
+    return hip_status(dsa::launch_rotate_quant(rows, dim, x, x_dtype, codes, scales, stream));
+}
+
+DSA_EXPORT size_t dsa_forward_workspace_size(const dsa_shape* s)
+{
+    if (check_forward_shape(s) != DSA_OK) return 0;
+    return fwd_layout(s, s->n_q, true).total;
+}
+
+DSA_EXPORT size_t dsa_forward_min_workspace_size(const dsa_shape* s)
+{
+    if (check_forward_shape(s) != DSA_OK) return 0;
+    return min_forward_ws(s, true);
+}
+
+DSA_EXPORT dsa_status dsa_forward(const dsa_shape* s, const void* q_idx, const float* w, const void* k_idx,
+                                  const float* k_scale, const void* q, const void* kv, const int32_t* kv_len,
+                                  int32_t* idx_out, void* out, float* lse, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream)
+{
+    DSA_TRY(check_forward_shape(s));
+    DSA_TRY(ptr_ok(q_idx, 16));
+    DSA_TRY(ptr_ok(w, 4));
+    DSA_TRY(ptr_ok(k_idx, 16));
+    DSA_TRY(ptr_ok(q, 16));
+    DSA_TRY(ptr_ok(kv, 16));
+    DSA_TRY(ptr_ok(kv_len, 4));
+    DSA_TRY(ptr_ok(out, 16));
+    if (s->idx_dtype == DSA_FP8_E4M3) DSA_TRY(ptr_ok(k_scale, 4));
+    if (idx_out && !aligned(idx_out, 4)) return DSA_ERR_ALIGN;
+    if (lse && !aligned(lse, 4)) return DSA_ERR_ALIGN;
+    if (!workspace) return DSA_ERR_WORKSPACE;
+    if (!aligned(workspace, kAlign)) return DSA_ERR_ALIGN;
+
+    const bool own_idx = idx_out == nullptr;
+    // largest query chunk whose workspace fits
+    int tc = s->n_q;
+    while (tc > 0 && fwd_layout(s, tc, own_idx).total > ws_bytes) tc = next_chunk(tc);
+    if (tc == 0) return DSA_ERR_WORKSPACE;
+    const FwdLayout lay = fwd_layout(s, tc, own_idx);
+
+    char* ws = (char*)workspace;
+    int32_t* idx = own_idx ? (int32_t*)(ws + lay.idx) : idx_out;
+    float* scores = (float*)(ws + lay.scores);
+    float* part = (float*)(ws + lay.part);
+    const void* qi = q_idx;
+    const float* qsc = nullptr;
+    if (s->idx_dtype == DSA_FP8_E4M3) {
+        uint8_t* qc = (uint8_t*)(ws + lay.qcodes);
+        float* qs = (float*)(ws + lay.qscale);
+        const int64_t rows = (int64_t)s->batch * s->n_q * s->idx_heads;
+        hipError_t e = dsa::launch_rotate_quant(rows, s->idx_dim, q_idx, DSA_BF16, qc, qs, stream);
+        if (e != hipSuccess) return DSA_ERR_HIP;
+        qi = qc;
+        qsc = qs;
+    }
+    for (int t0 = 0; t0 < s->n_q; t0 += tc) {
+        const int cnt = (s->n_q - t0) < tc ? (s->n_q - t0) : tc;
+        const dsa::IndexerArgs ia = indexer_args(s, qi, qsc, w, k_idx, k_scale, kv_len, scores, t0, cnt, 0);
+        if (dsa::launch_indexer(s->idx_dtype, ia, stream) != hipSuccess) return DSA_ERR_HIP;
+        const dsa::TopkArgs ta = topk_args(s, scores, kv_len, idx, t0, cnt);
+        if (dsa::launch_topk(ta, stream) != hipSuccess) return DSA_ERR_HIP;
+        const int ns = dsa::mla_split_count(s->batch, cnt, s->heads, s->topk);
+        const dsa::MlaArgs ma = mla_args(s, q, kv, idx, kv_len, out, lse, part, t0, cnt, ns);
+        if (dsa::launch_mla(s->mla_dtype, ma, stream) != hipSuccess) return DSA_ERR_HIP;
+    }
+    return DSA_OK;
+}

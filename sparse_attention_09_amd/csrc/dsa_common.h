@@ -1,0 +1,107 @@
+// dsa_common.h -- device helpers shared by the gfx950 kernels of the DSA path.
+//
+// MFMA lane layouts used throughout (wave64; checked on the hardware):
+//   v_mfma_f32_16x16x32_bf16 / _16x16x32_fp8_fp8 / _16x16x4f32
+//     A (16 x K): lane l holds row l%16, k-block l/16 (8, 8 or 1 elements)
+//     B (K x 16): lane l holds column l%16, the same k-block
+//     C (16 x 16): lane l holds column l%16, rows 4*(l/16) + 0..3
+// Because a product sums over k, any fixed assignment of the contraction index
+// to (k-block, slot) works as long as A and B use the same one; the kernels
+// use that freedom to keep each lane's share of a row contiguous in memory.
+//
+// ds_read_b64_tr_b16 (gfx950): inside every 16-lane group, lane i receives
+// element j (j = 0..3) from the address supplied by lane 4*j + i/4 of its group,
+// at 16-bit offset i%4.  Handing it rows of a row-major tile gives a lane the
+// column-wise (contraction-major) operand of a value matrix.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum DType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// 16-byte global load / store through plain vector accesses.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_fp8(u32x2 a, u32x2 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b), c,
+                                                      0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Order-preserving map of fp32 onto uint32 (larger float -> larger key);
+// -0.0 is folded onto +0.0 first.
+__device__ __forceinline__ uint32_t float_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// Sum / max over the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group4_sum(float v)
+{
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+__device__ __forceinline__ float group4_max(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+}  // namespace dsa

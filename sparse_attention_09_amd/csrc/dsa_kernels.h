@@ -1,0 +1,67 @@
+// dsa_kernels.h -- internal launch interface between the C ABI layer and the
+// gfx950 kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Lightning-indexer scores for queries [t_begin, t_begin + t_count) of every
+// sequence.  Output row of (b, t) starts at scores + b * ld_b + (t - t_begin) * ld_t.
+struct IndexerArgs {
+    int B, T, Lmax, H, D;
+    int t_begin, t_count;
+    const void* q;          // [B,T,H,D] (rows of the full query tensor)
+    const float* q_scale;   // [B,T,H] fp8 only
+    const float* w;         // [B,T,H]
+    const void* k;          // [B,Lmax,D]
+    const float* k_scale;   // [B,Lmax] fp8 only
+    const int32_t* kv_len;  // [B]
+    float* scores;
+    long long ld_b, ld_t;
+    int fill;               // write -inf for every s > p(t)
+};
+
+// Top-k over score rows laid out as in IndexerArgs; writes idx rows of the full
+// [B,T,K] tensor for queries [t_begin, t_begin + t_count).
+struct TopkArgs {
+    int B, T, Lmax, K;
+    int t_begin, t_count;
+    const float* scores;
+    long long ld_b, ld_t;
+    const int32_t* kv_len;
+    int32_t* idx;
+};
+
+// Sparse absorbed MLA for queries [t_begin, t_begin + t_count).
+struct MlaArgs {
+    int B, T, Lmax, H, Dqk, Dv, K;
+    int t_begin, t_count;
+    float sm_scale;
+    const void* q;          // [B,T,H,Dqk]
+    const void* kv;         // [B,Lmax,Dqk]
+    const int32_t* idx;     // [B,T,K]
+    const int32_t* kv_len;  // [B]
+    void* out;              // [B,T,H,Dv]
+    float* lse;             // [B,T,H] or null
+    float* part;            // split partials (workspace) or null
+    int n_split;
+};
+
+bool indexer_supported(int dtype, int D, int H);
+hipError_t launch_indexer(int dtype, const IndexerArgs& a, hipStream_t s);
+
+size_t topk_workspace_bytes(int B, int T, int Lmax, int K);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+bool mla_supported(int dtype, int Dqk, int Dv);
+int mla_split_count(int B, int t_count, int H, int K);
+size_t mla_partial_bytes(int B, int t_count, int H, int Dv, int n_split);
+hipError_t launch_mla(int dtype, const MlaArgs& a, hipStream_t s);
+
+hipError_t launch_rotate_quant(int64_t rows, int dim, const void* x, int x_dtype, uint8_t* codes, float* scales,
+                               hipStream_t s);
+
+}  // namespace dsa

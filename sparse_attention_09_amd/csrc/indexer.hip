@@ -1,0 +1,337 @@
+// indexer.hip -- lightning-indexer scores on gfx950 MFMA.
+//
+// DeepSeek-V3.2 model documentation, "DeepSeek Sparse Attention (DSA)", item 1:
+// every query is scored against every previous key of a single-head index-key
+// cache (width index_head_dim).  Score form used: I[t,s] = sum_h w[t,h] *
+// relu(q[t,h,:] . k[s,:]); with an FP8 indexer the operands are e4m3 codes and
+// I[t,s] = k_scale[s] * sum_h (w[t,h] q_scale[t,h]) relu(codes . codes), which
+// equals the dequantised product because relu is positively homogeneous.
+//
+// Contraction on MFMA with heads on the M axis (16-head tiles) and keys on N
+// (16-key tiles), d on K.  In the C tile a lane holds one key and four heads,
+// so relu + the weighted head sum run in-lane, followed by one sum over the
+// four 16-lane groups.  Scores stay fp32 from the accumulator on.
+//
+// Two tilings of the same arithmetic:
+//   decode  (few queries, long cache): each wave owns a strip of 16-key tiles
+//           and streams them straight from HBM into registers, all loads of a
+//           strip issued before any MFMA (HBM-bound, no LDS, no barriers);
+//   prefill (many queries): 4 waves x 2 queries share 64-key tiles staged in
+//           LDS (double buffered through registers), so each key row leaves L2
+//           once per 8 queries; blocks are issued longest-row first.
+#include "dsa_common.h"
+#include "dsa_kernels.h"
+
+namespace dsa {
+namespace {
+
+template <int DT> struct ElemBytes;
+template <> struct ElemBytes<kF32> { static constexpr int v = 4; };
+template <> struct ElemBytes<kBF16> { static constexpr int v = 2; };
+template <> struct ElemBytes<kFP8> { static constexpr int v = 1; };
+
+// A lane's contiguous share of one D-wide row: D/4 elements = NCH 16-byte chunks.
+template <int DT, int D> struct Share {
+    static constexpr int bytes = D * ElemBytes<DT>::v / 4;
+    static constexpr int nch = bytes / 16;
+    static_assert(bytes % 16 == 0, "row share must be whole 16-byte chunks");
+};
+
+// acc += A_share . B_share over the lane-contiguous contraction mapping.
+template <int DT, int NCH>
+__device__ __forceinline__ f32x4 dot_share(const u32x4 (&a)[NCH], const u32x4 (&b)[NCH], f32x4 acc)
+{
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        if constexpr (DT == kBF16) {
+            acc = mfma_bf16(a[c], b[c], acc);
+        } else if constexpr (DT == kFP8) {
+            acc = mfma_fp8(u32x2{a[c][0], a[c][1]}, u32x2{b[c][0], b[c][1]}, acc);
+            acc = mfma_fp8(u32x2{a[c][2], a[c][3]}, u32x2{b[c][2], b[c][3]}, acc);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc = mfma_f32(__uint_as_float(a[c][e]), __uint_as_float(b[c][e]), acc);
+        }
+    }
+    return acc;
+}
+
+// Load query rows (A operand) and the weights of the heads whose scores this
+// lane holds in the C tile.  Heads beyond H read as zero weight and zero query.
+template <int DT, int D, int HT>
+__device__ __forceinline__ void load_query(const IndexerArgs& a, int b, int t, bool valid,
+                                           u32x4 (&qa)[HT][Share<DT, D>::nch], float (&wv)[HT][4])
+{
+    constexpr int NCH = Share<DT, D>::nch;
+    constexpr int EB = ElemBytes<DT>::v;
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const size_t qrow = ((size_t)b * a.T + t) * a.H;
+#pragma unroll
+    for (int m = 0; m < HT; ++m) {
+        const int h = 16 * m + n;
+        const bool ok = valid && h < a.H;
+        const char* src = (const char*)a.q + ((qrow + (ok ? h : 0)) * D) * EB + g * Share<DT, D>::bytes;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) qa[m][c] = ok ? ld16(src + 16 * c) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hh = 16 * m + 4 * g + i;
+            float wt = 0.f;
+            if (valid && hh < a.H) {
+                wt = a.w[qrow + hh];
+                if constexpr (DT == kFP8) wt *= a.q_scale[qrow + hh];
+            }
+            wv[m][i] = wt;
+        }
+    }
+}
+
+template <int HT>
+__device__ __forceinline__ float head_sum(const f32x4 (&acc)[HT], const float (&wv)[HT][4])
+{
+    float v = 0.f;
+#pragma unroll
+    for (int m = 0; m < HT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaf(wv[m][i], fmaxf(acc[m][i], 0.f), v);
+    return group4_sum(v);
+}
+
+__device__ __forceinline__ int seq_len(const IndexerArgs& a, int b)
+{
+    const int L = a.kv_len[b];
+    return L < a.Lmax ? L : a.Lmax;
+}
+
+// ---------------------------------------------------------------- decode tiling
+template <int DT, int D, int HT, int QPW, int TPW>
+__global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a)
+{
+    constexpr int NCH = Share<DT, D>::nch;
+    constexpr int EB = ElemBytes<DT>::v;
+    constexpr int CHUNK = 4 * TPW * 16;
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const int wave = threadIdx.x >> 6;
+    const int b = blockIdx.z;
+    const int L = seq_len(a, b);
+    const int chunk0 = blockIdx.x * CHUNK;
+
+    int tq[QPW], pq[QPW];
+    bool vq[QPW];
+    int kend = 0;
+#pragma unroll
+    for (int q = 0; q < QPW; ++q) {
+        tq[q] = a.t_begin + blockIdx.y * QPW + q;
+        vq[q] = tq[q] < a.t_begin + a.t_count;
+        pq[q] = vq[q] ? L - a.T + tq[q] : -1;
+        kend = max(kend, pq[q] + 1);
+    }
+
+    u32x4 qa[QPW][HT][NCH];
+    float wv[QPW][HT][4];
+#pragma unroll
+    for (int q = 0; q < QPW; ++q) load_query<DT, D, HT>(a, b, vq[q] ? tq[q] : a.t_begin, vq[q], qa[q], wv[q]);
+
+    // Issue every key load of this wave's strip first.
+    u32x4 kb[TPW][NCH];
+    const char* kbase = (const char*)a.k + (size_t)b * a.Lmax * D * EB + g * Share<DT, D>::bytes;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int key = chunk0 + 16 * (wave + 4 * i) + n;
+        const bool ok = key < kend;
+        const char* src = kbase + (size_t)(ok ? key : 0) * D * EB;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) kb[i][c] = ok ? ld16(src + 16 * c) : u32x4{0, 0, 0, 0};
+    }
+
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int tile = chunk0 + 16 * (wave + 4 * i);
+        const int key = tile + n;
+        if (tile < kend) {
+            float ks = 1.f;
+            if constexpr (DT == kFP8) ks = (key < kend && g == 0) ? a.k_scale[(size_t)b * a.Lmax + key] : 0.f;
+#pragma unroll
+            for (int q = 0; q < QPW; ++q) {
+                f32x4 acc[HT];
+#pragma unroll
+                for (int m = 0; m < HT; ++m) acc[m] = dot_share<DT, NCH>(qa[q][m], kb[i], f32x4{0, 0, 0, 0});
+                const float v = head_sum<HT>(acc, wv[q]);
+                if (g == 0 && vq[q] && key < a.Lmax) {
+                    float* dst = a.scores + b * a.ld_b + (long long)(tq[q] - a.t_begin) * a.ld_t + key;
+                    if (key <= pq[q])
+                        *dst = v * ks;
+                    else if (a.fill)
+                        *dst = -INFINITY;
+                }
+            }
+        } else if (a.fill && g == 0) {
+#pragma unroll
+            for (int q = 0; q < QPW; ++q)
+                if (vq[q] && key < a.Lmax)
+                    a.scores[b * a.ld_b + (long long)(tq[q] - a.t_begin) * a.ld_t + key] = -INFINITY;
+        }
+    }
+}
+
+// --------------------------------------------------------------- prefill tiling
+constexpr int kPrefillQPW = 2;
+constexpr int kPrefillTK = 64;  // keys per LDS tile
+
+template <int DT, int D, int HT>
+__global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs a)
+{
+    constexpr int QPW = kPrefillQPW;
+    constexpr int QPB = 4 * QPW;
+    constexpr int TK = kPrefillTK;
+    constexpr int NCH = Share<DT, D>::nch;
+    constexpr int EB = ElemBytes<DT>::v;
+    constexpr int ROWB = D * EB;          // bytes of a key row
+    constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
+    constexpr int PITCH = ROWB + 16;      // padded LDS row pitch (conflict-free 16-lane reads)
+    constexpr int NLD = TK * CPR / 256;   // chunks each thread stages per tile
+    static_assert(NLD >= 1 && (TK * CPR) % 256 == 0, "tile must split evenly over 256 threads");
+    __shared__ __attribute__((aligned(16))) char smem[2][TK * PITCH];
+
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const int wave = threadIdx.x >> 6;
+    const int b = blockIdx.y;
+    const int qb = gridDim.x - 1 - blockIdx.x;  // longest rows first
+    const int L = seq_len(a, b);
+    const int t_end = a.t_begin + a.t_count;
+    const int t0 = a.t_begin + qb * QPB;
+    const int t_last = min(t0 + QPB, t_end) - 1;
+    const int kend_blk = max(0, min(a.Lmax, L - a.T + t_last + 1));
+
+    int tq[QPW], pq[QPW];
+    bool vq[QPW];
+    int kend_w = 0;
+#pragma unroll
+    for (int q = 0; q < QPW; ++q) {
+        tq[q] = t0 + wave * QPW + q;
+        vq[q] = tq[q] < t_end;
+        pq[q] = vq[q] ? L - a.T + tq[q] : -1;
+        kend_w = max(kend_w, pq[q] + 1);
+    }
+    u32x4 qa[QPW][HT][NCH];
+    float wv[QPW][HT][4];
+#pragma unroll
+    for (int q = 0; q < QPW; ++q) load_query<DT, D, HT>(a, b, vq[q] ? tq[q] : a.t_begin, vq[q], qa[q], wv[q]);
+
+    const char* kbase = (const char*)a.k + (size_t)b * a.Lmax * ROWB;
+    const int ntile = (kend_blk + TK - 1) / TK;
+    u32x4 st[NLD];
+    auto fetch = [&](int tile) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int c = threadIdx.x + 256 * i;
+            const int row = tile * TK + c / CPR;
+            st[i] = row < kend_blk ? ld16(kbase + (size_t)row * ROWB + (c % CPR) * 16) : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int c = threadIdx.x + 256 * i;
+            *reinterpret_cast<u32x4*>(&smem[buf][(c / CPR) * PITCH + (c % CPR) * 16]) = st[i];
+        }
+    };
+
+    if (ntile > 0) {
+        fetch(0);
+        stash(0);
+    }
+    __syncthreads();
+    for (int it = 0; it < ntile; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < ntile) fetch(it + 1);
+        const int tile0 = it * TK;
+        if (tile0 < kend_w) {
+#pragma unroll
+            for (int sub = 0; sub < TK / 16; ++sub) {
+                const int kb0 = tile0 + 16 * sub;
+                if (kb0 < kend_w) {
+                    u32x4 kb[NCH];
+                    const char* rowp = &smem[buf][(16 * sub + n) * PITCH + g * Share<DT, D>::bytes];
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) kb[c] = *reinterpret_cast<const u32x4*>(rowp + 16 * c);
+                    const int key = kb0 + n;
+                    float ks = 1.f;
+                    if constexpr (DT == kFP8) ks = (g == 0 && key < kend_blk) ? a.k_scale[(size_t)b * a.Lmax + key] : 0.f;
+#pragma unroll
+                    for (int q = 0; q < QPW; ++q) {
+                        f32x4 acc[HT];
+#pragma unroll
+                        for (int m = 0; m < HT; ++m) acc[m] = dot_share<DT, NCH>(qa[q][m], kb, f32x4{0, 0, 0, 0});
+                        const float v = head_sum<HT>(acc, wv[q]);
+                        if (g == 0 && key <= pq[q])
+                            a.scores[b * a.ld_b + (long long)(tq[q] - a.t_begin) * a.ld_t + key] = v * ks;
+                    }
+                }
+            }
+        }
+        if (it + 1 < ntile) stash(buf ^ 1);
+        __syncthreads();
+    }
+
+    if (a.fill) {
+#pragma unroll
+        for (int q = 0; q < QPW; ++q) {
+            if (!vq[q]) continue;
+            float* row = a.scores + b * a.ld_b + (long long)(tq[q] - a.t_begin) * a.ld_t;
+            for (int s = max(pq[q] + 1, 0) + lane; s < a.Lmax; s += 64) row[s] = -INFINITY;
+        }
+    }
+}
+
+template <int DT, int D, int HT>
+hipError_t launch_dt(const IndexerArgs& a, hipStream_t s)
+{
+    if (a.t_count <= 0 || a.B <= 0) return hipSuccess;
+    if (a.t_count <= 2) {
+        if (a.t_count == 1) {
+            constexpr int TPW = (Share<DT, D>::nch <= 2) ? 16 : 8;
+            constexpr int CHUNK = 4 * TPW * 16;
+            dim3 grid((a.Lmax + CHUNK - 1) / CHUNK, a.t_count, a.B);
+            indexer_decode_kernel<DT, D, HT, 1, TPW><<<grid, 256, 0, s>>>(a);
+        } else {
+            constexpr int TPW = (Share<DT, D>::nch <= 2) ? 8 : 4;
+            constexpr int CHUNK = 4 * TPW * 16;
+            dim3 grid((a.Lmax + CHUNK - 1) / CHUNK, 1, a.B);
+            indexer_decode_kernel<DT, D, HT, 2, TPW><<<grid, 256, 0, s>>>(a);
+        }
+    } else {
+        constexpr int QPB = 4 * kPrefillQPW;
+        dim3 grid((a.t_count + QPB - 1) / QPB, a.B);
+        indexer_prefill_kernel<DT, D, HT><<<grid, 256, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_heads(const IndexerArgs& a, hipStream_t s)
+{
+    return a.H <= 16 ? launch_dt<DT, D, 1>(a, s) : launch_dt<DT, D, 4>(a, s);
+}
+
+}  // namespace
+
+bool indexer_supported(int dtype, int D, int H)
+{
+    if (H < 1 || H > 64) return false;
+    if (dtype == kF32) return D == 32 || D == 64 || D == 128;
+    if (dtype == kBF16 || dtype == kFP8) return D == 128;
+    return false;
+}
+
+hipError_t launch_indexer(int dtype, const IndexerArgs& a, hipStream_t s)
+{
+    if (dtype == kBF16) return launch_heads<kBF16, 128>(a, s);
+    if (dtype == kFP8) return launch_heads<kFP8, 128>(a, s);
+    if (a.D == 32) return launch_heads<kF32, 32>(a, s);
+    if (a.D == 64) return launch_heads<kF32, 64>(a, s);
+    return launch_heads<kF32, 128>(a, s);
+}
+
+}  // namespace dsa

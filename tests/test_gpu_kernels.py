@@ -1,0 +1,215 @@
+"""GPU parity of each entry point against the CPU oracle (same seeded inputs).
+
+Entry points: dsa_rotate_quant_fp8, dsa_index_scores, dsa_topk,
+dsa_sparse_mla_fwd, all called through the C ABI.  Integer-valued inputs make
+the indexer exact on both sides (bit-for-bit comparison); Gaussian inputs are
+compared at the dtype tolerance; top-k is compared exactly on shared score rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import TOL, announce, rel_rowmax
+from workloads import get, make_inputs, make_scores
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def shape_of(dsa, **kw):
+    base = dict(batch=1, n_q=1, max_kv=64, idx_heads=64, idx_dim=128, topk=64, heads=128, qk_dim=576, v_dim=512,
+                sm_scale=1 / 192 ** 0.5, idx_dtype="bf16", mla_dtype="bf16")
+    base.update(kw)
+    return dsa.DsaShape(**base)
+
+
+# ------------------------------------------------------------ rotate + quantise
+@pytest.mark.parametrize("dim", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("xdt", [torch.bfloat16, torch.float32])
+def test_rotate_quant_codes_and_scales_exact(dsa, orc, dim, xdt):
+    g = torch.Generator().manual_seed(dim)
+    x = torch.randn(2000, dim, generator=g) * torch.exp(0.5 * torch.randn(2000, 1, generator=g))
+    x[3] = 0
+    x[7] = 0
+    x[7, 5] = -3e-3
+    x[11] *= 1e-6
+    x = x.to(xdt)
+    codes, scales = dsa.rotate_quant_fp8(x.to(DEV))
+    torch.cuda.synchronize()
+    oc, os_ = orc.rotate_quant(x)
+    gc = codes.cpu().numpy()
+    bad = int((gc != oc).sum())
+    assert bad == 0, f"{bad} codes differ"
+    assert np.array_equal(scales.cpu().numpy(), os_)
+
+
+# ------------------------------------------------------------------- indexer
+def _int_inputs(B, T, H, D, Lmax, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randint(-3, 4, (B, T, H, D), generator=g).float()
+    k = torch.randint(-3, 4, (B, Lmax, D), generator=g).float()
+    w = torch.randint(-4, 5, (B, T, H), generator=g).float()
+    return q, w, k
+
+
+@pytest.mark.parametrize("dt,D,H", [("f32", 32, 4), ("f32", 64, 64), ("f32", 128, 20), ("bf16", 128, 64),
+                                    ("bf16", 128, 16), ("bf16", 128, 7)])
+@pytest.mark.parametrize("T", [1, 2, 5, 37])
+def test_indexer_integer_inputs_bit_exact(dsa, orc, dt, D, H, T):
+    B, Lmax = 2, 300
+    lens = [300, 150]
+    q, w, k = _int_inputs(B, T, H, D, Lmax, seed=T * 100 + H)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    kl = torch.tensor(lens, dtype=torch.int32)
+    s = shape_of(dsa, batch=B, n_q=T, max_kv=Lmax, idx_heads=H, idx_dim=D, idx_dtype=dt)
+    got = dsa.index_scores(s, q.to(tdt).to(DEV), w.to(DEV), k.to(tdt).to(DEV), kl.to(DEV))
+    ref = orc.index_scores(q, w, k, kl).reshape(B, T, Lmax)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("T", [1, 2, 9])
+def test_indexer_fp8_exact_codes(dsa, orc, T):
+    # small-integer codes with power-of-two scales: every partial sum is exact
+    B, H, D, Lmax = 2, 64, 128, 200
+    g = torch.Generator().manual_seed(T)
+    qv = torch.randint(-4, 5, (B, T, H, D), generator=g).float()
+    kv = torch.randint(-4, 5, (B, Lmax, D), generator=g).float()
+    w = torch.randint(-3, 4, (B, T, H), generator=g).float()
+    qs = 2.0 ** torch.randint(-2, 3, (B, T, H), generator=g).float()
+    ks = 2.0 ** torch.randint(-2, 3, (B, Lmax), generator=g).float()
+    qc = torch.from_numpy(orc.e4m3_encode(qv.numpy()))
+    kc = torch.from_numpy(orc.e4m3_encode(kv.numpy()))
+    kl = torch.tensor([200, 77], dtype=torch.int32)
+    s = shape_of(dsa, batch=B, n_q=T, max_kv=Lmax, idx_dtype="fp8")
+    got = dsa.index_scores(s, qc.to(DEV), w.to(DEV), kc.to(DEV), kl.to(DEV), q_scale=qs.to(DEV),
+                           k_scale=ks.to(DEV))
+    ref = orc.index_scores_fp8(qc, qs, w, kc, ks, kl).reshape(B, T, Lmax)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("name,seqs,rows", [("tiny_f32", None, None), ("prefill_4k", None, [0, 1, 7, 8, 2047, 2048,
+                                                                                             3001, 4095]),
+                                            ("decode_32k", [0, 33, 63], None)])
+def test_indexer_gaussian_within_tolerance(dsa, orc, name, seqs, rows):
+    wl = get(name)
+    inp = make_inputs(wl, device=DEV, with_mla=False)
+    s = dsa.DsaShape.of(wl)
+    got = dsa.index_scores(s, inp["q_idx"], inp["w"], inp["k_idx"], inp["kv_len"]).cpu()
+    T = wl.n_q
+    if seqs is not None:
+        sub = {k: v[seqs].cpu() for k, v in inp.items()}
+        ref = orc.index_scores(sub["q_idx"], sub["w"], sub["k_idx"], sub["kv_len"])
+        g = got[seqs].reshape(len(seqs) * T, -1).numpy()
+    else:
+        r = list(range(wl.rows)) if rows is None else rows
+        cpu = {k: v.cpu() for k, v in inp.items()}
+        ref = orc.index_scores(cpu["q_idx"], cpu["w"], cpu["k_idx"], cpu["kv_len"], rows=r)
+        g = got.reshape(wl.rows, -1)[r].numpy()
+    err = rel_rowmax(g, ref)
+    assert err.max() < TOL[wl.idx_dtype] / 10, err.max()
+
+
+def test_indexer_fp8_on_oracle_codes_long_context(dsa, orc):
+    # 2 sequences of the 131072-token fp8 workload; codes made by the oracle feed both sides
+    wl = get("decode_128k_fp8").replace(batch=2)
+    inp = make_inputs(wl, with_mla=False)
+    qc, qs = orc.rotate_quant(inp["q_idx"])
+    kc, ks = orc.rotate_quant(inp["k_idx"])
+    s = dsa.DsaShape.of(wl)
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    got = dsa.index_scores(s, t(qc), inp["w"].to(DEV), t(kc), inp["kv_len"].to(DEV), q_scale=t(qs),
+                           k_scale=t(ks)).cpu().reshape(2, -1).numpy()
+    ref = orc.index_scores_fp8(qc, qs, inp["w"], kc, ks, inp["kv_len"])
+    assert rel_rowmax(got, ref).max() < 1e-4
+    # the method's own precision loss: fp8 scores against unquantised ones
+    plain = orc.index_scores(inp["q_idx"], inp["w"], inp["k_idx"], inp["kv_len"])
+    assert rel_rowmax(got, plain).max() < TOL["fp8"]
+
+
+# --------------------------------------------------------------------- top-k
+TOPK_CASES = [
+    # (B, T, Lmax, lens, K)
+    (2, 3, 5000, [5000, 2100], 2048),
+    (1, 300, 300, [300], 64),
+    (2, 1, 40000, [40000, 33000], 2048),  # rows longer than the LDS-resident limit
+    (3, 4, 900, [900, 10, 3], 1),
+    (1, 8, 100, [100], 4096),             # every row shorter than K
+    (2, 2, 2049, [2049, 2048], 2048),     # one candidate over / exactly K
+]
+
+
+@pytest.mark.parametrize("kind", ["gauss", "ties", "int", "const", "signed_zero"])
+@pytest.mark.parametrize("case", TOPK_CASES)
+def test_topk_exact_against_oracle(dsa, orc, kind, case):
+    B, T, Lmax, lens, K = case
+    sc = make_scores(B * T, Lmax, seed=len(kind) + Lmax, kind=kind).reshape(B, T, Lmax).clone()
+    # entries past each row's last visible position must never be read
+    for b in range(B):
+        for t in range(T):
+            p = lens[b] - T + t
+            sc[b, t, max(p + 1, 0):] = 1e30
+    kl = torch.tensor(lens, dtype=torch.int32)
+    s = shape_of(dsa, batch=B, n_q=T, max_kv=Lmax, topk=K)
+    got = dsa.topk(s, sc.to(DEV), kl.to(DEV)).cpu().numpy().reshape(B * T, K)
+    ref = orc.topk(sc.reshape(B * T, Lmax), kl, T, K)
+    for r in range(B * T):
+        want = sorted(x for x in ref[r] if x >= 0)
+        want = want + [-1] * (K - len(want))
+        assert list(got[r]) == want, f"row {r}"
+
+
+# ---------------------------------------------------------------- sparse MLA
+def _mla_case(B, T, H, Dqk, Dv, Lmax, lens, K, dt, seed, kind="topk"):
+    g = torch.Generator().manual_seed(seed)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    q = (torch.randn(B, T, H, Dqk, generator=g) * 3).to(tdt)  # logits ~ N(0, 9): a peaked softmax
+    kv = (torch.randn(B, Lmax, Dqk, generator=g)).to(tdt)
+    idx = torch.full((B, T, K), -1, dtype=torch.int32)
+    for b in range(B):
+        for t in range(T):
+            p = lens[b] - T + t
+            n = max(0, min(K, p + 1))
+            perm = torch.randperm(max(p + 1, 1), generator=g)[:n]
+            idx[b, t, :n] = perm.int()
+            if kind == "messy" and K >= 8:
+                idx[b, t, 0] = idx[b, t, 1]          # a duplicate
+                idx[b, t, 2] = lens[b] + 5           # out of range -> skipped
+                idx[b, t, 3] = -7                    # negative -> skipped
+    return q, kv, idx, torch.tensor(lens, dtype=torch.int32)
+
+
+MLA_CASES = [
+    # B, T, H, Dqk, Dv, Lmax, lens, K, dt, kind
+    (1, 256, 4, 80, 64, 256, [256], 64, "f32", "topk"),
+    (2, 3, 9, 80, 64, 100, [100, 40], 64, "f32", "messy"),
+    (4, 1, 128, 576, 512, 4096, [4096, 3000, 2048, 700], 2048, "bf16", "topk"),
+    (1, 40, 128, 576, 512, 1000, [1000], 256, "bf16", "messy"),
+    (2, 5, 20, 192, 128, 600, [600, 300], 128, "bf16", "topk"),
+    (3, 2, 128, 576, 512, 64, [64, 2, 1], 32, "bf16", "topk"),
+]
+
+
+@pytest.mark.parametrize("case", MLA_CASES)
+def test_sparse_mla_against_oracle(dsa, orc, case):
+    B, T, H, Dqk, Dv, Lmax, lens, K, dt, kind = case
+    q, kv, idx, kl = _mla_case(B, T, H, Dqk, Dv, Lmax, lens, K, dt, seed=B * 1000 + T + H, kind=kind)
+    sm = Dqk ** -0.5
+    s = shape_of(dsa, batch=B, n_q=T, max_kv=Lmax, heads=H, qk_dim=Dqk, v_dim=Dv, topk=K, sm_scale=sm,
+                 mla_dtype=dt)
+    out, lse = dsa.sparse_mla_fwd(s, q.to(DEV), kv.to(DEV), idx.to(DEV), kl.to(DEV))
+    out = out.float().cpu().numpy().reshape(B * T, H, Dv)
+    lse = lse.cpu().numpy().reshape(B * T, H)
+    # the oracle skips out-of-range entries the same way the header defines
+    ix = idx.clone().reshape(B * T, K)
+    for r in range(B * T):
+        L = lens[r // T]
+        bad = (ix[r] >= L) | (ix[r] < 0)
+        ix[r][bad] = -1
+    ro, rl = orc.sparse_mla(q, kv, ix, sm, v_dim=Dv)
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(lse), empty)
+    assert np.all(out[empty] == 0)
+    live = ~empty
+    err = rel_rowmax(out[live], ro[live])
+    assert err.max() < TOL[dt], err.max()
+    assert np.abs(lse[live] - rl[live]).max() < TOL[dt] * max(1.0, np.abs(rl[live]).max())

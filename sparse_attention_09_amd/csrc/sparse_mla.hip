@@ -7,19 +7,27 @@
 // first Dv columns are the value, so all heads of a query share each gathered
 // row:  z_j = sm_scale * q_h . kv[idx_j],  o_h = sum_j softmax(z)_j kv[idx_j, :Dv].
 //
-// Work item = (query, group of 16*NW heads, split of the index list).  Per
-// 32-entry tile: the selected rows are gathered (coalesced 16-byte loads of
-// whole rows) into an LDS tile; each wave (16 heads) computes
-//   S^T[32 keys x 16 heads] = K_tile . Q^T        (keys on M, heads on N)
-// so a lane holds one head's logits for 8 keys, runs the online softmax in
-// registers, and feeds P^T directly as the B operand of
-//   O^T[Dv x 16 heads] += V^T . P^T               (value dims on M)
-// whose A operand (V^T) is read from the row-major tile with the LDS transpose
-// load; the key order inside the contraction is permuted to match the lanes'
-// logits.  Queries' heads of one (query, split) unit are launched on the same
-// XCD so the second head group finds the gathered rows in that XCD's L2.
-// Splits write fp32 partials (unnormalised O, running max, running sum) that a
-// combine kernel merges by log-sum-exp.
+// bf16 kernel (the DeepSeek shapes).  One 512-thread workgroup owns a
+// (query, split of the index list) unit and all 128 heads, so every selected
+// row is gathered once per query.  Per 32-entry tile:
+//   - the rows are gathered straight into LDS (global_load_lds, 16 B per lane,
+//     whole rows, double buffered: tile t+1 is in flight while t is computed);
+//   - wave pair p (heads 32p..32p+31) splits the contraction: wave (p, h)
+//     computes S^T_h[32 keys x 32 heads] = K[:, d-half h] . Q^T[d-half h] on
+//     32x32x16 MFMA (keys on M, heads on N), the halves are summed through LDS,
+//     and both waves run the same online softmax in registers;
+//   - wave (p, h) then accumulates O^T[value half h (Dv/2) x 32 heads] +=
+//     V^T . P^T, P^T taken straight from the logit registers (the key order of
+//     the contraction is permuted to match) and V^T read from the row-major tile
+//     with the LDS transpose load.
+// Thirty-two heads per wave halve the LDS bytes per MFMA flop against 16, and
+// the contraction split keeps two waves per SIMD.  Units of consecutive
+// queries go to one XCD, whose L2 then serves rows that neighbouring queries
+// share.  Splits write fp32 partials (unnormalised O, running max, running
+// sum) merged by a log-sum-exp combine kernel.
+//
+// fp32 kernel (small shapes only): 16 heads per wave on 16x16x4 MFMA, the
+// gathered tile staged through registers.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -30,71 +38,333 @@ constexpr int kTileKeys = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int DT> struct MlaElem;
-template <> struct MlaElem<kF32> { static constexpr int v = 4; };
-template <> struct MlaElem<kBF16> { static constexpr int v = 2; };
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int DT, int DQK, int DV, int NW>
-struct MlaCfg {
-    static constexpr int EB = MlaElem<DT>::v;
-    static constexpr int ROWB = DQK * EB;        // bytes of one latent row
-    static constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
-    static constexpr int PITCH = ROWB + 16;      // padded LDS row pitch
-    static constexpr int SHB = ROWB / 4;         // bytes of a lane's contraction share
-    static constexpr int QCH = SHB / 16;         // 16-byte chunks in that share
-    static constexpr int VT = DV / 16;           // value-dim tiles of 16
-    static constexpr int NT = NW * 64;           // threads
-    static constexpr int HPB = 16 * NW;          // heads per block
-    static_assert(ROWB % 64 == 0, "row share must be whole 16-byte chunks");
-    static_assert(DV % 16 == 0 && DV <= DQK, "value width");
-};
-
-// Work-item decode with XCD grouping: blocks L, L+8, ... land on one XCD, so
-// all head groups of a (query, split) unit share L2.
-__device__ __forceinline__ void mla_item(int L, int HG, int& unit, int& hg)
+__device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c)
 {
-    const int xcd = L & 7, rest = L >> 3;
-    hg = rest % HG;
-    unit = (rest / HG) * 8 + xcd;
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
 }
 
-template <int DT, int DQK, int DV, int NW>
-__global__ __launch_bounds__(NW * 64) void mla_kernel(MlaArgs a)
+__device__ __forceinline__ int valid_key(const MlaArgs& a, const int32_t* idxr, int j, int j_end, int L)
 {
-    using C = MlaCfg<DT, DQK, DV, NW>;
+    const int s = j < j_end ? idxr[j] : -1;
+    return (s >= 0 && s < L) ? s : -1;
+}
+
+// Units of consecutive index go to one XCD: blocks are dealt round-robin over
+// the 8 XCDs, so block L runs on XCD L % 8.
+__device__ __forceinline__ int xcd_unit(int L, int n_units)
+{
+    const int per = (n_units + 7) >> 3;
+    return (L & 7) * per + (L >> 3);
+}
+
+// ================================================================ bf16 kernel
+template <int DQK, int DV>
+struct Bf16Cfg {
+    static constexpr int ROWB = DQK * 2;          // bytes of a latent row
+    static constexpr int CPR = DQK / 8;           // 16-byte chunks per row
+    static constexpr int PCH = CPR + 1;           // LDS pitch in chunks (one pad chunk)
+    static constexpr int PITCH = PCH * 16;
+    static constexpr int TILE_CH = kTileKeys * PCH;
+    static constexpr int DMA_PER_WAVE = (TILE_CH + 511) / 512;  // 1 KiB direct loads per wave per tile
+    static constexpr int BUF_CH = DMA_PER_WAVE * 512;           // buffer size in chunks (dummy tail)
+    static constexpr int HALF = DQK / 2;          // contraction share of a wave
+    static constexpr int SHARE = DQK / 4;         // share of one 32-lane k-block
+    static constexpr int QS = SHARE / 8;          // 32x32x16 steps over a half
+    static constexpr int VH = DV / 2;             // value dims of a wave
+    static constexpr int VT = VH / 32;            // 32-row value tiles of a wave
+    static_assert(DQK % 32 == 0 && DV % 64 == 0 && DV <= DQK, "shape");
+};
+
+constexpr int kHeadsPerBlock = 128;  // 4 wave pairs x 32 heads
+constexpr int kMaxListLen = 4096;    // longest index list a split holds in LDS
+
+// Issue this wave's direct loads of index-list tile [j0, j0 + 32) (sanitised in
+// LDS, -1 = skip) into LDS buffer dst: position P holds row P / PCH, chunk
+// P % PCH; the pad chunk and the dummy tail past the tile repeat row 0, so every
+// wave issues exactly DMA_PER_WAVE loads.  Skipped entries fetch row 0 and are
+// masked by the caller.
+template <int DQK, int DV>
+__device__ __forceinline__ void gather_tile(const char* kvb, const int* lidx, int j0, int w, int lane, u32x4* dst)
+{
+    using C = Bf16Cfg<DQK, DV>;
+    // recompute addresses per load (an opaque lane id keeps them out of the loop's live set)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+    for (int k = 0; k < C::DMA_PER_WAVE; ++k) {
+        const int u = wu + 8 * k;
+        const int P = u * 64 + ln;
+        int s = 0, c = 0;
+        if (P < C::TILE_CH) {
+            const int r = P / C::PCH;
+            c = P - r * C::PCH;
+            c = c == C::CPR ? 0 : c;
+            s = lidx[j0 + r];
+            s = s < 0 ? 0 : s;
+        }
+        __builtin_amdgcn_global_load_lds(kvb + (size_t)s * C::ROWB + c * 16,
+                                         (__attribute__((address_space(3))) void*)(dst + u * 64), 16, 0, 0);
+    }
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose vmcnt(0)
+// would also drain the tile prefetch): wait for this wave's LDS traffic (and,
+// with VM, its direct loads), then s_barrier.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void barrier_lds_vm() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int DQK, int DV>
+struct Bf16State {
+    f32x16 o[Bf16Cfg<DQK, DV>::VT];
+    float m_run, l_run;
+};
+
+// One 32-entry tile for wave (pair, half): partial S^T over the contraction
+// half, exchange with the partner wave, online softmax, O^T[value half] += V^T.P^T.
+template <int DQK, int DV>
+__device__ __forceinline__ void tile_compute(const u32x4* tile, uint32_t vmask, const u32x4 (&qb)[Bf16Cfg<DQK, DV>::QS],
+                                             Bf16State<DQK, DV>& st, float zc, float (*xbuf)[16][64], int w,
+                                             int lane)
+{
+    using C = Bf16Cfg<DQK, DV>;
+    asm volatile("" : "+v"(lane));  // lane-derived addresses are recomputed per tile, not kept live
+    const int col = lane & 31, kb = lane >> 5, half = w & 1;
+    const char* tb = reinterpret_cast<const char*>(tile);
+    f32x16 sacc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+    const char* kr = tb + col * C::PITCH + (C::HALF * half + C::SHARE * kb) * 2;
+#pragma unroll
+    for (int s = 0; s < C::QS; ++s) sacc = mfma32_bf16(*reinterpret_cast<const u32x4*>(kr + 16 * s), qb[s], sacc);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xbuf[w][e][lane] = sacc[e];
+    barrier_lds();
+    // lane holds keys 8*i + 4*kb + j (register 4*i + j) of head `col`
+    float tmax = -INFINITY;
+    if (vmask == 0xFFFFFFFFu) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            sacc[e] = (sacc[e] + xbuf[w ^ 1][e][lane]) * zc;
+            tmax = fmaxf(tmax, sacc[e]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int key = 8 * (e >> 2) + 4 * kb + (e & 3);
+            const float sv = sacc[e] + xbuf[w ^ 1][e][lane];
+            sacc[e] = ((vmask >> key) & 1u) ? sv * zc : -INFINITY;
+            tmax = fmaxf(tmax, sacc[e]);
+        }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // Lazy rescaling: the reference max m_run only moves when a logit exceeds
+    // it by more than 8 (log2 units), so p <= 2^8 and O, l stay exact in fp32
+    // while the rescale of O is rare.
+    if (__ballot(tmax > st.m_run + 8.f)) {
+        const float m_new = fmaxf(st.m_run, tmax);
+        const float alpha = st.m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+        st.l_run *= alpha;
+#pragma unroll
+        for (int v = 0; v < C::VT; ++v) st.o[v] *= alpha;
+        st.m_run = m_new;
+    }
+    const float m_use = st.m_run == -INFINITY ? 0.f : st.m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        sacc[e] = __builtin_amdgcn_exp2f(sacc[e] - m_use);
+        psum += sacc[e];
+    }
+    st.l_run += psum;
+    // transpose-load roles: this lane supplies row 8*(2*step+i') + 4*kbv + jr, column vb + 4*qc
+    const int grp = lane >> 4, m16 = lane & 15;
+    const int kbv = grp >> 1, vb = 16 * (grp & 1);
+    const int jr = m16 >> 2, qc = m16 & 3;
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+        u32x4 pb;
+        pb[0] = pack_bf16x2(sacc[8 * step + 0], sacc[8 * step + 1]);
+        pb[1] = pack_bf16x2(sacc[8 * step + 2], sacc[8 * step + 3]);
+        pb[2] = pack_bf16x2(sacc[8 * step + 4], sacc[8 * step + 5]);
+        pb[3] = pack_bf16x2(sacc[8 * step + 6], sacc[8 * step + 7]);
+        const char* r0 = tb + (16 * step + 4 * kbv + jr) * C::PITCH + (C::VH * half + vb + 4 * qc) * 2;
+        const char* r1 = r0 + 8 * C::PITCH;
+#pragma unroll
+        for (int v = 0; v < C::VT; ++v) {
+            const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(r0 + 64 * v));
+            const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(r1 + 64 * v));
+            const u32x2 y0 = __builtin_bit_cast(u32x2, x0);
+            const u32x2 y1 = __builtin_bit_cast(u32x2, x1);
+            st.o[v] = mfma32_bf16(u32x4{y0[0], y0[1], y1[0], y1[1]}, pb, st.o[v]);
+        }
+    }
+}
+
+// One 512-thread workgroup (8 waves, two per SIMD) owns a (query, split of the
+// index list) unit and 128 heads.  Wave w = (pair w/2, half w%2): heads
+// 32*(w/2).., contraction half and value half w%2.  Two LDS tile buffers named
+// statically (loop unrolled by two) keep the next tile's gather in flight
+// while the current one is consumed.
+template <int DQK, int DV>
+__global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
+{
+    using C = Bf16Cfg<DQK, DV>;
+    __shared__ __attribute__((aligned(16))) u32x4 tA[C::BUF_CH];
+    __shared__ __attribute__((aligned(16))) u32x4 tB[C::BUF_CH];
+    __shared__ float xbuf[8][16][64];
+    __shared__ int lidx[kMaxListLen];
+    __shared__ uint32_t tmask[kMaxListLen / kTileKeys];
+
+    const int HB = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    const int n_units = a.B * a.t_count * a.n_split * HB;
+    const int unit = xcd_unit(blockIdx.x, n_units);
+    if (unit >= n_units) return;
+    const int hb = unit % HB;
+    const int split = (unit / HB) % a.n_split;
+    const int rq = unit / HB / a.n_split;
+    const int b = rq / a.t_count;
+    const int t = a.t_begin + rq % a.t_count;
+    const size_t row = (size_t)b * a.T + t;
+    const int L = min(a.kv_len[b], a.Lmax);
+
+    const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    const int pair = w >> 1, half = w & 1;
+    const int col = lane & 31, kb = lane >> 5;
+    const int head = hb * kHeadsPerBlock + pair * 32 + col;
+    const bool head_ok = head < a.H;
+
+    const int per = ((a.K + a.n_split - 1) / a.n_split + kTileKeys - 1) / kTileKeys * kTileKeys;
+    const int j_begin = split * per;
+    const int j_end = min(a.K, j_begin + per);
+    const int n_tiles = j_end > j_begin ? (j_end - j_begin + kTileKeys - 1) / kTileKeys : 0;
+
+    // Q^T operand: head `head`, contraction d in [HALF*half + SHARE*kb, + SHARE)
+    u32x4 qb[C::QS];
+    {
+        const char* src = (const char*)a.q + ((row * a.H + (head_ok ? head : 0)) * DQK) * 2 +
+                          (C::HALF * half + C::SHARE * kb) * 2;
+#pragma unroll
+        for (int s = 0; s < C::QS; ++s) qb[s] = head_ok ? ld16(src + 16 * s) : u32x4{0, 0, 0, 0};
+    }
+    const char* kvb = (const char*)a.kv + (size_t)b * a.Lmax * C::ROWB;
+    const int32_t* idxr = a.idx + row * a.K;
+    // the split's index list, sanitised (-1 = skip) and padded to whole tiles,
+    // plus a validity mask per tile
+    for (int j = tid; j < n_tiles * kTileKeys; j += 512) {
+        const int sk = valid_key(a, idxr, j_begin + j, j_end, L);
+        lidx[j] = sk;
+        const uint64_t bits = __ballot(sk >= 0);  // 64 consecutive entries = two tiles
+        if (lane == 0) {
+            tmask[j / kTileKeys] = (uint32_t)bits;
+            if (j / kTileKeys + 1 < kMaxListLen / kTileKeys) tmask[j / kTileKeys + 1] = (uint32_t)(bits >> 32);
+        }
+    }
+    __syncthreads();
+
+    Bf16State<DQK, DV> st;
+#pragma unroll
+    for (int v = 0; v < C::VT; ++v)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st.o[v][e] = 0.f;
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+    const float zc = a.sm_scale * kLog2e;
+
+    // tile `it` lives in buffer it % 2; each step issues tile it + 1 into the other buffer
+    if (n_tiles > 0) gather_tile<DQK, DV>(kvb, lidx, 0, w, lane, tA);
+#pragma unroll 1
+    for (int it = 0; it < n_tiles; it += 2) {
+        barrier_lds_vm();
+        if (it + 1 < n_tiles) gather_tile<DQK, DV>(kvb, lidx, (it + 1) * kTileKeys, w, lane, tB);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_compute<DQK, DV>(tA, tmask[it], qb, st, zc, xbuf, w, lane);
+        if (it + 1 >= n_tiles) break;
+        barrier_lds_vm();
+        if (it + 2 < n_tiles) gather_tile<DQK, DV>(kvb, lidx, (it + 2) * kTileKeys, w, lane, tA);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_compute<DQK, DV>(tB, tmask[it + 1], qb, st, zc, xbuf, w, lane);
+    }
+
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
+    if (!head_ok) return;
+    const size_t orow = row * a.H + head;
+    // lane holds value dims VH*half + 32*v + 8*i + 4*kb + jj (register 4*i + jj)
+    if (a.n_split == 1) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t* dst = (uint16_t*)a.out + orow * DV + C::VH * half + 4 * kb;
+#pragma unroll
+        for (int v = 0; v < C::VT; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                u32x2 w2 = {pack_bf16x2(st.o[v][4 * i] * inv, st.o[v][4 * i + 1] * inv),
+                            pack_bf16x2(st.o[v][4 * i + 2] * inv, st.o[v][4 * i + 3] * inv)};
+                *reinterpret_cast<u32x2*>(dst + 32 * v + 8 * i) = w2;
+            }
+        if (a.lse && half == 0 && kb == 0) a.lse[orow] = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    } else {
+        float* pr = a.part + (((size_t)rq * a.n_split + split) * a.H + head) * (DV + 2);
+#pragma unroll
+        for (int v = 0; v < C::VT; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<f32x4*>(pr + C::VH * half + 32 * v + 8 * i + 4 * kb) =
+                    f32x4{st.o[v][4 * i], st.o[v][4 * i + 1], st.o[v][4 * i + 2], st.o[v][4 * i + 3]};
+        if (half == 0 && kb == 0) {
+            pr[DV] = st.m_run;
+            pr[DV + 1] = l_tot;
+        }
+    }
+}
+
+// ================================================================ fp32 kernel
+template <int DQK, int DV>
+struct F32Cfg {
+    static constexpr int ROWB = DQK * 4;
+    static constexpr int CPR = ROWB / 16;
+    static constexpr int PITCH = ROWB + 16;
+    static constexpr int SHB = ROWB / 4;
+    static constexpr int QCH = SHB / 16;
+    static constexpr int VT = DV / 16;
+    static_assert(ROWB % 64 == 0 && DV % 16 == 0 && DV <= DQK, "shape");
+};
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(64) void mla_f32_kernel(MlaArgs a)
+{
+    using C = F32Cfg<DQK, DV>;
     __shared__ __attribute__((aligned(16))) char tile[kTileKeys * C::PITCH];
     __shared__ int sidx[kTileKeys];
 
-    const int HG = (a.H + C::HPB - 1) / C::HPB;
-    int unit, hg;
-    mla_item(blockIdx.x, HG, unit, hg);
-    const int n_units = a.B * a.t_count * a.n_split;
+    const int HG = (a.H + 15) / 16;
+    const int n_units = a.B * a.t_count * a.n_split * HG;
+    const int unit = xcd_unit(blockIdx.x, n_units);
     if (unit >= n_units) return;
-    const int split = unit % a.n_split;
-    const int rq = unit / a.n_split;            // query row within this launch
+    const int hg = unit % HG;
+    const int split = (unit / HG) % a.n_split;
+    const int rq = unit / HG / a.n_split;
     const int b = rq / a.t_count;
     const int t = a.t_begin + rq % a.t_count;
-    const size_t row = (size_t)b * a.T + t;     // row of the full [B,T,...] tensors
+    const size_t row = (size_t)b * a.T + t;
     const int L = min(a.kv_len[b], a.Lmax);
-
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const int n = lane & 15, g = lane >> 4;
-    const int head = hg * C::HPB + wave * 16 + n;
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const int head = hg * 16 + n;
     const bool head_ok = head < a.H;
-
-    // split range over the index list, whole tiles
     const int per = ((a.K + a.n_split - 1) / a.n_split + kTileKeys - 1) / kTileKeys * kTileKeys;
     const int j_begin = split * per;
     const int j_end = min(a.K, j_begin + per);
 
-    // Q^T operand: lane holds head `head`, contraction share g.
     u32x4 qb[C::QCH];
     {
-        const char* src = (const char*)a.q + ((row * a.H + (head_ok ? head : 0)) * DQK) * C::EB + g * C::SHB;
+        const char* src = (const char*)a.q + ((row * a.H + (head_ok ? head : 0)) * DQK) * 4 + g * C::SHB;
 #pragma unroll
         for (int c = 0; c < C::QCH; ++c) qb[c] = head_ok ? ld16(src + 16 * c) : u32x4{0, 0, 0, 0};
     }
-
     f32x4 o[C::VT];
 #pragma unroll
     for (int v = 0; v < C::VT; ++v) o[v] = f32x4{0, 0, 0, 0};
@@ -105,22 +375,15 @@ __global__ __launch_bounds__(NW * 64) void mla_kernel(MlaArgs a)
 
 #pragma unroll 1
     for (int j0 = j_begin; j0 < j_end; j0 += kTileKeys) {
-        if (tid < kTileKeys) {
-            const int j = j0 + tid;
-            int s = j < j_end ? idxr[j] : -1;
-            sidx[tid] = (s >= 0 && s < L) ? s : -1;
-        }
+        if (lane < kTileKeys) sidx[lane] = valid_key(a, idxr, j0 + lane, j_end, L);
         __syncthreads();
-        // gather the tile's rows (invalid rows become zeros)
-        for (int c = tid; c < kTileKeys * C::CPR; c += C::NT) {
-            const int r = c / C::CPR, col = c % C::CPR;
+        for (int c = lane; c < kTileKeys * C::CPR; c += 64) {
+            const int r = c / C::CPR, cc = c % C::CPR;
             const int s = sidx[r];
-            const u32x4 v = s >= 0 ? ld16(kvb + (size_t)s * C::ROWB + col * 16) : u32x4{0, 0, 0, 0};
-            *reinterpret_cast<u32x4*>(&tile[r * C::PITCH + col * 16]) = v;
+            const u32x4 v = s >= 0 ? ld16(kvb + (size_t)s * C::ROWB + cc * 16) : u32x4{0, 0, 0, 0};
+            *reinterpret_cast<u32x4*>(&tile[r * C::PITCH + cc * 16]) = v;
         }
         __syncthreads();
-
-        // S^T = K_tile . Q^T for two 16-key M tiles
         f32x4 s[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -129,78 +392,45 @@ __global__ __launch_bounds__(NW * 64) void mla_kernel(MlaArgs a)
 #pragma unroll
             for (int c = 0; c < C::QCH; ++c) {
                 const u32x4 ka = *reinterpret_cast<const u32x4*>(kr + 16 * c);
-                if constexpr (DT == kBF16) {
-                    acc = mfma_bf16(ka, qb[c], acc);
-                } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc = mfma_f32(__uint_as_float(ka[e]), __uint_as_float(qb[c][e]), acc);
-                }
+                for (int e = 0; e < 4; ++e) acc = mfma_f32(__uint_as_float(ka[e]), __uint_as_float(qb[c][e]), acc);
             }
             s[mt] = acc;
         }
-
-        // online softmax (log2 domain); lane holds keys 16*mt + 4*g + i of head `head`
         float z[2][4];
         float tmax = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok = sidx[16 * mt + 4 * g + i] >= 0;
-                z[mt][i] = ok ? s[mt][i] * zc : -INFINITY;
+                z[mt][i] = sidx[16 * mt + 4 * g + i] >= 0 ? s[mt][i] * zc : -INFINITY;
                 tmax = fmaxf(tmax, z[mt][i]);
             }
         tmax = group4_max(tmax);
         const float m_new = fmaxf(m_run, tmax);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = exp2f(m_run - m_use);
-        float p[2][4];
         float psum = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[mt][i] = exp2f(z[mt][i] - m_use);
-                psum += p[mt][i];
+                z[mt][i] = exp2f(z[mt][i] - m_use);
+                psum += z[mt][i];
             }
         l_run = l_run * alpha + psum;
         m_run = m_new;
-        if (__ballot(alpha != 1.f)) {
 #pragma unroll
-            for (int v = 0; v < C::VT; ++v) o[v] *= alpha;
-        }
-
-        // O^T += V^T . P^T
-        if constexpr (DT == kBF16) {
-            u32x4 pb;
-            pb[0] = pack_bf16x2(p[0][0], p[0][1]);
-            pb[1] = pack_bf16x2(p[0][2], p[0][3]);
-            pb[2] = pack_bf16x2(p[1][0], p[1][1]);
-            pb[3] = pack_bf16x2(p[1][2], p[1][3]);
-            // transpose-load addresses: this lane supplies row key_j = 4g + j (and 16 + 4g + j),
-            // columns 16*vt + 4q, for j = n / 4, q = n % 4
-            const int jr = n >> 2, qc = n & 3;
-            const char* r1 = &tile[(4 * g + jr) * C::PITCH + 8 * qc];
-            const char* r2 = &tile[(16 + 4 * g + jr) * C::PITCH + 8 * qc];
+        for (int v = 0; v < C::VT; ++v) o[v] *= alpha;
+        // O^T += V^T . P^T in eight 4-key steps; step st pairs lane group g with key
+        // 4g + st (st < 4) or 16 + 4g + st - 4, the keys whose logits the lane holds
 #pragma unroll
-            for (int v = 0; v < C::VT; ++v) {
-                const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(r1 + 32 * v));
-                const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(r2 + 32 * v));
-                const u32x2 y1 = __builtin_bit_cast(u32x2, x1);
-                const u32x2 y2 = __builtin_bit_cast(u32x2, x2);
-                o[v] = mfma_bf16(u32x4{y1[0], y1[1], y2[0], y2[1]}, pb, o[v]);
-            }
-        } else {
+        for (int st = 0; st < 8; ++st) {
+            const int key = st < 4 ? 4 * g + st : 16 + 4 * g + (st - 4);
+            const float pv = st < 4 ? z[0][st] : z[1][st - 4];
+            const float* vr = reinterpret_cast<const float*>(&tile[key * C::PITCH]);
 #pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                const int key = st < 4 ? 4 * g + st : 16 + 4 * g + (st - 4);
-                const float pv = st < 4 ? p[0][st] : p[1][st - 4];
-                const float* vr = reinterpret_cast<const float*>(&tile[key * C::PITCH]);
-#pragma unroll
-                for (int v = 0; v < C::VT; ++v) o[v] = mfma_f32(vr[16 * v + n], pv, o[v]);
-            }
+            for (int v = 0; v < C::VT; ++v) o[v] = mfma_f32(vr[16 * v + n], pv, o[v]);
         }
         __syncthreads();
     }
@@ -211,18 +441,10 @@ __global__ __launch_bounds__(NW * 64) void mla_kernel(MlaArgs a)
     if (a.n_split == 1) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-        for (int v = 0; v < C::VT; ++v) {
-            const int d0 = 16 * v + 4 * g;
-            if constexpr (DT == kBF16) {
-                u32x2 w2 = {pack_bf16x2(o[v][0] * inv, o[v][1] * inv), pack_bf16x2(o[v][2] * inv, o[v][3] * inv)};
-                *reinterpret_cast<u32x2*>((char*)a.out + (orow * DV + d0) * 2) = w2;
-            } else {
-                *reinterpret_cast<f32x4*>((float*)a.out + orow * DV + d0) = o[v] * inv;
-            }
-        }
+        for (int v = 0; v < C::VT; ++v)
+            *reinterpret_cast<f32x4*>((float*)a.out + orow * DV + 16 * v + 4 * g) = o[v] * inv;
         if (a.lse && g == 0) a.lse[orow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
-        // partial record: O[DV] (unnormalised), m (log2 domain), l
         float* pr = a.part + (((size_t)rq * a.n_split + split) * a.H + head) * (DV + 2);
 #pragma unroll
         for (int v = 0; v < C::VT; ++v) *reinterpret_cast<f32x4*>(pr + 16 * v + 4 * g) = o[v];
@@ -233,7 +455,8 @@ __global__ __launch_bounds__(NW * 64) void mla_kernel(MlaArgs a)
     }
 }
 
-// Merge split partials: one wave per (query, head).
+// ============================================================ split combine
+// One wave per (query, head): merge the split partials by log-sum-exp.
 template <int DT, int DV>
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a)
 {
@@ -263,19 +486,33 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a)
     if (a.lse && lane == 0) a.lse[orow] = Ls > 0.f ? (Mu + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
-template <int DT, int DQK, int DV, int NW>
-hipError_t launch_cfg(const MlaArgs& a, hipStream_t s)
+template <int DT, int DV>
+hipError_t launch_combine(const MlaArgs& a, hipStream_t s)
 {
-    using C = MlaCfg<DT, DQK, DV, NW>;
-    const int HG = (a.H + C::HPB - 1) / C::HPB;
-    const long long units = (long long)a.B * a.t_count * a.n_split;
-    const long long blocks = 8LL * HG * ((units + 7) / 8);
-    mla_kernel<DT, DQK, DV, NW><<<dim3((unsigned)blocks), C::NT, 0, s>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.n_split == 1) return e;
+    if (a.n_split == 1) return hipSuccess;
     const long long waves = (long long)a.B * a.t_count * a.H;
     mla_combine_kernel<DT, DV><<<dim3((unsigned)((waves + 3) / 4)), 256, 0, s>>>(a);
     return hipGetLastError();
+}
+
+template <int DQK, int DV>
+hipError_t launch_bf16(const MlaArgs& a, hipStream_t s)
+{
+    const int HB = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    const long long units = (long long)a.B * a.t_count * a.n_split * HB;
+    mla_bf16_kernel<DQK, DV><<<dim3((unsigned)(8 * ((units + 7) / 8))), 512, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_combine<kBF16, DV>(a, s);
+}
+
+template <int DQK, int DV>
+hipError_t launch_f32(const MlaArgs& a, hipStream_t s)
+{
+    const int HG = (a.H + 15) / 16;
+    const long long units = (long long)a.B * a.t_count * a.n_split * HG;
+    mla_f32_kernel<DQK, DV><<<dim3((unsigned)(8 * ((units + 7) / 8))), 64, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_combine<kF32, DV>(a, s);
 }
 
 }  // namespace
@@ -287,11 +524,12 @@ bool mla_supported(int dtype, int Dqk, int Dv)
     return false;
 }
 
+// Split the index list only when the queries alone leave CUs idle.
 int mla_split_count(int B, int t_count, int H, int K)
 {
-    const long long hg = (H + 63) / 64;
-    const long long units = (long long)B * t_count * hg;
-    long long ns = (512 + units - 1) / units;
+    const long long hb = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    const long long units = (long long)B * t_count * hb;
+    long long ns = (256 + units - 1) / units;
     const long long max_ns = K / 128 > 1 ? K / 128 : 1;
     if (ns > max_ns) ns = max_ns;
     if (ns > 16) ns = 16;
@@ -307,9 +545,9 @@ size_t mla_partial_bytes(int B, int t_count, int H, int Dv, int n_split)
 hipError_t launch_mla(int dtype, const MlaArgs& a, hipStream_t s)
 {
     if (a.t_count <= 0 || a.B <= 0) return hipSuccess;
-    if (dtype == kF32) return launch_cfg<kF32, 80, 64, 1>(a, s);
-    if (a.Dqk == 192) return launch_cfg<kBF16, 192, 128, 4>(a, s);
-    return launch_cfg<kBF16, 576, 512, 4>(a, s);
+    if (dtype == kF32) return launch_f32<80, 64>(a, s);
+    if (a.Dqk == 192) return launch_bf16<192, 128>(a, s);
+    return launch_bf16<576, 512>(a, s);
 }
 
 }  // namespace dsa

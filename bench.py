@@ -135,6 +135,7 @@ def time_stages(dsa, torch, cases, steps):
         if c.scores is None:
             c.scores = torch.empty((B, T, Lmax), dtype=torch.float32, device="cuda")
         c.mla_ws = torch.empty((max(dsa.sparse_mla_workspace_size(sh), 1),), dtype=torch.uint8, device="cuda")
+        c.topk_ws = torch.empty((max(dsa.topk_workspace_size(sh), 1),), dtype=torch.uint8, device="cuda")
     names = ["indexer", "topk", "mla"]
     acc = {n: 0.0 for n in names}
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -146,7 +147,7 @@ def time_stages(dsa, torch, cases, steps):
         dsa.index_scores(sh, qi, i["w"], c.k_idx, i["kv_len"], q_scale=getattr(c, "q_scale", None),
                          k_scale=c.k_scale, scores=c.scores)
         ev[1].record(stream)
-        dsa.topk(sh, c.scores, i["kv_len"], idx=c.idx)
+        dsa.topk(sh, c.scores, i["kv_len"], idx=c.idx, workspace=c.topk_ws)
         ev[2].record(stream)
         dsa.sparse_mla_fwd(sh, i["q"], i["kv"], c.idx, i["kv_len"], out=c.out, lse=c.lse, workspace=c.mla_ws)
         ev[3].record(stream)

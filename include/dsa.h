@@ -109,7 +109,11 @@ dsa_status dsa_index_scores(const dsa_shape* shape, const void* q_idx, const flo
  *          largest scores, ties broken towards the smaller position, written in
  *          ascending position order, followed by K - k_eff entries of -1.
  *          -0.0 counts as equal to +0.0; NaN scores are not supported.
- *   workspace / ws_bytes: at least dsa_topk_workspace_size(shape) bytes. */
+ *   workspace / ws_bytes: at least dsa_topk_workspace_size(shape) bytes, 16-byte
+ *          aligned, owned by the caller; its contents are scratch on entry and exit.
+ *          The size is 0 (workspace may be NULL) unless the rows are few and long
+ *          (B*T <= 256 and L_max >= 8192), when each row is split over many
+ *          workgroups.  Too small: DSA_ERR_WORKSPACE. */
 size_t dsa_topk_workspace_size(const dsa_shape* shape);
 dsa_status dsa_topk(const dsa_shape* shape, const float* scores, const int32_t* kv_len,
                     int32_t* idx, void* workspace, size_t ws_bytes, hipStream_t stream);

@@ -97,10 +97,10 @@ dsa::IndexerArgs indexer_args(const dsa_shape* s, const void* q, const float* qs
     return a;
 }
 
-dsa::TopkArgs topk_args(const dsa_shape* s, const float* scores, const int32_t* kv_len, int32_t* idx, int t_begin,
-                        int t_count)
+dsa::TopkArgs topk_args(const dsa_shape* s, const float* scores, const int32_t* kv_len, int32_t* idx, void* ws,
+                        int t_begin, int t_count)
 {
-    dsa::TopkArgs a;
+    dsa::TopkArgs a{};
     a.B = s->batch;
     a.T = s->n_q;
     a.Lmax = s->max_kv;
@@ -112,6 +112,7 @@ dsa::TopkArgs topk_args(const dsa_shape* s, const float* scores, const int32_t* 
     a.ld_b = (long long)t_count * s->max_kv;
     a.kv_len = kv_len;
     a.idx = idx;
+    a.ws = ws;
     return a;
 }
 
@@ -146,7 +147,9 @@ size_t mla_ws(const dsa_shape* s, int t_count)
     return dsa::mla_partial_bytes(s->batch, t_count, s->heads, s->v_dim, ns);
 }
 
-// Workspace layout of dsa_forward for a query chunk of tc rows.
+// Workspace layout of dsa_forward for a query chunk of tc rows.  The top-k
+// scratch and the MLA split partials share one region: on one stream the top-k
+// of a chunk has finished before its MLA starts.
 struct FwdLayout {
     size_t qcodes = 0, qscale = 0, idx = 0, scores = 0, part = 0, total = 0;
 };
@@ -169,7 +172,9 @@ FwdLayout fwd_layout(const dsa_shape* s, int tc, bool own_idx)
     l.scores = off;
     off += align_up((size_t)s->batch * tc * s->max_kv * sizeof(float));
     l.part = off;
-    off += align_up(mla_ws(s, tc));
+    const size_t tk = dsa::topk_workspace_bytes(s->batch, tc, s->max_kv, s->topk);
+    const size_t pw = mla_ws(s, tc);
+    off += align_up(tk > pw ? tk : pw);
     l.total = off;
     return l;
 }
@@ -250,8 +255,11 @@ DSA_EXPORT dsa_status dsa_topk(const dsa_shape* s, const float* scores, const in
     DSA_TRY(ptr_ok(kv_len, 4));
     DSA_TRY(ptr_ok(idx, 4));
     const size_t need = dsa::topk_workspace_bytes(s->batch, s->n_q, s->max_kv, s->topk);
-    if (need > 0 && (!workspace || ws_bytes < need)) return DSA_ERR_WORKSPACE;
-    const dsa::TopkArgs a = topk_args(s, scores, kv_len, idx, 0, s->n_q);
+    if (need > 0) {
+        if (!workspace || ws_bytes < need) return DSA_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return DSA_ERR_ALIGN;
+    }
+    const dsa::TopkArgs a = topk_args(s, scores, kv_len, idx, need > 0 ? workspace : nullptr, 0, s->n_q);
     return hip_status(dsa::launch_topk(a, stream));
 }
 
@@ -352,7 +360,7 @@ DSA_EXPORT dsa_status dsa_forward(const dsa_shape* s, const void* q_idx, const f
         const int cnt = (s->n_q - t0) < tc ? (s->n_q - t0) : tc;
         const dsa::IndexerArgs ia = indexer_args(s, qi, qsc, w, k_idx, k_scale, kv_len, scores, t0, cnt, 0);
         if (dsa::launch_indexer(s->idx_dtype, ia, stream) != hipSuccess) return DSA_ERR_HIP;
-        const dsa::TopkArgs ta = topk_args(s, scores, kv_len, idx, t0, cnt);
+        const dsa::TopkArgs ta = topk_args(s, scores, kv_len, idx, part, t0, cnt);
         if (dsa::launch_topk(ta, stream) != hipSuccess) return DSA_ERR_HIP;
         const int ns = dsa::mla_split_count(s->batch, cnt, s->heads, s->topk);
         const dsa::MlaArgs ma = mla_args(s, q, kv, idx, kv_len, out, lse, part, t0, cnt, ns);

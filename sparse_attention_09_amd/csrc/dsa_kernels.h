@@ -33,6 +33,7 @@ struct TopkArgs {
     long long ld_b, ld_t;
     const int32_t* kv_len;
     int32_t* idx;
+    void* ws;               // topk_workspace_bytes(B, t_count, Lmax, K) bytes, 16-byte aligned
 };
 
 // Sparse absorbed MLA for queries [t_begin, t_begin + t_count).
@@ -53,7 +54,8 @@ struct MlaArgs {
 bool indexer_supported(int dtype, int D, int H);
 hipError_t launch_indexer(int dtype, const IndexerArgs& a, hipStream_t s);
 
-size_t topk_workspace_bytes(int B, int T, int Lmax, int K);
+// Workspace of one top-k launch over B * t_count rows (0 when none is needed).
+size_t topk_workspace_bytes(int B, int t_count, int Lmax, int K);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 bool mla_supported(int dtype, int Dqk, int Dv);

@@ -35,6 +35,8 @@ namespace dsa {
 namespace {
 
 constexpr int kTileKeys = 32;
+// A split partial row holds DV values, then m (log2 domain) and l, padded to 16 bytes.
+constexpr int kPartExtra = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
             }
         if (a.lse && half == 0 && kb == 0) a.lse[orow] = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
-        float* pr = a.part + (((size_t)rq * a.n_split + split) * a.H + head) * (DV + 2);
+        float* pr = a.part + (((size_t)rq * a.n_split + split) * a.H + head) * (DV + kPartExtra);
 #pragma unroll
         for (int v = 0; v < C::VT; ++v)
 #pragma unroll
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(64) void mla_f32_kernel(MlaArgs a)
             *reinterpret_cast<f32x4*>((float*)a.out + orow * DV + 16 * v + 4 * g) = o[v] * inv;
         if (a.lse && g == 0) a.lse[orow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
-        float* pr = a.part + (((size_t)rq * a.n_split + split) * a.H + head) * (DV + 2);
+        float* pr = a.part + (((size_t)rq * a.n_split + split) * a.H + head) * (DV + kPartExtra);
 #pragma unroll
         for (int v = 0; v < C::VT; ++v) *reinterpret_cast<f32x4*>(pr + 16 * v + 4 * g) = o[v];
         if (g == 0) {
@@ -456,7 +458,8 @@ __global__ __launch_bounds__(64) void mla_f32_kernel(MlaArgs a)
 }
 
 // ============================================================ split combine
-// One wave per (query, head): merge the split partials by log-sum-exp.
+// One wave per (query, head): merge the split partials by log-sum-exp.  Lane sp
+// holds the weight of split sp; the value rows are read as float4.
 template <int DT, int DV>
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a)
 {
@@ -466,22 +469,30 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a)
     const int head = wid % a.H, rq = wid / a.H;
     const int b = rq / a.t_count, t = a.t_begin + rq % a.t_count;
     const size_t orow = ((size_t)b * a.T + t) * a.H + head;
-    const float* base = a.part + ((size_t)rq * a.n_split * a.H + head) * (DV + 2);
-    const size_t sstride = (size_t)a.H * (DV + 2);
-    float M = -INFINITY;
-    for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, base[sp * sstride + DV]);
+    constexpr int RS = DV + kPartExtra;
+    const float* base = a.part + ((size_t)rq * a.n_split * a.H + head) * RS;
+    const size_t sstride = (size_t)a.H * RS;
+    const int ns = a.n_split;
+    const float mi = lane < ns ? base[lane * sstride + DV] : -INFINITY;
+    const float li = lane < ns ? base[lane * sstride + DV + 1] : 0.f;
+    const float M = wave_max(mi);
     const float Mu = M == -INFINITY ? 0.f : M;
-    float Ls = 0.f;
-    for (int sp = 0; sp < a.n_split; ++sp) Ls += exp2f(base[sp * sstride + DV] - Mu) * base[sp * sstride + DV + 1];
+    const float wi = lane < ns ? exp2f(mi - Mu) : 0.f;
+    const float Ls = wave_sum(wi * li);
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    for (int d = lane; d < DV; d += 64) {
-        float acc = 0.f;
-        for (int sp = 0; sp < a.n_split; ++sp) acc += exp2f(base[sp * sstride + DV] - Mu) * base[sp * sstride + d];
+    for (int c = lane; c < DV / 4; c += 64) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < ns; ++sp) {
+            const float wsp = __shfl(wi, sp, 64);
+            acc += wsp * *reinterpret_cast<const f32x4*>(base + sp * sstride + 4 * c);
+        }
         acc *= inv;
-        if constexpr (DT == kBF16)
-            ((uint16_t*)a.out)[orow * DV + d] = f32_to_bf16(acc);
-        else
-            ((float*)a.out)[orow * DV + d] = acc;
+        if constexpr (DT == kBF16) {
+            const u32x2 w2 = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            *reinterpret_cast<u32x2*>((uint16_t*)a.out + orow * DV + 4 * c) = w2;
+        } else {
+            *reinterpret_cast<f32x4*>((float*)a.out + orow * DV + 4 * c) = acc;
+        }
     }
     if (a.lse && lane == 0) a.lse[orow] = Ls > 0.f ? (Mu + log2f(Ls)) * kLn2 : -INFINITY;
 }
@@ -539,7 +550,7 @@ int mla_split_count(int B, int t_count, int H, int K)
 size_t mla_partial_bytes(int B, int t_count, int H, int Dv, int n_split)
 {
     if (n_split <= 1) return 0;
-    return (size_t)B * t_count * n_split * H * (Dv + 2) * sizeof(float);
+    return (size_t)B * t_count * n_split * H * (Dv + kPartExtra) * sizeof(float);
 }
 
 hipError_t launch_mla(int dtype, const MlaArgs& a, hipStream_t s)

@@ -4,16 +4,31 @@
 // for each query the indexer keeps the index_topk best-scored tokens.  A query
 // at position p has p + 1 candidates; with no more than K of them all are kept.
 //
-// One 1024-thread workgroup per query row.  Scores become order-preserving
-// uint32 keys (held in LDS when the row fits, else re-read from L2), the K-th
-// largest key is found by radix select (12 + 12 + 8 bit digits, histograms in
-// LDS), and the selection is written by an ordered compaction: each wave owns a
-// contiguous segment, counts its "greater" and "equal" keys, and after a scan of
-// the 16 segment counts writes positions in ascending order.  Among keys equal
-// to the threshold the smallest positions win, so the selected set is exactly
-// "score descending, position ascending" and the output is deterministic.
+// Every path selects exactly "score descending, position ascending" and writes
+// the positions in ascending order.  Scores become order-preserving uint32 keys
+// (-0 folded onto +0).
+//
+// Many rows (prefill): one 1024-thread workgroup per row.  The row's keys sit in
+// LDS when they fit (else are re-read from L2); radix select (12 + 12 + 8 bit
+// digits, LDS histograms) finds the K-th largest key tau; an ordered compaction
+// over 16 contiguous wave segments then writes every key > tau and the first
+// (by position) keys == tau.
+//
+// Few long rows (decode): the row is split over 4096-entry chunks so the whole
+// GPU works on it.
+//   hist   : each chunk histograms the top 12 bits of its keys in LDS and adds
+//            the non-zero bins to the row's global histogram;
+//   filter : each chunk finds the bin d1 holding the K-th largest key from that
+//            histogram, appends keys above d1 to the row's "selected" list and
+//            keys in d1 to its "candidate" list (wave-aggregated atomics);
+//   finish : one workgroup per row resolves the candidates in LDS (radix select
+//            on the low 20 bits, then smallest positions among equal keys),
+//            merges them with the selected list and sorts the K positions.
+// A candidate list that overflows its buffer falls back to the whole-row select.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
+
+#include <algorithm>
 
 namespace dsa {
 namespace {
@@ -22,6 +37,9 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kTopkStageMax = 32768;  // longest row held in LDS (128 KiB of keys)
 constexpr int kHistBins = 4096;
+constexpr int kChunk = 4096;          // entries per chunk of the split path
+constexpr int kCandCap = 16384;       // candidate buffer per row of the split path
+constexpr int kMaxK = 4096;
 
 struct TopkShared {
     uint32_t keys[kTopkStageMax];
@@ -34,29 +52,104 @@ struct TopkShared {
     int sel_above;
 };
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a)
+struct FinishShared {
+    union {
+        struct {
+            uint32_t ckey[kCandCap];
+            int32_t cidx[kCandCap];
+        };
+        uint32_t bits[2 * kCandCap];  // position bitmap, reuses the candidate space
+    };
+    int32_t out[kMaxK];
+    uint32_t hist[1024];
+    uint32_t sel_digit;
+    int sel_above;
+    int n_out;
+};
+
+static_assert(2 * kCandCap * 32 >= (1 << 20), "bitmap must cover the longest row");
+
+union TopkUnion {
+    TopkShared full;
+    FinishShared fin;
+};
+
+// Wave 0 scans hist[0..nbins) from the top for the bin holding the k-th
+// largest element: writes its digit and the count strictly above it.
+__device__ __forceinline__ void find_digit_desc(const uint32_t* hist, int nbins, uint32_t k, uint32_t* digit,
+                                                int* above_out)
 {
-    __shared__ TopkShared sh;
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const int b = blockIdx.x / a.t_count;
-    const int t = a.t_begin + blockIdx.x % a.t_count;
-    const int L = min(a.kv_len[b], a.Lmax);
-    const int n = max(0, min(a.Lmax, L - a.T + t + 1));  // candidates 0 .. p
-    const int K = a.K;
-    int32_t* dst = a.idx + ((size_t)b * a.T + t) * K;
-
-    if (n <= K) {
-        for (int j = tid; j < K; j += kTopkThreads) dst[j] = j < n ? j : -1;
-        return;
+    const int lane = lane_id();
+    const int per = nbins / 64;
+    uint32_t s = 0;
+    for (int j = 0; j < per; ++j) s += hist[lane * per + j];
+    uint32_t incl = s;  // suffix sum over lanes >= lane
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_down(incl, off, 64);
+        if (lane + off < 64) incl += o;
     }
+    const uint32_t excl = incl - s;
+    if (excl < k && incl >= k) {
+        uint32_t above = excl;
+        for (int j = per - 1; j >= 0; --j) {
+            const uint32_t h = hist[lane * per + j];
+            if (above + h >= k) {
+                *digit = (uint32_t)(lane * per + j);
+                *above_out = (int)above;
+                break;
+            }
+            above += h;
+        }
+    }
+}
 
-    const float* src = a.scores + b * a.ld_b + (long long)(t - a.t_begin) * a.ld_t;
+// The same from the bottom: the bin holding the k-th smallest element and the
+// count strictly below it.
+__device__ __forceinline__ void find_digit_asc(const uint32_t* hist, int nbins, uint32_t k, uint32_t* digit,
+                                               int* below_out)
+{
+    const int lane = lane_id();
+    const int per = nbins / 64;
+    uint32_t s = 0;
+    for (int j = 0; j < per; ++j) s += hist[lane * per + j];
+    uint32_t incl = s;  // prefix sum over lanes <= lane
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    const uint32_t excl = incl - s;
+    if (excl < k && incl >= k) {
+        uint32_t below = excl;
+        for (int j = 0; j < per; ++j) {
+            const uint32_t h = hist[lane * per + j];
+            if (below + h >= k) {
+                *digit = (uint32_t)(lane * per + j);
+                *below_out = (int)below;
+                break;
+            }
+            below += h;
+        }
+    }
+}
+
+struct RowKeys {
+    const float* src;
+    const uint32_t* staged;
+    __device__ __forceinline__ uint32_t operator()(int i) const { return staged ? staged[i] : float_key(src[i]); }
+};
+
+// Whole-row select by one 1024-thread workgroup (n > K): radix select of the
+// K-th largest key, then an ordered compaction writing ascending positions.
+__device__ void block_select(TopkShared& sh, const float* src, int n, int K, int32_t* dst)
+{
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const bool staged = n <= kTopkStageMax;
     if (staged)
         for (int i = tid; i < n; i += kTopkThreads) sh.keys[i] = float_key(src[i]);
-    auto key_at = [&](int i) -> uint32_t { return staged ? sh.keys[i] : float_key(src[i]); };
+    const RowKeys key_at{src, staged ? sh.keys : nullptr};
 
-    // ---- radix select of the K-th largest key
     uint32_t prefix = 0, pmask = 0;
     int krem = K;  // how many still to take among keys matching the prefix
 #pragma unroll 1
@@ -70,42 +163,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a)
             if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & (nbins - 1)], 1u);
         }
         __syncthreads();
-        if (wave == 0) {
-            // lane l sums bins [l*per, (l+1)*per); suffix-scan the lane sums from the top
-            const int per = nbins / 64;
-            uint32_t s = 0;
-            for (int j = 0; j < per; ++j) s += sh.hist[lane * per + j];
-            uint32_t incl = s;  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t o = __shfl_down(incl, off, 64);
-                if (lane + off < 64) incl += o;
-            }
-            const uint32_t excl = incl - s;  // lanes strictly above
-            const bool here = excl < (uint32_t)krem && incl >= (uint32_t)krem;
-            if (here) {
-                uint32_t above = excl;
-                for (int j = per - 1; j >= 0; --j) {
-                    const uint32_t h = sh.hist[lane * per + j];
-                    if (above + h >= (uint32_t)krem) {
-                        sh.sel_digit = (uint32_t)(lane * per + j);
-                        sh.sel_above = (int)above;
-                        break;
-                    }
-                    above += h;
-                }
-            }
-        }
+        if (wave == 0) find_digit_desc(sh.hist, nbins, (uint32_t)krem, &sh.sel_digit, &sh.sel_above);
         __syncthreads();
-        const uint32_t d = sh.sel_digit;
         krem -= sh.sel_above;
-        prefix |= d << shift;
+        prefix |= sh.sel_digit << shift;
         pmask |= (uint32_t)(nbins - 1) << shift;
         __syncthreads();
     }
     const uint32_t tau = prefix;  // key of the K-th largest score; take krem keys equal to it
 
-    // ---- ordered compaction over 16 contiguous wave segments
     const int seg = ((n + kTopkWaves - 1) / kTopkWaves + 63) & ~63;
     const int s0 = min(n, wave * seg), s1 = min(n, s0 + seg);
     int gt = 0, eq = 0;
@@ -148,14 +214,334 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a)
     }
 }
 
+__device__ __forceinline__ void row_of(const TopkArgs& a, int r, int& b, int& t, int& n)
+{
+    b = r / a.t_count;
+    t = a.t_begin + r % a.t_count;
+    const int L = min(a.kv_len[b], a.Lmax);
+    n = max(0, min(a.Lmax, L - a.T + t + 1));  // candidates 0 .. p
+}
+
+__device__ __forceinline__ const float* row_scores(const TopkArgs& a, int b, int t)
+{
+    return a.scores + b * a.ld_b + (long long)(t - a.t_begin) * a.ld_t;
+}
+
+__device__ __forceinline__ void write_all(int32_t* dst, int n, int K)
+{
+    for (int j = threadIdx.x; j < K; j += blockDim.x) dst[j] = j < n ? j : -1;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a)
+{
+    __shared__ TopkShared sh;
+    int b, t, n;
+    row_of(a, blockIdx.x, b, t, n);
+    int32_t* dst = a.idx + ((size_t)b * a.T + t) * a.K;
+    if (n <= a.K) {
+        write_all(dst, n, a.K);
+        return;
+    }
+    block_select(sh, row_scores(a, b, t), n, a.K, dst);
+}
+
+// ------------------------------------------------------------ split path
+struct SplitWs {
+    uint32_t* hist;  // [rows][4096]
+    uint32_t* cnt;   // [rows][4]: selected count, candidate count
+    int32_t* sel;    // [rows][K]
+    uint2* cand;     // [rows][kCandCap] (key, position)
+};
+
+__device__ __forceinline__ SplitWs split_ws(const TopkArgs& a)
+{
+    const size_t rows = (size_t)a.B * a.t_count;
+    char* p = (char*)a.ws;
+    SplitWs w;
+    w.hist = (uint32_t*)p;
+    p += rows * kHistBins * 4;
+    w.cnt = (uint32_t*)p;
+    p += rows * 4 * 4;
+    w.sel = (int32_t*)p;
+    p += rows * (size_t)a.K * 4;
+    w.cand = (uint2*)p;
+    return w;
+}
+
+size_t split_ws_bytes(size_t rows, int K)
+{
+    return rows * (kHistBins * 4 + 16 + (size_t)K * 4 + (size_t)kCandCap * 8);
+}
+
+size_t split_zero_words(size_t rows) { return rows * (kHistBins + 4); }
+
+__global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* p, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a)
+{
+    __shared__ uint32_t lh[kHistBins];
+    int b, t, n;
+    row_of(a, blockIdx.y, b, t, n);
+    const int c0 = blockIdx.x * kChunk;
+    if (n <= a.K || c0 >= n) return;
+    const int c1 = min(n, c0 + kChunk);
+    const SplitWs w = split_ws(a);
+    const float* src = row_scores(a, b, t);
+    for (int i = threadIdx.x; i < kHistBins; i += 256) lh[i] = 0u;
+    __syncthreads();
+    for (int i = c0 + threadIdx.x; i < c1; i += 256) atomicAdd(&lh[float_key(src[i]) >> 20], 1u);
+    __syncthreads();
+    uint32_t* gh = w.hist + (size_t)blockIdx.y * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += 256) {
+        const uint32_t v = lh[i];
+        if (v) atomicAdd(&gh[i], v);
+    }
+}
+
+// Inclusive scan over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+constexpr int kFilterPer = kChunk / 256;  // keys per thread in the filter pass
+
+__global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a)
+{
+    __shared__ uint32_t lh[kHistBins];
+    __shared__ uint32_t sh_digit;
+    __shared__ int sh_above;
+    __shared__ uint32_t wtot[2][4];
+    __shared__ uint32_t gbase[2];
+    int b, t, n;
+    row_of(a, blockIdx.y, b, t, n);
+    const int c0 = blockIdx.x * kChunk;
+    if (n <= a.K || c0 >= n) return;
+    const int c1 = min(n, c0 + kChunk);
+    const SplitWs w = split_ws(a);
+    const size_t row = blockIdx.y;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const float* src = row_scores(a, b, t);
+    // keys of this thread: c0 + tid + 256 * j (loads in flight while the threshold is found)
+    uint32_t key[kFilterPer];
+#pragma unroll
+    for (int j = 0; j < kFilterPer; ++j) {
+        const int i = c0 + tid + 256 * j;
+        key[j] = i < c1 ? float_key(src[i]) : 0u;
+    }
+    for (int i = tid; i < kHistBins; i += 256) lh[i] = w.hist[row * kHistBins + i];
+    __syncthreads();
+    if (wave == 0) find_digit_desc(lh, kHistBins, (uint32_t)a.K, &sh_digit, &sh_above);
+    __syncthreads();
+    const uint32_t d1 = sh_digit;
+    uint32_t ns = 0, nc = 0;
+#pragma unroll
+    for (int j = 0; j < kFilterPer; ++j) {
+        const bool ok = c0 + tid + 256 * j < c1;
+        const uint32_t dg = key[j] >> 20;
+        ns += (ok && dg > d1) ? 1u : 0u;
+        nc += (ok && dg == d1) ? 1u : 0u;
+    }
+    const uint32_t is = wave_incl_scan(ns), ic = wave_incl_scan(nc);
+    if (lane == 63) {
+        wtot[0][wave] = is;
+        wtot[1][wave] = ic;
+    }
+    __syncthreads();
+    if (tid == 0) {  // one reservation per workgroup and list
+        const uint32_t ts = wtot[0][0] + wtot[0][1] + wtot[0][2] + wtot[0][3];
+        const uint32_t tc = wtot[1][0] + wtot[1][1] + wtot[1][2] + wtot[1][3];
+        gbase[0] = ts ? atomicAdd(&w.cnt[row * 4 + 0], ts) : 0u;
+        gbase[1] = tc ? atomicAdd(&w.cnt[row * 4 + 1], tc) : 0u;
+    }
+    __syncthreads();
+    uint32_t ps = gbase[0] + is - ns, pc = gbase[1] + ic - nc;
+    for (int v = 0; v < wave; ++v) {
+        ps += wtot[0][v];
+        pc += wtot[1][v];
+    }
+    int32_t* sel = w.sel + row * a.K;
+    uint2* cand = w.cand + row * kCandCap;
+#pragma unroll
+    for (int j = 0; j < kFilterPer; ++j) {
+        const int i = c0 + tid + 256 * j;
+        const uint32_t dg = key[j] >> 20;
+        if (i < c1 && dg > d1) sel[ps++] = i;
+        if (i < c1 && dg == d1) {
+            if (pc < (uint32_t)kCandCap) cand[pc] = make_uint2(key[j], (uint32_t)i);
+            ++pc;
+        }
+    }
+}
+
+// Block-wide exclusive scan (1024 threads); `tmp` holds 16 words.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp)
+{
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint32_t incl = wave_incl_scan(v);
+    if (lane == 63) tmp[wave] = incl;
+    __syncthreads();
+    uint32_t base = 0;
+    for (int u = 0; u < wave; ++u) base += tmp[u];
+    return base + incl - v;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_finish_kernel(TopkArgs a)
+{
+    __shared__ TopkUnion u;
+    int b, t, n;
+    row_of(a, blockIdx.x, b, t, n);
+    const int K = a.K;
+    int32_t* dst = a.idx + ((size_t)b * a.T + t) * K;
+    if (n <= K) {
+        write_all(dst, n, K);
+        return;
+    }
+    const SplitWs w = split_ws(a);
+    const size_t row = blockIdx.x;
+    const int n_sel = (int)w.cnt[row * 4 + 0];
+    const int n_cand = (int)w.cnt[row * 4 + 1];
+    if (n_cand > kCandCap) {  // candidate buffer overflowed: select over the whole row
+        block_select(u.full, row_scores(a, b, t), n, K, dst);
+        return;
+    }
+    FinishShared& f = u.fin;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const uint2* cand = w.cand + row * kCandCap;
+    for (int i = tid; i < n_cand; i += kTopkThreads) {
+        const uint2 c = cand[i];
+        f.ckey[i] = c.x;
+        f.cidx[i] = (int32_t)c.y;
+    }
+    const int krem = K - n_sel;  // candidates to take, 1 <= krem <= n_cand
+    // radix select of the krem-th largest candidate key on bits 19..10 then 9..0
+    uint32_t prefix = 0, pmask = 0;
+    int need = krem;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = pass == 0 ? 10 : 0;
+        for (int i = tid; i < 1024; i += kTopkThreads) f.hist[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < n_cand; i += kTopkThreads) {
+            const uint32_t k = f.ckey[i];
+            if ((k & pmask) == prefix) atomicAdd(&f.hist[(k >> shift) & 1023u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) find_digit_desc(f.hist, 1024, (uint32_t)need, &f.sel_digit, &f.sel_above);
+        __syncthreads();
+        need -= f.sel_above;
+        prefix |= f.sel_digit << shift;
+        pmask |= 1023u << shift;
+        __syncthreads();
+    }
+    const uint32_t tau_low = prefix;  // low 20 bits of the threshold key
+    const int count_eq = (int)f.hist[tau_low & 1023u];
+    __syncthreads();  // every thread has read the histogram before it is cleared again
+    // among keys equal to the threshold, keep the `need` smallest positions
+    uint32_t iota = 0xFFFFFFFFu;
+    if (need < count_eq) {
+        uint32_t ip = 0, im = 0;
+        int k2 = need;
+#pragma unroll 1
+        for (int pass = 0; pass < 2; ++pass) {
+            const int shift = pass == 0 ? 10 : 0;
+            for (int i = tid; i < 1024; i += kTopkThreads) f.hist[i] = 0;
+            __syncthreads();
+            for (int i = tid; i < n_cand; i += kTopkThreads) {
+                const uint32_t p = (uint32_t)f.cidx[i];
+                if ((f.ckey[i] & 0xFFFFFu) == tau_low && (p & im) == ip) atomicAdd(&f.hist[(p >> shift) & 1023u], 1u);
+            }
+            __syncthreads();
+            if (wave == 0) find_digit_asc(f.hist, 1024, (uint32_t)k2, &f.sel_digit, &f.sel_above);
+            __syncthreads();
+            k2 -= f.sel_above;
+            ip |= f.sel_digit << shift;
+            im |= 1023u << shift;
+            __syncthreads();
+        }
+        iota = ip;
+    }
+    // the chosen candidates go to `out` before the bitmap reuses the candidate space
+    if (tid == 0) f.n_out = 0;
+    __syncthreads();
+    for (int i = tid; i < n_cand; i += kTopkThreads) {
+        const uint32_t lk = f.ckey[i] & 0xFFFFFu;
+        if (lk > tau_low || (lk == tau_low && (uint32_t)f.cidx[i] <= iota)) {
+            const int slot = atomicAdd(&f.n_out, 1);
+            if (slot < K) f.out[slot] = f.cidx[i];
+        }
+    }
+    __syncthreads();
+    const int n_chosen = min(f.n_out, K);
+    // bitmap over positions [0, n): set the selected and chosen positions
+    uint32_t* bits = f.bits;
+    const int n_words = (n + 31) >> 5;
+    for (int i = tid; i < n_words; i += kTopkThreads) bits[i] = 0u;
+    __syncthreads();
+    const int32_t* sel = w.sel + row * K;
+    for (int i = tid; i < n_sel; i += kTopkThreads) {
+        const int p = sel[i];
+        atomicOr(&bits[p >> 5], 1u << (p & 31));
+    }
+    for (int i = tid; i < n_chosen; i += kTopkThreads) {
+        const int p = f.out[i];
+        atomicOr(&bits[p >> 5], 1u << (p & 31));
+    }
+    __syncthreads();
+    // ordered emission: each thread owns a contiguous run of words
+    const int per = (n_words + kTopkThreads - 1) / kTopkThreads;
+    const int w0 = min(n_words, tid * per), w1 = min(n_words, w0 + per);
+    uint32_t cnt = 0;
+    for (int i = w0; i < w1; ++i) cnt += __popc(bits[i]);
+    uint32_t pos = block_excl_scan(cnt, f.hist);
+    for (int i = w0; i < w1; ++i) {
+        uint32_t m = bits[i];
+        while (m) {
+            const int bit = __ffs(m) - 1;
+            m &= m - 1;
+            if (pos < (uint32_t)K) dst[pos] = (i << 5) + bit;
+            ++pos;
+        }
+    }
+}
+
+bool use_split(const TopkArgs& a) { return (long long)a.B * a.t_count <= 256 && a.Lmax >= 2 * kChunk; }
+
 }  // namespace
 
-size_t topk_workspace_bytes(int, int, int, int) { return 0; }
+size_t topk_workspace_bytes(int B, int T, int Lmax, int K)
+{
+    TopkArgs a{};
+    a.B = B;
+    a.t_count = T;
+    a.Lmax = Lmax;
+    a.K = K;
+    return use_split(a) ? split_ws_bytes((size_t)B * T, K) : 0;
+}
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s)
 {
     if (a.t_count <= 0 || a.B <= 0) return hipSuccess;
-    topk_kernel<<<dim3(a.B * a.t_count), kTopkThreads, 0, s>>>(a);
+    const int rows = a.B * a.t_count;
+    if (!use_split(a)) {
+        topk_kernel<<<dim3(rows), kTopkThreads, 0, s>>>(a);
+        return hipGetLastError();
+    }
+    const size_t zw = split_zero_words(rows);
+    topk_zero_kernel<<<dim3((unsigned)std::min<size_t>((zw + 255) / 256, 1024)), 256, 0, s>>>((uint32_t*)a.ws, zw);
+    const dim3 grid((a.Lmax + kChunk - 1) / kChunk, rows);
+    topk_hist_kernel<<<grid, 256, 0, s>>>(a);
+    topk_filter_kernel<<<grid, 256, 0, s>>>(a);
+    topk_finish_kernel<<<dim3(rows), kTopkThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 

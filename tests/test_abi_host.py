@@ -101,6 +101,20 @@ def test_topk_and_mla_reject_bad_arguments(dsa):
     assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == -5
 
 
+def test_topk_workspace_only_for_few_long_rows(dsa):
+    L = dsa.lib()
+    # few long rows are split over many workgroups and need scratch
+    s = _shape(dsa, batch=64, n_q=1, topk=2048, max_kv=32768)
+    need = dsa.topk_workspace_size(s)
+    assert need >= 64 * (4096 * 4 + 2048 * 4)
+    assert L.dsa_topk(ctypes.byref(s.c()), FAKE, FAKE, FAKE, None, 0, None) == -5
+    assert L.dsa_topk(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, need - 1, None) == -5
+    assert L.dsa_topk(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE + 4, need, None) == -4
+    # many rows, or short rows: one workgroup per row, no scratch
+    assert dsa.topk_workspace_size(_shape(dsa, batch=1, n_q=4096, topk=2048, max_kv=32768)) == 0
+    assert dsa.topk_workspace_size(_shape(dsa, batch=64, n_q=1, topk=2048, max_kv=4096)) == 0
+
+
 def test_rotate_quant_rejects_bad_arguments(dsa):
     L = dsa.lib()
     assert L.dsa_rotate_quant_fp8(0, 128, FAKE, 1, FAKE, FAKE, None) == -2

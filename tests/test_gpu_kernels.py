@@ -135,10 +135,15 @@ TOPK_CASES = [
     (3, 4, 900, [900, 10, 3], 1),
     (1, 8, 100, [100], 4096),             # every row shorter than K
     (2, 2, 2049, [2049, 2048], 2048),     # one candidate over / exactly K
+    # few long rows: each row split over 4096-entry chunks
+    (4, 2, 12000, [12000, 9000, 8193, 5000], 2048),
+    (3, 1, 20000, [20000, 2048, 1], 2048),
+    (2, 1, 9000, [9000, 8500], 1000),     # K not a power of two
+    (1, 1, 131072, [131072], 2048),
 ]
 
 
-@pytest.mark.parametrize("kind", ["gauss", "ties", "int", "const", "signed_zero"])
+@pytest.mark.parametrize("kind", ["gauss", "ties", "int", "const", "signed_zero", "narrow"])
 @pytest.mark.parametrize("case", TOPK_CASES)
 def test_topk_exact_against_oracle(dsa, orc, kind, case):
     B, T, Lmax, lens, K = case

@@ -86,7 +86,9 @@ def make_scores(n_rows: int, Lmax: int, device="cpu", seed: int = 0, kind: str =
 
     kind: "gauss" (continuous), "ties" (a few distinct values, many exact ties),
     "int" (small integers), "const" (every entry equal), "signed_zero" (zeros of
-    both signs among negatives and positives).
+    both signs among negatives and positives), "narrow" (1 + j/65536 for
+    j < 4096: values that share sign, exponent and leading mantissa bits, with
+    ties).
     """
     g = _gen(device, 7, 0, seed)
     if kind == "gauss":
@@ -102,4 +104,7 @@ def make_scores(n_rows: int, Lmax: int, device="cpu", seed: int = 0, kind: str =
         neg0 = torch.randint(0, 2, (n_rows, Lmax), generator=g, device=device).bool() & (x == 0)
         x[neg0] = -0.0
         return x
+    if kind == "narrow":
+        j = torch.randint(0, 4096, (n_rows, Lmax), generator=g, device=device).float()
+        return 1.0 + j / 65536.0
     raise ValueError(kind)

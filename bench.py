@@ -6,10 +6,12 @@ A step is one dsa_forward call (fp8 workloads: q rotation + quantisation,
 index scores, top-k, sparse MLA) over one batch of synthetic inputs already
 resident in HBM.  Decode workloads alternate between two independent input
 sets so that consecutive steps cannot be served from the 256 MB Infinity Cache.
-After the timed forward loop, a second timed loop calls the stage entry points
-(same launch configurations) with HIP events between them to get per-kernel
-durations; the dominant kernel is reported against its roofline.  The CPU
-oracle is timed on a bounded sample of the same workload on the host cores.
+After the timed forward loop, each stage entry point (same launch
+configurations) is timed as back-to-back launches between two HIP events on
+the launch stream; the dominant stage is reported against its roofline, with
+the HBM traffic of its kernel taken from a committed rocprofv3 counter summary
+under profiles/ while the kernel source still matches it.  The CPU oracle is
+timed on a bounded sample of the same workload on the host cores.
 
 Prints one JSON line.
 """
@@ -67,12 +69,12 @@ def dominant(wl, stage_us: dict) -> tuple[str, dict]:
     if name != "topk" and ai > ridge:
         achieved = a["flops"] / (us * 1e-6) / 1e12
         peak = PEAK_TFLOPS[dt]
-        return name, {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+        return name, {"kernel": STAGE_KERNELS[name], "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": recorded_traffic(wl, name),
                       "work_per_launch": a["flops"], "avg_launch_us": round(us, 2)}
     achieved = a["bytes"] / (us * 1e-6) / 1e9
-    return name, {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                  "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+    return name, {"kernel": STAGE_KERNELS[name], "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                  "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": recorded_traffic(wl, name),
                   "work_per_launch": a["bytes"], "avg_launch_us": round(us, 2)}
 
 
@@ -123,8 +125,13 @@ def time_forward(dsa, torch, cases, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def time_stages(dsa, torch, cases, steps):
-    """Per-stage durations through the stage entry points (events on the launch stream)."""
+STAGE_KERNELS = {"indexer": "indexer", "topk": "topk (zero, hist, filter, finish) or topk_kernel",
+                 "mla": "mla_bf16_kernel + mla_combine_kernel"}
+
+
+def time_stages(dsa, torch, cases, reps):
+    """Average duration of each stage entry point, measured as `reps` back-to-back
+    launches (alternating input sets) between two HIP events on the launch stream."""
     stream = torch.cuda.current_stream()
     wl = cases[0].wl
     sh = cases[0].shape
@@ -136,29 +143,63 @@ def time_stages(dsa, torch, cases, steps):
             c.scores = torch.empty((B, T, Lmax), dtype=torch.float32, device="cuda")
         c.mla_ws = torch.empty((max(dsa.sparse_mla_workspace_size(sh), 1),), dtype=torch.uint8, device="cuda")
         c.topk_ws = torch.empty((max(dsa.topk_workspace_size(sh), 1),), dtype=torch.uint8, device="cuda")
-    names = ["indexer", "topk", "mla"]
-    acc = {n: 0.0 for n in names}
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    for rep in range(steps + 2):
-        c = cases[rep % len(cases)]
+
+    def indexer(c):
         i = c.inp
         qi = c.q_codes if wl.idx_dtype == "fp8" else i["q_idx"]
-        ev[0].record(stream)
         dsa.index_scores(sh, qi, i["w"], c.k_idx, i["kv_len"], q_scale=getattr(c, "q_scale", None),
                          k_scale=c.k_scale, scores=c.scores)
-        ev[1].record(stream)
-        dsa.topk(sh, c.scores, i["kv_len"], idx=c.idx, workspace=c.topk_ws)
-        ev[2].record(stream)
+
+    def topk(c):
+        dsa.topk(sh, c.scores, c.inp["kv_len"], idx=c.idx, workspace=c.topk_ws)
+
+    def mla(c):
+        i = c.inp
         dsa.sparse_mla_fwd(sh, i["q"], i["kv"], c.idx, i["kv_len"], out=c.out, lse=c.lse, workspace=c.mla_ws)
-        ev[3].record(stream)
+
+    stages = {"indexer": indexer, "topk": topk, "mla": mla}
+    for c in cases:  # every stage reads what the previous one wrote for the same case
+        for f in stages.values():
+            f(c)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, f in stages.items():
+        f(cases[0])
+        e0.record(stream)
+        for r in range(reps):
+            f(cases[r % len(cases)])
+        e1.record(stream)
         torch.cuda.synchronize()
-        if rep >= 2:
-            for k, n in enumerate(names):
-                acc[n] += ev[k].elapsed_time(ev[k + 1]) * 1000.0
-    return {n: acc[n] / steps for n in names}
+        res[name] = e0.elapsed_time(e1) * 1000.0 / reps
+    return res
 
 
-def cpu_baseline(wl, budget_rows: int | None = None) -> dict:
+def recorded_traffic(wl, stage: str):
+    """HBM bytes per launch of a stage's kernel from a committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy); None when
+    no summary covers this workload or the kernel source has changed since."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            if not line.startswith("bench-traffic:"):
+                continue
+            kv = dict(x.split("=", 1) for x in line.split()[1:])
+            if kv.get("workload") != wl.name or kv.get("stage") != stage:
+                continue
+            src = os.path.join(ROOT, kv["source"])
+            if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["sha256"]:
+                return None
+            return int(kv["fetch_bytes"]) + int(kv["write_bytes"])
+    return None
+
+
+CPU_BUDGET_S = 10.0  # oracle work to time, at least (one pass is always completed)
+
+
+def cpu_baseline(wl) -> dict:
     """The oracle, as it stands, on a bounded sample of the workload (host cores)."""
     import numpy as np
 
@@ -167,28 +208,49 @@ def cpu_baseline(wl, budget_rows: int | None = None) -> dict:
     oracle.build()
     threads = oracle.num_threads()
     if wl.n_q == 1:
-        n = budget_rows or min(wl.batch, max(2, threads))
-        seqs = list(range(n))
-        sub = wl.replace(batch=n)
-        inp = make_inputs(sub, seqs=seqs)
-        rows = list(range(n))
-        t0 = time.perf_counter()
-        oracle.forward(inp, sub, rows=rows)
-        dt = time.perf_counter() - t0
-        sample = f"{n} of {wl.batch} sequences (one decode query each, full {wl.kv_len}-token context)"
-    else:
-        n = budget_rows or max(2, threads)
-        rng = np.random.default_rng(0)
-        rows = sorted(rng.choice(wl.rows, size=n, replace=False).tolist())
+        # every sequence of the batch, in repeated passes until the budget is spent
         inp = make_inputs(wl)
-        flat = lambda t: t.reshape(wl.rows, *t.shape[2:])[rows]
-        cin = dict(inp, q_idx=flat(inp["q_idx"]), w=flat(inp["w"]), q=flat(inp["q"]))
-        t0 = time.perf_counter()
-        oracle.forward(cin, wl, rows=rows, compact=True)
-        dt = time.perf_counter() - t0
+        rows = list(range(wl.batch))
+        passes, dt = 0, 0.0
+        while dt < CPU_BUDGET_S and dt < 30.0:
+            t0 = time.perf_counter()
+            oracle.forward(inp, wl, rows=rows)
+            dt += time.perf_counter() - t0
+            passes += 1
+        n = passes * wl.batch
+        sample = f"all {wl.batch} sequences (one decode query each, {wl.kv_len}-token context), {passes} passes"
+        used = min(threads, wl.batch)
+    else:
+        # uniformly drawn query rows, the count doubled until one run fills the budget
+        rng = np.random.default_rng(0)
+        inp = make_inputs(wl)
+        n = min(wl.rows, max(2, threads))
+        while True:
+            rows = sorted(rng.choice(wl.rows, size=n, replace=False).tolist())
+            flat = lambda t: t.reshape(wl.rows, *t.shape[2:])[rows]
+            cin = dict(inp, q_idx=flat(inp["q_idx"]), w=flat(inp["w"]), q=flat(inp["q"]))
+            t0 = time.perf_counter()
+            oracle.forward(cin, wl, rows=rows, compact=True)
+            dt = time.perf_counter() - t0
+            if dt >= CPU_BUDGET_S or n >= wl.rows or dt * 2 > 30.0:
+                break
+            n = min(wl.rows, int(n * max(2.0, min(8.0, CPU_BUDGET_S / max(dt, 1e-3)))))
         sample = f"{n} uniformly drawn query rows of {wl.rows}"
-    return {"value": round(len(rows) / dt, 3), "unit": "queries/s", "cores": min(threads, len(rows)),
-            "kind": "oracle", "sample": sample, "seconds": round(dt, 2)}
+        used = min(threads, n)
+    return {"value": round(n / dt, 3), "unit": "queries/s", "cores": used, "kind": "oracle", "sample": sample,
+            "seconds": round(dt, 2)}
+
+
+def copy_calibration(nbytes: int, reps: int) -> dict:
+    """Plain device-to-device copies of a known size, for calibrating HBM counters."""
+    import torch
+    src = torch.empty((nbytes,), dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes": nbytes, "reps": reps}
 
 
 def run(args) -> dict:
@@ -237,11 +299,16 @@ def main():
     ap.add_argument("--workload", default="decode_32k")
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run plain device copies of BYTES bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(args.copy_calibration, args.steps or 3)), flush=True)
+        return
     print(json.dumps(run(args)), flush=True)
 
 

@@ -7,7 +7,7 @@
 //     C (16 x 16): lane l holds column l%16, rows 4*(l/16) + 0..3
 // Because a product sums over k, any fixed assignment of the contraction index
 // to (k-block, slot) works as long as A and B use the same one; the kernels
-// use that freedom to keep each lane's share of a row contiguous in memory.
+// use that freedom to choose which 16-byte chunks of a row each lane loads.
 //
 // ds_read_b64_tr_b16 (gfx950): inside every 16-lane group, lane i receives
 // element j (j = 0..3) from the address supplied by lane 4*j + i/4 of its group,

@@ -22,6 +22,8 @@
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
+#include <algorithm>
+
 namespace dsa {
 namespace {
 
@@ -30,14 +32,18 @@ template <> struct ElemBytes<kF32> { static constexpr int v = 4; };
 template <> struct ElemBytes<kBF16> { static constexpr int v = 2; };
 template <> struct ElemBytes<kFP8> { static constexpr int v = 1; };
 
-// A lane's contiguous share of one D-wide row: D/4 elements = NCH 16-byte chunks.
+// A lane's share of one D-wide row: D/4 elements = NCH 16-byte chunks.  The
+// 16-lane group g takes chunks g, g + 4, g + 8, ... (byte offset 64 c + 16 g for
+// its c-th chunk), so that one load instruction over a 16-row tile reads 64
+// contiguous bytes of every row.
 template <int DT, int D> struct Share {
     static constexpr int bytes = D * ElemBytes<DT>::v / 4;
     static constexpr int nch = bytes / 16;
     static_assert(bytes % 16 == 0, "row share must be whole 16-byte chunks");
+    static __device__ __forceinline__ int off(int g, int c) { return 64 * c + 16 * g; }
 };
 
-// acc += A_share . B_share over the lane-contiguous contraction mapping.
+// acc += A_share . B_share over the chunk mapping of Share::off.
 template <int DT, int NCH>
 __device__ __forceinline__ f32x4 dot_share(const u32x4 (&a)[NCH], const u32x4 (&b)[NCH], f32x4 acc)
 {
@@ -71,9 +77,9 @@ __device__ __forceinline__ void load_query(const IndexerArgs& a, int b, int t, b
     for (int m = 0; m < HT; ++m) {
         const int h = 16 * m + n;
         const bool ok = valid && h < a.H;
-        const char* src = (const char*)a.q + ((qrow + (ok ? h : 0)) * D) * EB + g * Share<DT, D>::bytes;
+        const char* src = (const char*)a.q + ((qrow + (ok ? h : 0)) * D) * EB;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) qa[m][c] = ok ? ld16(src + 16 * c) : u32x4{0, 0, 0, 0};
+        for (int c = 0; c < NCH; ++c) qa[m][c] = ok ? ld16(src + Share<DT, D>::off(g, c)) : u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int hh = 16 * m + 4 * g + i;
@@ -105,17 +111,91 @@ __device__ __forceinline__ int seq_len(const IndexerArgs& a, int b)
 }
 
 // ---------------------------------------------------------------- decode tiling
+// A strip is TPW consecutive 16-key tiles.  A key at or past kend (>= 1) reads
+// row kend - 1 instead: its score column is never stored, and unconditional
+// loads keep the register prefetch free of waits.
+// Scores leave a strip four tiles at a time: lane (n, g) stores key n of tile
+// 4 j + g, so one store covers 64 consecutive keys.  The fp8 key scales are
+// loaded with the strip in that store layout, so no load waits behind it.
+template <int TPW> struct StripOut { static constexpr int n = (TPW + 3) / 4; };
+
+template <int DT, int D, int TPW>
+__device__ __forceinline__ void load_strip(const IndexerArgs& a, int b, int strip, int kend,
+                                           u32x4 (&kb)[TPW][Share<DT, D>::nch], float (&ks)[StripOut<TPW>::n])
+{
+    constexpr int NCH = Share<DT, D>::nch;
+    constexpr int EB = ElemBytes<DT>::v;
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const char* kbase = (const char*)a.k + (size_t)b * a.Lmax * D * EB;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int key = min((strip * TPW + i) * 16 + n, kend - 1);
+        const char* src = kbase + (size_t)key * D * EB;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) kb[i][c] = ld16(src + Share<DT, D>::off(g, c));
+    }
+#pragma unroll
+    for (int j = 0; j < StripOut<TPW>::n; ++j) {
+        const int key = min((strip * TPW + 4 * j + g) * 16 + n, kend - 1);
+        if constexpr (DT == kFP8)
+            ks[j] = a.k_scale[(size_t)b * a.Lmax + key];
+        else
+            ks[j] = 1.f;
+    }
+}
+
+template <int DT, int D, int HT, int QPW, int TPW>
+__device__ __forceinline__ void score_strip(const IndexerArgs& a, int b, int strip,
+                                            const u32x4 (&kb)[TPW][Share<DT, D>::nch],
+                                            const float (&ks)[StripOut<TPW>::n],
+                                            const u32x4 (&qa)[QPW][HT][Share<DT, D>::nch],
+                                            const float (&wv)[QPW][HT][4], const int (&tq)[QPW],
+                                            const int (&pq)[QPW], const bool (&vq)[QPW], int kend)
+{
+    constexpr int NCH = Share<DT, D>::nch;
+    constexpr int NO = StripOut<TPW>::n;
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int q = 0; q < QPW; ++q) {
+        float vv[4 * NO];
+#pragma unroll
+        for (int i = 0; i < 4 * NO; ++i) vv[i] = 0.f;
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            if ((strip * TPW + i) * 16 >= kend) break;
+            f32x4 acc[HT];
+#pragma unroll
+            for (int m = 0; m < HT; ++m) acc[m] = dot_share<DT, NCH>(qa[q][m], kb[i], f32x4{0, 0, 0, 0});
+            vv[i] = head_sum<HT>(acc, wv[q]);
+        }
+        if (!vq[q]) continue;
+        float* row = a.scores + b * a.ld_b + (long long)(tq[q] - a.t_begin) * a.ld_t;
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {
+            const float v = g == 0 ? vv[4 * j] : g == 1 ? vv[4 * j + 1] : g == 2 ? vv[4 * j + 2] : vv[4 * j + 3];
+            const int tile = (strip * TPW + 4 * j + g) * 16;
+            const int key = tile + n;
+            if (4 * j + g < TPW && tile < kend && key < a.Lmax) {
+                if (key <= pq[q])
+                    row[key] = v * ks[j];
+                else if (a.fill)
+                    row[key] = -INFINITY;
+            }
+        }
+    }
+}
+
+// Persistent waves: the W waves of a sequence take strips w, w + W, ...; the
+// loads of the next strip are in flight while the current one is scored.
 template <int DT, int D, int HT, int QPW, int TPW>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a)
 {
     constexpr int NCH = Share<DT, D>::nch;
-    constexpr int EB = ElemBytes<DT>::v;
-    constexpr int CHUNK = 4 * TPW * 16;
-    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
-    const int wave = threadIdx.x >> 6;
+    constexpr int SK = TPW * 16;  // keys per strip
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int b = blockIdx.z;
     const int L = seq_len(a, b);
-    const int chunk0 = blockIdx.x * CHUNK;
 
     int tq[QPW], pq[QPW];
     bool vq[QPW];
@@ -127,51 +207,39 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a)
         pq[q] = vq[q] ? L - a.T + tq[q] : -1;
         kend = max(kend, pq[q] + 1);
     }
+    kend = min(kend, a.Lmax);
 
     u32x4 qa[QPW][HT][NCH];
     float wv[QPW][HT][4];
 #pragma unroll
     for (int q = 0; q < QPW; ++q) load_query<DT, D, HT>(a, b, vq[q] ? tq[q] : a.t_begin, vq[q], qa[q], wv[q]);
 
-    // Issue every key load of this wave's strip first.
-    u32x4 kb[TPW][NCH];
-    const char* kbase = (const char*)a.k + (size_t)b * a.Lmax * D * EB + g * Share<DT, D>::bytes;
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int key = chunk0 + 16 * (wave + 4 * i) + n;
-        const bool ok = key < kend;
-        const char* src = kbase + (size_t)(ok ? key : 0) * D * EB;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) kb[i][c] = ok ? ld16(src + 16 * c) : u32x4{0, 0, 0, 0};
+    const int W = gridDim.x * 4;
+    const int w0 = blockIdx.x * 4 + wave;
+    const int n_load = (kend + SK - 1) / SK;
+    u32x4 kA[TPW][NCH], kB[TPW][NCH];
+    float sA[StripOut<TPW>::n], sB[StripOut<TPW>::n];
+    // Every prefetch is issued unconditionally (past the end a wave re-reads the
+    // strip it holds), so the wait before scoring a strip covers that strip only.
+    if (w0 < n_load) {
+        load_strip<DT, D, TPW>(a, b, w0, kend, kA, sA);
+        for (int s0 = w0;; s0 += 2 * W) {
+            const int s1 = s0 + W;
+            load_strip<DT, D, TPW>(a, b, s1 < n_load ? s1 : s0, kend, kB, sB);
+            score_strip<DT, D, HT, QPW, TPW>(a, b, s0, kA, sA, qa, wv, tq, pq, vq, kend);
+            if (s1 >= n_load) break;
+            const int s2 = s1 + W;
+            load_strip<DT, D, TPW>(a, b, s2 < n_load ? s2 : s1, kend, kA, sA);
+            score_strip<DT, D, HT, QPW, TPW>(a, b, s1, kB, sB, qa, wv, tq, pq, vq, kend);
+            if (s2 >= n_load) break;
+        }
     }
-
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int tile = chunk0 + 16 * (wave + 4 * i);
-        const int key = tile + n;
-        if (tile < kend) {
-            float ks = 1.f;
-            if constexpr (DT == kFP8) ks = (key < kend && g == 0) ? a.k_scale[(size_t)b * a.Lmax + key] : 0.f;
-#pragma unroll
-            for (int q = 0; q < QPW; ++q) {
-                f32x4 acc[HT];
-#pragma unroll
-                for (int m = 0; m < HT; ++m) acc[m] = dot_share<DT, NCH>(qa[q][m], kb[i], f32x4{0, 0, 0, 0});
-                const float v = head_sum<HT>(acc, wv[q]);
-                if (g == 0 && vq[q] && key < a.Lmax) {
-                    float* dst = a.scores + b * a.ld_b + (long long)(tq[q] - a.t_begin) * a.ld_t + key;
-                    if (key <= pq[q])
-                        *dst = v * ks;
-                    else if (a.fill)
-                        *dst = -INFINITY;
-                }
-            }
-        } else if (a.fill && g == 0) {
+    if (a.fill) {  // -inf for every position past the last scored tile
+        const int f0 = (kend + 15) & ~15;
+        for (int s = f0 + (w0 * 64 + lane); s < a.Lmax; s += W * 64)
 #pragma unroll
             for (int q = 0; q < QPW; ++q)
-                if (vq[q] && key < a.Lmax)
-                    a.scores[b * a.ld_b + (long long)(tq[q] - a.t_begin) * a.ld_t + key] = -INFINITY;
-        }
+                if (vq[q]) a.scores[b * a.ld_b + (long long)(tq[q] - a.t_begin) * a.ld_t + s] = -INFINITY;
     }
 }
 
@@ -253,9 +321,10 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs a)
                 const int kb0 = tile0 + 16 * sub;
                 if (kb0 < kend_w) {
                     u32x4 kb[NCH];
-                    const char* rowp = &smem[buf][(16 * sub + n) * PITCH + g * Share<DT, D>::bytes];
+                    const char* rowp = &smem[buf][(16 * sub + n) * PITCH];
 #pragma unroll
-                    for (int c = 0; c < NCH; ++c) kb[c] = *reinterpret_cast<const u32x4*>(rowp + 16 * c);
+                    for (int c = 0; c < NCH; ++c)
+                        kb[c] = *reinterpret_cast<const u32x4*>(rowp + Share<DT, D>::off(g, c));
                     const int key = kb0 + n;
                     float ks = 1.f;
                     if constexpr (DT == kFP8) ks = (g == 0 && key < kend_blk) ? a.k_scale[(size_t)b * a.Lmax + key] : 0.f;
@@ -290,15 +359,19 @@ hipError_t launch_dt(const IndexerArgs& a, hipStream_t s)
 {
     if (a.t_count <= 0 || a.B <= 0) return hipSuccess;
     if (a.t_count <= 2) {
+        constexpr int NCH = Share<DT, D>::nch;
+        // about 2048 resident waves over the whole grid; 8 KB strips keep the
+        // window of rows in flight small (measured best among 4, 8 and 16 KB)
+        const int per_seq = (2048 + 4 * a.B - 1) / (4 * a.B);
         if (a.t_count == 1) {
-            constexpr int TPW = (Share<DT, D>::nch <= 2) ? 16 : 8;
-            constexpr int CHUNK = 4 * TPW * 16;
-            dim3 grid((a.Lmax + CHUNK - 1) / CHUNK, a.t_count, a.B);
+            constexpr int TPW = NCH >= 8 ? 1 : 8 / NCH;
+            const int strips = (a.Lmax + TPW * 16 - 1) / (TPW * 16);
+            dim3 grid(std::max(1, std::min(per_seq, (strips + 3) / 4)), 1, a.B);
             indexer_decode_kernel<DT, D, HT, 1, TPW><<<grid, 256, 0, s>>>(a);
         } else {
-            constexpr int TPW = (Share<DT, D>::nch <= 2) ? 8 : 4;
-            constexpr int CHUNK = 4 * TPW * 16;
-            dim3 grid((a.Lmax + CHUNK - 1) / CHUNK, 1, a.B);
+            constexpr int TPW = NCH >= 8 ? 1 : 8 / NCH;
+            const int strips = (a.Lmax + TPW * 16 - 1) / (TPW * 16);
+            dim3 grid(std::max(1, std::min(per_seq, (strips + 3) / 4)), 1, a.B);
             indexer_decode_kernel<DT, D, HT, 2, TPW><<<grid, 256, 0, s>>>(a);
         }
     } else {

@@ -1,0 +1,56 @@
+"""Host-side checks of bench.py: the one-GPU guard, the algorithmic work model
+and the lookup of recorded HBM traffic (no GPU needed)."""
+import hashlib
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from workloads import get  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_work_of_decode_32k():
+    wl = get("decode_32k")
+    a = bench.algorithmic(wl)
+    # every key of every sequence is scored once: 64 x 32768 keys x 128 dims x 2 bytes
+    assert a["indexer"]["bytes"] >= 64 * 32768 * 128 * 2
+    assert a["indexer"]["flops"] == 2.0 * 64 * 32768 * 64 * 128
+    # 2048 selected rows per query, 128 heads, QK over 576 and PV over 512
+    assert a["mla"]["flops"] == 2.0 * 64 * 2048 * 128 * (576 + 512)
+    assert a["mla"]["bytes"] >= 64 * 2048 * 576 * 2
+
+
+def test_algorithmic_counts_only_causal_pairs():
+    wl = get("tiny_f32")  # 256 queries over 256 keys: 256 * 257 / 2 causal pairs
+    a = bench.algorithmic(wl)
+    assert a["indexer"]["flops"] == 2.0 * (256 * 257 // 2) * wl.idx_heads * wl.idx_dim
+
+
+def test_recorded_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1\n")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    sha = hashlib.sha256(src.read_bytes()).hexdigest()
+    (prof / "x.md").write_text(
+        "# summary\n"
+        f"bench-traffic: workload=decode_32k stage=indexer fetch_bytes=1000 write_bytes=24 source=k.hip sha256={sha}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    wl = get("decode_32k")
+    assert bench.recorded_traffic(wl, "indexer") == 1024
+    assert bench.recorded_traffic(wl, "mla") is None
+    assert bench.recorded_traffic(get("decode_128k_fp8"), "indexer") is None
+    src.write_text("kernel v2\n")  # counters no longer describe this kernel
+    assert bench.recorded_traffic(wl, "indexer") is None

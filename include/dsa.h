@@ -76,7 +76,7 @@ typedef struct {
     int32_t heads;      /* H  MLA query heads, >= 1                                 */
     int32_t qk_dim;     /* D_qk = kv_lora_rank + qk_rope_head_dim (key width)       */
     int32_t v_dim;      /* D_v  = kv_lora_rank (value = first D_v columns of a row) */
-    float sm_scale;     /* softmax scale applied to q . k; no default               */
+    float sm_scale;     /* softmax scale applied to q . k, finite and > 0; no default */
     int32_t idx_dtype;  /* DSA_F32 | DSA_BF16 | DSA_FP8_E4M3                         */
     int32_t mla_dtype;  /* DSA_F32 | DSA_BF16                                        */
 } dsa_shape;

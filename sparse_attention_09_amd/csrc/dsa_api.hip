@@ -50,7 +50,7 @@ dsa_status check_mla_shape(const dsa_shape* s)
 {
     if (s->heads <= 0 || s->qk_dim <= 0 || s->v_dim <= 0 || s->topk <= 0) return DSA_ERR_SHAPE;
     if (s->v_dim > s->qk_dim) return DSA_ERR_SHAPE;
-    if (!isfinite(s->sm_scale)) return DSA_ERR_SHAPE;
+    if (!isfinite(s->sm_scale) || !(s->sm_scale > 0.f)) return DSA_ERR_SHAPE;
     if (s->mla_dtype != DSA_F32 && s->mla_dtype != DSA_BF16) return DSA_ERR_DTYPE;
     if (s->topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
     if (!dsa::mla_supported(s->mla_dtype, s->qk_dim, s->v_dim)) return DSA_ERR_UNSUPPORTED;

@@ -83,33 +83,38 @@ struct Bf16Cfg {
 constexpr int kHeadsPerBlock = 128;  // 4 wave pairs x 32 heads
 constexpr int kMaxListLen = 4096;    // longest index list a split holds in LDS
 
-// Issue this wave's direct loads of index-list tile [j0, j0 + 32) (sanitised in
-// LDS, -1 = skip) into LDS buffer dst: position P holds row P / PCH, chunk
-// P % PCH; the pad chunk and the dummy tail past the tile repeat row 0, so every
-// wave issues exactly DMA_PER_WAVE loads.  Skipped entries fetch row 0 and are
-// masked by the caller.
+// Issue this wave's direct loads of index-list tile [j0, j0 + 32) into LDS
+// buffer dst: position P holds row r = P / PCH, chunk P % PCH; the pad chunk
+// and the dummy tail past the tile fetch row 0, so every wave issues exactly
+// DMA_PER_WAVE loads.  lidx holds row 0 for skipped entries (masked by the
+// caller).  Load k of a wave is position P0 + 512 k, so (r, chunk) advance by a
+// constant step instead of a division per load, and the row address is a
+// 32-bit offset from the sequence's base.
 template <int DQK, int DV>
 __device__ __forceinline__ void gather_tile(const char* kvb, const int* lidx, int j0, int w, int lane, u32x4* dst)
 {
     using C = Bf16Cfg<DQK, DV>;
-    // recompute addresses per load (an opaque lane id keeps them out of the loop's live set)
+    constexpr int DR = 512 / C::PCH, DCH = 512 % C::PCH;
+    // an opaque lane id keeps the per-lane addresses out of the loop's live set
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int wu = __builtin_amdgcn_readfirstlane(w);
+    int r = (wu * 64 + ln) / C::PCH;
+    int c = wu * 64 + ln - r * C::PCH;
 #pragma unroll
     for (int k = 0; k < C::DMA_PER_WAVE; ++k) {
         const int u = wu + 8 * k;
-        const int P = u * 64 + ln;
-        int s = 0, c = 0;
-        if (P < C::TILE_CH) {
-            const int r = P / C::PCH;
-            c = P - r * C::PCH;
-            c = c == C::CPR ? 0 : c;
-            s = lidx[j0 + r];
-            s = s < 0 ? 0 : s;
+        const bool real = r < kTileKeys;
+        const int s = lidx[j0 + (real ? r : 0)];
+        const uint32_t off = (real ? (uint32_t)s * C::ROWB : 0u) + (c == C::CPR ? 0u : (uint32_t)c * 16u);
+        __builtin_amdgcn_global_load_lds(kvb + off, (__attribute__((address_space(3))) void*)(dst + u * 64), 16, 0,
+                                         0);
+        r += DR;
+        c += DCH;
+        if (c >= C::PCH) {
+            c -= C::PCH;
+            ++r;
         }
-        __builtin_amdgcn_global_load_lds(kvb + (size_t)s * C::ROWB + c * 16,
-                                         (__attribute__((address_space(3))) void*)(dst + u * 64), 16, 0, 0);
     }
 }
 
@@ -145,12 +150,14 @@ __device__ __forceinline__ void tile_compute(const u32x4* tile, uint32_t vmask, 
 #pragma unroll
     for (int e = 0; e < 16; ++e) xbuf[w][e][lane] = sacc[e];
     barrier_lds();
-    // lane holds keys 8*i + 4*kb + j (register 4*i + j) of head `col`
+    // lane holds keys 8*i + 4*kb + j (register 4*i + j) of head `col`; the
+    // maximum is taken over q.k (zc > 0 keeps the order) and zc is folded into
+    // the exponent below
     float tmax = -INFINITY;
     if (vmask == 0xFFFFFFFFu) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            sacc[e] = (sacc[e] + xbuf[w ^ 1][e][lane]) * zc;
+            sacc[e] += xbuf[w ^ 1][e][lane];
             tmax = fmaxf(tmax, sacc[e]);
         }
     } else {
@@ -158,11 +165,11 @@ __device__ __forceinline__ void tile_compute(const u32x4* tile, uint32_t vmask, 
         for (int e = 0; e < 16; ++e) {
             const int key = 8 * (e >> 2) + 4 * kb + (e & 3);
             const float sv = sacc[e] + xbuf[w ^ 1][e][lane];
-            sacc[e] = ((vmask >> key) & 1u) ? sv * zc : -INFINITY;
+            sacc[e] = ((vmask >> key) & 1u) ? sv : -INFINITY;
             tmax = fmaxf(tmax, sacc[e]);
         }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * zc;
     // Lazy rescaling: the reference max m_run only moves when a logit exceeds
     // it by more than 8 (log2 units), so p <= 2^8 and O, l stay exact in fp32
     // while the rescale of O is rare.
@@ -178,7 +185,7 @@ __device__ __forceinline__ void tile_compute(const u32x4* tile, uint32_t vmask, 
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        sacc[e] = __builtin_amdgcn_exp2f(sacc[e] - m_use);
+        sacc[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e], zc, -m_use));
         psum += sacc[e];
     }
     st.l_run += psum;
@@ -260,7 +267,7 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
     // plus a validity mask per tile
     for (int j = tid; j < n_tiles * kTileKeys; j += 512) {
         const int sk = valid_key(a, idxr, j_begin + j, j_end, L);
-        lidx[j] = sk;
+        lidx[j] = sk < 0 ? 0 : sk;  // skipped entries fetch row 0; tmask masks them
         const uint64_t bits = __ballot(sk >= 0);  // 64 consecutive entries = two tiles
         if (lane == 0) {
             tmask[j / kTileKeys] = (uint32_t)bits;

@@ -93,8 +93,9 @@ def test_topk_and_mla_reject_bad_arguments(dsa):
     assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == -6
     s = _shape(dsa, mla_dtype="fp8")
     assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == -3
-    s = _shape(dsa, sm_scale=float("nan"))
-    assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == -2
+    for bad_scale in (float("nan"), 0.0, -0.07):
+        s = _shape(dsa, sm_scale=bad_scale)
+        assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == -2
     # decode shapes split the index list and need a workspace
     s = _shape(dsa, batch=4, n_q=1, topk=2048, max_kv=4096)
     assert dsa.sparse_mla_workspace_size(s) > 0

@@ -93,19 +93,25 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-// Sum / max over the four 16-lane groups (lanes l, l^16, l^32, l^48).
+// Sum / max over the four 16-lane groups (lanes l, l^16, l^32, l^48), on the
+// gfx950 row swaps instead of LDS permutes: v_permlane16_swap of a register
+// with itself leaves rows (r0, r0, r2, r2) in one copy and (r1, r1, r3, r3) in
+// the other, v_permlane32_swap does the same for row pairs.  The pairing of the
+// additions is that of the xor-16-then-xor-32 shuffle sum.
 __device__ __forceinline__ float group4_sum(float v)
 {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 __device__ __forceinline__ float group4_max(float v)
 {
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 }  // namespace dsa

@@ -4,14 +4,17 @@
 
 A step is one dsa_forward call (fp8 workloads: q rotation + quantisation,
 index scores, top-k, sparse MLA) over one batch of synthetic inputs already
-resident in HBM.  Decode workloads alternate between two independent input
-sets so that consecutive steps cannot be served from the 256 MB Infinity Cache.
+resident in HBM.  Decode workloads rotate over three independent input sets
+so that consecutive steps cannot be served from the 256 MB Infinity Cache.
 After the timed forward loop, each stage entry point (same launch
 configurations) is timed as back-to-back launches between two HIP events on
-the launch stream; the dominant stage is reported against its roofline, with
-the HBM traffic of its kernel taken from a committed rocprofv3 counter summary
-under profiles/ while the kernel source still matches it.  The CPU oracle is
-timed on a bounded sample of the same workload on the host cores.
+the launch stream; the dominant stage is reported against its roofline (every
+stage's fraction of its own roofline in "stages_frac"), with the HBM traffic of
+its kernel taken from a committed rocprofv3 counter summary under profiles/
+while the kernel source still matches it.  FP8 workloads build the index-key
+cache through the cache-append entry point and report that kernel's bandwidth
+("cache_append"), outside the timed step.  The CPU oracle is timed on a bounded
+sample of the same workload on the host cores.
 
 Prints one JSON line.
 """
@@ -78,6 +81,23 @@ def dominant(wl, stage_us: dict) -> tuple[str, dict]:
                   "work_per_launch": a["bytes"], "avg_launch_us": round(us, 2)}
 
 
+def stage_fractions(wl, stage_us: dict) -> dict:
+    """Each stage's algorithmic work over its duration, as a fraction of the roofline
+    that bounds it (MFMA when its arithmetic intensity is above the ridge, else HBM)."""
+    alg = algorithmic(wl)
+    out = {}
+    for name, us in stage_us.items():
+        a = alg[name]
+        dt = wl.idx_dtype if name == "indexer" else wl.mla_dtype
+        peak_f = PEAK_TFLOPS.get(dt, PEAK_TFLOPS["bf16"])
+        ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+        if name != "topk" and a["flops"] / max(a["bytes"], 1.0) > ridge:
+            out[name] = {"bound": "mfma", "frac": round(a["flops"] / (us * 1e-6) / 1e12 / peak_f, 4)}
+        else:
+            out[name] = {"bound": "hbm", "frac": round(a["bytes"] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
+
+
 class Case:
     """Device inputs, outputs and workspace of one workload."""
 
@@ -88,9 +108,25 @@ class Case:
         inp = make_inputs(wl, device="cuda", seed=seed)
         self.inp = inp
         self.k_idx, self.k_scale = inp["k_idx"], None
+        self.append_us = None
         if wl.idx_dtype == "fp8":
-            self.k_idx, self.k_scale = dsa.rotate_quant_fp8(inp["k_idx"])
-            del inp["k_idx"]
+            # the fp8 index-key cache, built through the cache-append entry point
+            # (every row of every sequence appended at once), timed here
+            k_new = inp["k_idx"]
+            codes = torch.empty(k_new.shape, dtype=torch.uint8, device="cuda")
+            scales = torch.empty(k_new.shape[:2], dtype=torch.float32, device="cuda")
+            full = torch.full((wl.batch,), wl.max_kv, dtype=torch.int32, device="cuda")
+            dsa.index_cache_append_fp8(k_new, full, codes, scales)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 3
+            e0.record()
+            for _ in range(reps):
+                dsa.index_cache_append_fp8(k_new, full, codes, scales)
+            e1.record()
+            torch.cuda.synchronize()
+            self.append_us = e0.elapsed_time(e1) * 1000.0 / reps
+            self.k_idx, self.k_scale = codes, scales
+            del inp["k_idx"], k_new
             q_codes, q_scale = dsa.rotate_quant_fp8(inp["q_idx"])
             self.q_codes, self.q_scale = q_codes, q_scale
         dev = "cuda"
@@ -189,8 +225,13 @@ def recorded_traffic(wl, stage: str):
             kv = dict(x.split("=", 1) for x in line.split()[1:])
             if kv.get("workload") != wl.name or kv.get("stage") != stage:
                 continue
-            src = os.path.join(ROOT, kv["source"])
-            if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["sha256"]:
+            h = hashlib.sha256()
+            for rel in kv["source"].split(","):  # the kernel source and the build script (compile flags)
+                src = os.path.join(ROOT, rel)
+                if not os.path.exists(src):
+                    return None
+                h.update(open(src, "rb").read())
+            if h.hexdigest() != kv["sha256"]:
                 return None
             return int(kv["fetch_bytes"]) + int(kv["write_bytes"])
     return None
@@ -262,7 +303,7 @@ def run(args) -> dict:
     wl = get(args.workload)
     steps = args.steps if args.steps is not None else DEFAULT_STEPS.get(wl.name, 20)
     warmup = args.warmup
-    n_sets = 2 if wl.n_q == 1 else 1
+    n_sets = 3 if wl.n_q == 1 else 1
     cases = [Case(dsa, wl, seed, torch) for seed in range(n_sets)]
     torch.cuda.synchronize()
     ms, wall = time_forward(dsa, torch, cases, steps, warmup)
@@ -284,6 +325,15 @@ def run(args) -> dict:
             res["stages_us"] = {k: round(v, 2) for k, v in st.items()}
             _, roof = dominant(wl, st)
             res["roofline"] = roof
+            res["stages_frac"] = stage_fractions(wl, st)
+    if cases[0].append_us is not None:
+        rows = wl.batch * wl.max_kv
+        nbytes = rows * wl.idx_dim * (2 + 1) + rows * 4  # bf16 keys in, e4m3 codes + f32 scales out
+        gbs = nbytes / (cases[0].append_us * 1e-6) / 1e9
+        res["cache_append"] = {"kernel": "rotate_quant_kernel (index-key cache append)", "rows": rows,
+                               "avg_launch_us": round(cases[0].append_us, 2), "bound": "hbm",
+                               "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(gbs / PEAK_HBM_GBS, 4), "work_per_launch": nbytes}
     del cases
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -141,6 +141,21 @@ dsa_status dsa_sparse_mla_fwd(const dsa_shape* shape, const void* q, const void*
 dsa_status dsa_rotate_quant_fp8(int64_t rows, int32_t dim, const void* x, int32_t x_dtype,
                                 uint8_t* codes, float* scales, hipStream_t stream);
 
+/* Index-key cache update for the FP8 indexer (the cache hook that precedes the
+ * indexer, page item 1): the t_new newest keys of every sequence are rotated and
+ * quantised exactly as by dsa_rotate_quant_fp8 and written into their cache rows.
+ *   k_new  [B, t_new, dim] x_dtype (DSA_F32 or DSA_BF16), dim a power of two, 16..256
+ *   kv_len [B] int32 (device): sequence lengths that already count the new keys;
+ *          key t of sequence b goes to cache row p = kv_len[b] - t_new + t
+ *   codes  [B, max_kv, dim] uint8, scales [B, max_kv] f32 (caller-owned cache,
+ *          updated in place): rows p of the new keys are overwritten, rows with
+ *          p outside [0, max_kv) are skipped, every other row is left as it is.
+ * Errors: batch, t_new or max_kv <= 0 -> DSA_ERR_SHAPE; dim not supported ->
+ * DSA_ERR_UNSUPPORTED; other x_dtype -> DSA_ERR_DTYPE; NULL pointers -> DSA_ERR_NULL. */
+dsa_status dsa_index_cache_append_fp8(int32_t batch, int32_t t_new, int32_t max_kv, int32_t dim,
+                                      const void* k_new, int32_t x_dtype, const int32_t* kv_len,
+                                      uint8_t* codes, float* scales, hipStream_t stream);
+
 /* The whole path: (fp8 only) rotate + quantise q_idx, index scores, top-k,
  * sparse MLA.
  *   q_idx  [B,T,H_I,D_I]: idx_dtype for F32/BF16; for FP8 it is the unrotated

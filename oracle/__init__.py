@@ -146,6 +146,33 @@ def rotate_quant(x):
     return codes, scales
 
 
+def index_cache_append(k_new, kv_len, codes, scales):
+    """Index-key cache update before the indexer (DeepSeek-V3.2 model documentation,
+    "DeepSeek Sparse Attention (DSA)", item 1: the indexer keeps its own key cache,
+    which with the FP8 indexer holds rotated e4m3 codes and row scales).
+
+    The t_new newest keys k_new [B, t_new, D] of sequence b are the cache rows
+    p = kv_len[b] - t_new + t (the newest tokens are the last ones of the
+    sequence); each is rotated and quantised by ``rotate_quant`` and stored there.
+    Rows with p outside [0, max_kv) are skipped.  Returns updated copies of
+    codes [B, max_kv, D] and scales [B, max_kv].
+    """
+    k_new = _f32(k_new)
+    B, t_new, _ = k_new.shape
+    codes = np.array(codes, dtype=np.uint8, copy=True)
+    scales = np.array(scales, dtype=np.float32, copy=True)
+    max_kv = codes.shape[1]
+    kl = np.asarray(kv_len, dtype=np.int64)
+    for b in range(B):
+        for t in range(t_new):
+            p = int(kl[b]) - t_new + t
+            if 0 <= p < max_kv:
+                c, sc = rotate_quant(k_new[b, t][None, :])
+                codes[b, p] = c[0]
+                scales[b, p] = sc[0]
+    return codes, scales
+
+
 def dequant(codes, scales) -> np.ndarray:
     """decode(code) * scale in float64 (one scale per row of the last axis)."""
     return e4m3_decode(codes) * _f32(scales).astype(np.float64)[..., None]

@@ -24,7 +24,7 @@ STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_DTY
           -5: "DSA_ERR_WORKSPACE", -6: "DSA_ERR_UNSUPPORTED", -7: "DSA_ERR_HIP"}
 
 EXPORTS = ["dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_workspace_size",
-           "dsa_sparse_mla_fwd", "dsa_rotate_quant_fp8", "dsa_forward_workspace_size",
+           "dsa_sparse_mla_fwd", "dsa_rotate_quant_fp8", "dsa_index_cache_append_fp8", "dsa_forward_workspace_size",
            "dsa_forward_min_workspace_size", "dsa_forward", "dsa_status_string"]
 
 
@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "dsa_sparse_mla_workspace_size": ([SP], SZ),
             "dsa_sparse_mla_fwd": ([SP, P, P, P, P, P, P, P, SZ, P], I32),
             "dsa_rotate_quant_fp8": ([I64, I32, P, I32, P, P, P], I32),
+            "dsa_index_cache_append_fp8": ([I32, I32, I32, I32, P, I32, P, P, P, P], I32),
             "dsa_forward_workspace_size": ([SP], SZ),
             "dsa_forward_min_workspace_size": ([SP], SZ),
             "dsa_forward": ([SP, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
@@ -193,6 +194,20 @@ def rotate_quant_fp8(x, codes=None, scales=None, stream=None):
         scales = _empty(x.shape[:-1], torch.float32, x.device)
     _check("dsa_rotate_quant_fp8", lib().dsa_rotate_quant_fp8(rows, dim, _ptr(x), xt, _ptr(codes), _ptr(scales),
                                                                _stream(stream)))
+    return codes, scales
+
+
+def index_cache_append_fp8(k_new, kv_len, codes, scales, stream=None):
+    """Rotate + quantise the newest keys k_new [B, t_new, dim] into the fp8 index-key
+    cache codes [B, max_kv, dim] u8 / scales [B, max_kv] f32 (in place) at rows
+    kv_len[b] - t_new + t.  Returns (codes, scales)."""
+    B, t_new, dim = k_new.shape
+    xt = {torch.float32: F32, torch.bfloat16: BF16}[k_new.dtype]
+    if codes.shape[0] != B or codes.shape[2] != dim or tuple(scales.shape) != tuple(codes.shape[:2]):
+        raise ValueError("cache shape mismatch")
+    _check("dsa_index_cache_append_fp8",
+           lib().dsa_index_cache_append_fp8(B, t_new, codes.shape[1], dim, _ptr(k_new), xt, _ptr(kv_len),
+                                            _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
 
 

@@ -65,5 +65,8 @@ hipError_t launch_mla(int dtype, const MlaArgs& a, hipStream_t s);
 
 hipError_t launch_rotate_quant(int64_t rows, int dim, const void* x, int x_dtype, uint8_t* codes, float* scales,
                                hipStream_t s);
+// Rotate + quantise rows [B, t_new, dim] into cache rows kv_len[b] - t_new + t of [B, max_kv, dim].
+hipError_t launch_cache_append(int batch, int t_new, int max_kv, int dim, const void* x, int x_dtype,
+                               const int32_t* kv_len, uint8_t* codes, float* scales, hipStream_t s);
 
 }  // namespace dsa

@@ -125,6 +125,18 @@ def test_rotate_quant_rejects_bad_arguments(dsa):
     assert L.dsa_rotate_quant_fp8(4, 128, None, 1, FAKE, FAKE, None) == -1
 
 
+def test_cache_append_rejects_bad_arguments(dsa):
+    L = dsa.lib()
+    f = L.dsa_index_cache_append_fp8
+    assert f(0, 1, 16, 128, FAKE, 1, FAKE, FAKE, FAKE, None) == -2
+    assert f(2, 0, 16, 128, FAKE, 1, FAKE, FAKE, FAKE, None) == -2
+    assert f(2, 1, 0, 128, FAKE, 1, FAKE, FAKE, FAKE, None) == -2
+    assert f(2, 1, 16, 96, FAKE, 1, FAKE, FAKE, FAKE, None) == -6
+    assert f(2, 1, 16, 128, FAKE, 2, FAKE, FAKE, FAKE, None) == -3
+    assert f(2, 1, 16, 128, FAKE, 1, None, FAKE, FAKE, None) == -1
+    assert f(2, 1, 16, 128, FAKE, 1, FAKE, FAKE, None, None) == -1
+
+
 def test_forward_workspace_sizes_and_checks(dsa):
     from workloads import WORKLOADS
     L = dsa.lib()

@@ -41,16 +41,23 @@ def test_algorithmic_counts_only_causal_pairs():
 def test_recorded_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("kernel v1\n")
+    bld = tmp_path / "build.py"
+    bld.write_text("flags v1\n")
     prof = tmp_path / "profiles"
     prof.mkdir()
-    sha = hashlib.sha256(src.read_bytes()).hexdigest()
+    sha = hashlib.sha256(src.read_bytes() + bld.read_bytes()).hexdigest()
     (prof / "x.md").write_text(
         "# summary\n"
-        f"bench-traffic: workload=decode_32k stage=indexer fetch_bytes=1000 write_bytes=24 source=k.hip sha256={sha}\n")
+        f"bench-traffic: workload=decode_32k stage=indexer fetch_bytes=1000 write_bytes=24 source=k.hip,build.py "
+        f"sha256={sha}\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     wl = get("decode_32k")
     assert bench.recorded_traffic(wl, "indexer") == 1024
     assert bench.recorded_traffic(wl, "mla") is None
     assert bench.recorded_traffic(get("decode_128k_fp8"), "indexer") is None
-    src.write_text("kernel v2\n")  # counters no longer describe this kernel
+    bld.write_text("flags v2\n")  # other compile flags: counters no longer describe this kernel
+    assert bench.recorded_traffic(wl, "indexer") is None
+    bld.write_text("flags v1\n")
+    assert bench.recorded_traffic(wl, "indexer") == 1024
+    src.write_text("kernel v2\n")  # other source: the same
     assert bench.recorded_traffic(wl, "indexer") is None

@@ -43,6 +43,43 @@ def test_rotate_quant_codes_and_scales_exact(dsa, orc, dim, xdt):
     assert np.array_equal(scales.cpu().numpy(), os_)
 
 
+# ------------------------------------------------------ index-key cache append
+@pytest.mark.parametrize("dim,t_new,xdt", [(128, 1, torch.bfloat16), (128, 5, torch.float32), (64, 3, torch.bfloat16),
+                                           (256, 2, torch.float32)])
+def test_cache_append_matches_oracle(dsa, orc, dim, t_new, xdt):
+    g = torch.Generator().manual_seed(dim + t_new)
+    B, max_kv = 5, 50
+    codes0 = torch.randint(0, 256, (B, max_kv, dim), generator=g, dtype=torch.uint8)
+    scales0 = torch.rand(B, max_kv, generator=g)
+    k_new = (torch.randn(B, t_new, dim, generator=g) * torch.exp(torch.randn(B, t_new, 1, generator=g))).to(xdt)
+    k_new[0, 0] = 0  # all-zero row: codes 0, scale 1
+    # full cache, mid cache, only part of the new keys inside the cache, exactly t_new, one key
+    kv_len = torch.tensor([max_kv, 17, max(1, t_new - 1), t_new, 1], dtype=torch.int32)
+    codes, scales = codes0.clone().to(DEV), scales0.clone().to(DEV)
+    dsa.index_cache_append_fp8(k_new.to(DEV), kv_len.to(DEV), codes, scales)
+    torch.cuda.synchronize()
+    oc, os_ = orc.index_cache_append(k_new, kv_len.numpy(), codes0.numpy(), scales0.numpy())
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+
+
+def test_cache_built_by_appends_equals_rotate_quant(dsa, orc):
+    """A cache built one decode step at a time holds the codes of the whole key sequence."""
+    g = torch.Generator().manual_seed(3)
+    B, L, D = 4, 24, 128
+    k = torch.randn(B, L, D, generator=g).bfloat16()
+    codes = torch.zeros(B, L, D, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(B, L, device=DEV)
+    kd = k.to(DEV)
+    for p in range(L):
+        kl = torch.full((B,), p + 1, dtype=torch.int32, device=DEV)
+        dsa.index_cache_append_fp8(kd[:, p:p + 1].contiguous(), kl, codes, scales)
+    torch.cuda.synchronize()
+    oc, os_ = orc.rotate_quant(k)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+
+
 # ------------------------------------------------------------------- indexer
 def _int_inputs(B, T, H, D, Lmax, seed):
     g = torch.Generator().manual_seed(seed)

@@ -144,3 +144,41 @@ def test_rotate_quant_properties(orc):
     deq = orc.dequant(codes, scales)
     err = np.abs(deq - xr)[live]
     assert np.all(err <= np.maximum(np.abs(xr[live]) * 2.0 ** -4, 2.0 ** -10 * amax[live, None] / 448 * 1.01))
+
+
+# ------------------------------------------------------------ cache append
+def test_cache_built_by_appends_equals_one_shot_quantisation(orc):
+    """Appending keys in chunks (kv_len growing with each chunk) must place every
+    row where quantising the whole key sequence at once puts it."""
+    rng = np.random.default_rng(5)
+    B, L, D = 3, 40, 64
+    k = rng.standard_normal((B, L, D)).astype(np.float32)
+    whole_codes, whole_scales = orc.rotate_quant(k)
+    codes = np.zeros((B, L, D), np.uint8)
+    scales = np.zeros((B, L), np.float32)
+    for start, t_new in [(0, 8), (8, 1), (9, 16), (25, 15)]:
+        kv_len = np.full(B, start + t_new, np.int32)
+        codes, scales = orc.index_cache_append(k[:, start:start + t_new], kv_len, codes, scales)
+    assert np.array_equal(codes, whole_codes)
+    assert np.array_equal(scales, whole_scales)
+
+
+def test_cache_append_touches_only_the_new_rows(orc):
+    rng = np.random.default_rng(6)
+    B, max_kv, D, t_new = 3, 20, 32, 4
+    codes0 = rng.integers(0, 256, (B, max_kv, D), dtype=np.uint8)
+    scales0 = rng.random((B, max_kv)).astype(np.float32)
+    k_new = rng.standard_normal((B, t_new, D)).astype(np.float32)
+    # sequence 0 ends at row 12; sequence 1 holds only 2 keys (the two oldest new keys
+    # fall before row 0 and are skipped); sequence 2 fills the cache to its last row
+    kv_len = np.array([13, 2, 20], np.int32)
+    codes, scales = orc.index_cache_append(k_new, kv_len, codes0, scales0)
+    nc, ns = orc.rotate_quant(k_new)
+    expect_rows = {0: {9: 0, 10: 1, 11: 2, 12: 3}, 1: {0: 2, 1: 3}, 2: {16: 0, 17: 1, 18: 2, 19: 3}}
+    for b in range(B):
+        for p in range(max_kv):
+            if p in expect_rows[b]:
+                t = expect_rows[b][p]
+                assert np.array_equal(codes[b, p], nc[b, t]) and scales[b, p] == ns[b, t]
+            else:
+                assert np.array_equal(codes[b, p], codes0[b, p]) and scales[b, p] == scales0[b, p]

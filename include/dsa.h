@@ -137,7 +137,8 @@ dsa_status dsa_sparse_mla_fwd(const dsa_shape* shape, const void* q, const void*
  * are 0 and the scale 1, else codes = e4m3_rne(fp32(x' * fp32(448 / amax))) and
  * scale = fp32(amax / 448).
  *   x      [rows, dim]  x_dtype (DSA_F32 or DSA_BF16), dim a power of two, 16..256
- *   codes  [rows, dim]  uint8 out;  scales [rows] f32 out. */
+ *   codes  [rows, dim]  uint8 out;  scales [rows] f32 out.
+ *   x and codes 16-byte aligned (else DSA_ERR_ALIGN), scales 4-byte aligned. */
 dsa_status dsa_rotate_quant_fp8(int64_t rows, int32_t dim, const void* x, int32_t x_dtype,
                                 uint8_t* codes, float* scales, hipStream_t stream);
 
@@ -151,7 +152,8 @@ dsa_status dsa_rotate_quant_fp8(int64_t rows, int32_t dim, const void* x, int32_
  *          updated in place): rows p of the new keys are overwritten, rows with
  *          p outside [0, max_kv) are skipped, every other row is left as it is.
  * Errors: batch, t_new or max_kv <= 0 -> DSA_ERR_SHAPE; dim not supported ->
- * DSA_ERR_UNSUPPORTED; other x_dtype -> DSA_ERR_DTYPE; NULL pointers -> DSA_ERR_NULL. */
+ * DSA_ERR_UNSUPPORTED; other x_dtype -> DSA_ERR_DTYPE; NULL pointers -> DSA_ERR_NULL;
+ * k_new or codes not 16-byte aligned, kv_len or scales not 4-byte aligned -> DSA_ERR_ALIGN. */
 dsa_status dsa_index_cache_append_fp8(int32_t batch, int32_t t_new, int32_t max_kv, int32_t dim,
                                       const void* k_new, int32_t x_dtype, const int32_t* kv_len,
                                       uint8_t* codes, float* scales, hipStream_t stream);

@@ -297,8 +297,8 @@ DSA_EXPORT dsa_status dsa_rotate_quant_fp8(int64_t rows, int32_t dim, const void
     if (rows <= 0 || dim <= 0) return DSA_ERR_SHAPE;
     if (x_dtype != DSA_F32 && x_dtype != DSA_BF16) return DSA_ERR_DTYPE;
     if (dim < 16 || dim > 256 || (dim & (dim - 1)) != 0) return DSA_ERR_UNSUPPORTED;
-    DSA_TRY(ptr_ok(x, 4));
-    DSA_TRY(ptr_ok(codes, 1));
+    DSA_TRY(ptr_ok(x, 16));
+    DSA_TRY(ptr_ok(codes, 16));
     DSA_TRY(ptr_ok(scales, 4));
     return hip_status(dsa::launch_rotate_quant(rows, dim, x, x_dtype, codes, scales, stream));
 }
@@ -310,9 +310,9 @@ DSA_EXPORT dsa_status dsa_index_cache_append_fp8(int32_t batch, int32_t t_new, i
     if (batch <= 0 || t_new <= 0 || max_kv <= 0) return DSA_ERR_SHAPE;
     if (x_dtype != DSA_F32 && x_dtype != DSA_BF16) return DSA_ERR_DTYPE;
     if (dim < 16 || dim > 256 || (dim & (dim - 1)) != 0) return DSA_ERR_UNSUPPORTED;
-    DSA_TRY(ptr_ok(k_new, 4));
+    DSA_TRY(ptr_ok(k_new, 16));
     DSA_TRY(ptr_ok(kv_len, 4));
-    DSA_TRY(ptr_ok(codes, 1));
+    DSA_TRY(ptr_ok(codes, 16));
     DSA_TRY(ptr_ok(scales, 4));
     return hip_status(dsa::launch_cache_append(batch, t_new, max_kv, dim, k_new, x_dtype, kv_len, codes, scales,
                                                stream));

@@ -9,12 +9,14 @@
 //        scale = fp32(amax / 448).
 // The same transform feeds the index-key cache update that precedes the indexer:
 // a sequence's new key rows are quantised straight into their cache rows.
-// One wave per row.  The transform is the in-place butterfly, carried in fp64
+// The transform is the in-place butterfly, carried in fp64
 // so that its only rounding before the final fp32 is the 1/sqrt(dim) scaling;
 // the fp32 divisions are correctly rounded.  e4m3 (OCP E4M3FN: bias 7, max 448,
 // no infinities) is encoded from the fp32 bit pattern with round-half-even.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
+
+#include <algorithm>
 
 namespace dsa {
 namespace {
@@ -57,73 +59,91 @@ struct RowMap {
     }
 };
 
+// Lane layout: each lane holds 8 consecutive elements of a row (element index
+// i = 8 * li + j for lane li of the row's LPR = DIM / 8 lanes), a wave holds
+// 64 / LPR rows.  The butterfly stages h = 1, 2, 4 pair elements inside a lane,
+// the stages h >= 8 pair lanes li and li ^ (h / 8) of the same row.  Stages run
+// in increasing h with the same pairing and signs whatever the layout, so every
+// element goes through the same fp64 operations as in the plain transform.
 template <int DIM, int XT>
 __global__ __launch_bounds__(256) void rotate_quant_kernel(int64_t rows, const void* x, uint8_t* codes,
                                                            float* scales, double inv_sqrt_dim, RowMap map)
 {
-    constexpr int E = DIM >= 64 ? DIM / 64 : 1;   // elements per lane: index e*64 + lane
-    const int lane = lane_id();
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    const int64_t orow = map(row);
-    if (orow < 0) return;
-    double v[E];
+    constexpr int LPR = DIM / 8;   // lanes per row
+    constexpr int RPW = 64 / LPR;  // rows per wave
+    static_assert(DIM % 8 == 0 && LPR >= 1 && LPR <= 64, "dim");
+    const int lane = lane_id(), li = lane % LPR, grp = lane / LPR;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t n_waves = (int64_t)gridDim.x * 4;
+    for (int64_t row0 = wave * RPW; row0 < rows; row0 += n_waves * RPW) {
+        const int64_t row = row0 + grp;
+        const int64_t orow = row < rows ? map(row) : -1;
+        double v[8];
+        if (orow >= 0) {
+            if constexpr (XT == kBF16) {
+                const u32x4 raw = ld16((const uint16_t*)x + row * DIM + 8 * li);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int i = e * 64 + lane;
-        float xv = 0.f;
-        if (i < DIM) {
-            if constexpr (XT == kBF16)
-                xv = bf16_to_f32(((const uint16_t*)x)[row * DIM + i]);
-            else
-                xv = ((const float*)x)[row * DIM + i];
-        }
-        v[e] = (double)xv;
-    }
-    // butterfly over every bit of the element index
+                for (int k = 0; k < 4; ++k) {
+                    v[2 * k] = (double)__uint_as_float(raw[k] << 16);
+                    v[2 * k + 1] = (double)__uint_as_float(raw[k] & 0xFFFF0000u);
+                }
+            } else {
+                const u32x4 r0 = ld16((const float*)x + row * DIM + 8 * li);
+                const u32x4 r1 = ld16((const float*)x + row * DIM + 8 * li + 4);
 #pragma unroll
-    for (int h = 1; h < DIM; h <<= 1) {
-        if (h < 64) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const double o = __shfl_xor(v[e], h, 64);
-                v[e] = (lane & h) ? (o - v[e]) : (v[e] + o);
+                for (int k = 0; k < 4; ++k) {
+                    v[k] = (double)__uint_as_float(r0[k]);
+                    v[4 + k] = (double)__uint_as_float(r1[k]);
+                }
             }
         } else {
-            const int he = h / 64;
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                if (e & he) continue;
-                const double a0 = v[e], b0 = v[e + he];
-                v[e] = a0 + b0;
-                v[e + he] = a0 - b0;
+            for (int k = 0; k < 8; ++k) v[k] = 0.0;
+        }
+#pragma unroll
+        for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (k & h) continue;
+                const double a0 = v[k], b0 = v[k + h];
+                v[k] = a0 + b0;
+                v[k + h] = a0 - b0;
             }
+#pragma unroll
+        for (int hl = 1; hl < LPR; hl <<= 1)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const double o = __shfl_xor(v[k], hl, 64);
+                v[k] = (li & hl) ? (o - v[k]) : (v[k] + o);
+            }
+        float xf[8];
+        float amax = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            xf[k] = (float)(v[k] * inv_sqrt_dim);
+            amax = fmaxf(amax, fabsf(xf[k]));
+        }
+#pragma unroll
+        for (int hl = 1; hl < LPR; hl <<= 1) amax = fmaxf(amax, __shfl_xor(amax, hl, 64));
+        if (orow >= 0) {
+            const bool zero = amax == 0.f;
+            const float r = zero ? 0.f : 448.f / amax;
+            uint32_t packed[2] = {0u, 0u};
+            if (!zero)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) packed[k >> 2] |= (uint32_t)e4m3_encode(xf[k] * r) << (8 * (k & 3));
+            *reinterpret_cast<u32x2*>(codes + orow * DIM + 8 * li) = u32x2{packed[0], packed[1]};
+            if (li == 0) scales[orow] = zero ? 1.f : amax / 448.f;
         }
     }
-    float xf[E];
-    float amax = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const bool live = e * 64 + lane < DIM;
-        xf[e] = (float)(v[e] * inv_sqrt_dim);
-        if (live) amax = fmaxf(amax, fabsf(xf[e]));
-    }
-    amax = wave_max(amax);
-    const bool zero = amax == 0.f;
-    const float r = zero ? 0.f : 448.f / amax;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int i = e * 64 + lane;
-        if (i < DIM) codes[orow * DIM + i] = zero ? (uint8_t)0 : e4m3_encode(xf[e] * r);
-    }
-    if (lane == 0) scales[orow] = zero ? 1.f : amax / 448.f;
 }
 
 template <int DIM>
 hipError_t launch_dim(int64_t rows, const void* x, int xt, uint8_t* codes, float* scales, RowMap map, hipStream_t s)
 {
     const double inv = 1.0 / sqrt((double)DIM);
-    const dim3 grid((unsigned)((rows + 3) / 4));
+    constexpr int RPB = 4 * (64 / (DIM / 8));  // rows per block pass
+    const dim3 grid((unsigned)std::min<int64_t>((rows + RPB - 1) / RPB, 8192));
     if (xt == kBF16)
         rotate_quant_kernel<DIM, kBF16><<<grid, 256, 0, s>>>(rows, x, codes, scales, inv, map);
     else

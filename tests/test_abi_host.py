@@ -135,6 +135,9 @@ def test_cache_append_rejects_bad_arguments(dsa):
     assert f(2, 1, 16, 128, FAKE, 2, FAKE, FAKE, FAKE, None) == -3
     assert f(2, 1, 16, 128, FAKE, 1, None, FAKE, FAKE, None) == -1
     assert f(2, 1, 16, 128, FAKE, 1, FAKE, FAKE, None, None) == -1
+    assert f(2, 1, 16, 128, FAKE + 4, 1, FAKE, FAKE, FAKE, None) == -4
+    assert f(2, 1, 16, 128, FAKE, 1, FAKE, FAKE + 8, FAKE, None) == -4
+    assert L.dsa_rotate_quant_fp8(4, 128, FAKE + 4, 1, FAKE, FAKE, None) == -4
 
 
 def test_forward_workspace_sizes_and_checks(dsa):

@@ -50,6 +50,7 @@ struct TopkShared {
     int base_sel[kTopkWaves];
     uint32_t sel_digit;
     int sel_above;
+    uint32_t scan_tmp[kTopkWaves];
 };
 
 struct FinishShared {
@@ -65,6 +66,7 @@ struct FinishShared {
     uint32_t sel_digit;
     int sel_above;
     int n_out;
+    uint32_t scan_tmp[kTopkWaves];
 };
 
 static_assert(2 * kCandCap * 32 >= (1 << 20), "bitmap must cover the longest row");
@@ -74,64 +76,80 @@ union TopkUnion {
     FinishShared fin;
 };
 
-// Wave 0 scans hist[0..nbins) from the top for the bin holding the k-th
-// largest element: writes its digit and the count strictly above it.
-__device__ __forceinline__ void find_digit_desc(const uint32_t* hist, int nbins, uint32_t k, uint32_t* digit,
-                                                int* above_out)
+// Block-wide versions (all NT threads call them; they end with a barrier, after
+// which every thread may read *digit and *count): thread t owns bins
+// [t*per, (t+1)*per), the per-thread sums are scanned across waves through
+// tmp (NT/64 words of LDS), and the one thread whose range holds the k-th
+// element walks its bins.
+template <int NT>
+__device__ __forceinline__ void block_find_desc(const uint32_t* hist, int nbins, uint32_t k, uint32_t* tmp,
+                                                uint32_t* digit, int* above_out)
 {
-    const int lane = lane_id();
-    const int per = nbins / 64;
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int per = nbins >= NT ? nbins / NT : 1;
+    const int b0 = tid * per;
     uint32_t s = 0;
-    for (int j = 0; j < per; ++j) s += hist[lane * per + j];
-    uint32_t incl = s;  // suffix sum over lanes >= lane
+    if (b0 < nbins)
+        for (int j = 0; j < per; ++j) s += hist[b0 + j];
+    uint32_t incl = s;  // suffix sum over this wave's lanes >= lane
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const uint32_t o = __shfl_down(incl, off, 64);
         if (lane + off < 64) incl += o;
     }
+    if (lane == 0) tmp[wave] = incl;
+    __syncthreads();
+    for (int v = wave + 1; v < NW; ++v) incl += tmp[v];
     const uint32_t excl = incl - s;
     if (excl < k && incl >= k) {
         uint32_t above = excl;
         for (int j = per - 1; j >= 0; --j) {
-            const uint32_t h = hist[lane * per + j];
+            const uint32_t h = hist[b0 + j];
             if (above + h >= k) {
-                *digit = (uint32_t)(lane * per + j);
+                *digit = (uint32_t)(b0 + j);
                 *above_out = (int)above;
                 break;
             }
             above += h;
         }
     }
+    __syncthreads();
 }
 
-// The same from the bottom: the bin holding the k-th smallest element and the
-// count strictly below it.
-__device__ __forceinline__ void find_digit_asc(const uint32_t* hist, int nbins, uint32_t k, uint32_t* digit,
-                                               int* below_out)
+template <int NT>
+__device__ __forceinline__ void block_find_asc(const uint32_t* hist, int nbins, uint32_t k, uint32_t* tmp,
+                                               uint32_t* digit, int* below_out)
 {
-    const int lane = lane_id();
-    const int per = nbins / 64;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int per = nbins >= NT ? nbins / NT : 1;
+    const int b0 = tid * per;
     uint32_t s = 0;
-    for (int j = 0; j < per; ++j) s += hist[lane * per + j];
-    uint32_t incl = s;  // prefix sum over lanes <= lane
+    if (b0 < nbins)
+        for (int j = 0; j < per; ++j) s += hist[b0 + j];
+    uint32_t incl = s;  // prefix sum over this wave's lanes <= lane
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const uint32_t o = __shfl_up(incl, off, 64);
         if (lane >= off) incl += o;
     }
+    if (lane == 63) tmp[wave] = incl;
+    __syncthreads();
+    for (int v = 0; v < wave; ++v) incl += tmp[v];
     const uint32_t excl = incl - s;
     if (excl < k && incl >= k) {
         uint32_t below = excl;
         for (int j = 0; j < per; ++j) {
-            const uint32_t h = hist[lane * per + j];
+            const uint32_t h = hist[b0 + j];
             if (below + h >= k) {
-                *digit = (uint32_t)(lane * per + j);
+                *digit = (uint32_t)(b0 + j);
                 *below_out = (int)below;
                 break;
             }
             below += h;
         }
     }
+    __syncthreads();
 }
 
 struct RowKeys {
@@ -163,8 +181,7 @@ __device__ void block_select(TopkShared& sh, const float* src, int n, int K, int
             if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & (nbins - 1)], 1u);
         }
         __syncthreads();
-        if (wave == 0) find_digit_desc(sh.hist, nbins, (uint32_t)krem, &sh.sel_digit, &sh.sel_above);
-        __syncthreads();
+        block_find_desc<kTopkThreads>(sh.hist, nbins, (uint32_t)krem, sh.scan_tmp, &sh.sel_digit, &sh.sel_above);
         krem -= sh.sel_above;
         prefix |= sh.sel_digit << shift;
         pmask |= (uint32_t)(nbins - 1) << shift;
@@ -321,6 +338,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a)
     __shared__ uint32_t sh_digit;
     __shared__ int sh_above;
     __shared__ uint32_t wtot[2][4];
+    __shared__ uint32_t sh_tmp[4];
     __shared__ uint32_t gbase[2];
     int b, t, n;
     row_of(a, blockIdx.y, b, t, n);
@@ -340,8 +358,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a)
     }
     for (int i = tid; i < kHistBins; i += 256) lh[i] = w.hist[row * kHistBins + i];
     __syncthreads();
-    if (wave == 0) find_digit_desc(lh, kHistBins, (uint32_t)a.K, &sh_digit, &sh_above);
-    __syncthreads();
+    block_find_desc<256>(lh, kHistBins, (uint32_t)a.K, sh_tmp, &sh_digit, &sh_above);
     const uint32_t d1 = sh_digit;
     uint32_t ns = 0, nc = 0;
 #pragma unroll
@@ -436,8 +453,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_finish_kernel(TopkArgs a)
             if ((k & pmask) == prefix) atomicAdd(&f.hist[(k >> shift) & 1023u], 1u);
         }
         __syncthreads();
-        if (wave == 0) find_digit_desc(f.hist, 1024, (uint32_t)need, &f.sel_digit, &f.sel_above);
-        __syncthreads();
+        block_find_desc<kTopkThreads>(f.hist, 1024, (uint32_t)need, f.scan_tmp, &f.sel_digit, &f.sel_above);
         need -= f.sel_above;
         prefix |= f.sel_digit << shift;
         pmask |= 1023u << shift;
@@ -461,8 +477,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_finish_kernel(TopkArgs a)
                 if ((f.ckey[i] & 0xFFFFFu) == tau_low && (p & im) == ip) atomicAdd(&f.hist[(p >> shift) & 1023u], 1u);
             }
             __syncthreads();
-            if (wave == 0) find_digit_asc(f.hist, 1024, (uint32_t)k2, &f.sel_digit, &f.sel_above);
-            __syncthreads();
+            block_find_asc<kTopkThreads>(f.hist, 1024, (uint32_t)k2, f.scan_tmp, &f.sel_digit, &f.sel_above);
             k2 -= f.sel_above;
             ip |= f.sel_digit << shift;
             im |= 1023u << shift;

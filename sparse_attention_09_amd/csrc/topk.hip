@@ -160,12 +160,28 @@ struct RowKeys {
 
 // Whole-row select by one 1024-thread workgroup (n > K): radix select of the
 // K-th largest key, then an ordered compaction writing ascending positions.
+// Keys are read in batches of kBatch per thread (loads first, then use), so a
+// thread has kBatch reads in flight instead of waiting on each one; reads past
+// the end are clamped to the last key and ignored.
+constexpr int kBatch = 8;
+
 __device__ void block_select(TopkShared& sh, const float* src, int n, int K, int32_t* dst)
 {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const bool staged = n <= kTopkStageMax;
-    if (staged)
-        for (int i = tid; i < n; i += kTopkThreads) sh.keys[i] = float_key(src[i]);
+    if (staged) {
+        for (int base = 0; base < n; base += kTopkThreads * kBatch) {
+            float v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) v[u] = src[min(base + u * kTopkThreads + tid, n - 1)];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int i = base + u * kTopkThreads + tid;
+                if (i < n) sh.keys[i] = float_key(v[u]);
+            }
+        }
+        __syncthreads();
+    }
     const RowKeys key_at{src, staged ? sh.keys : nullptr};
 
     uint32_t prefix = 0, pmask = 0;
@@ -176,9 +192,14 @@ __device__ void block_select(TopkShared& sh, const float* src, int n, int K, int
         const int nbins = pass == 2 ? 256 : 4096;
         for (int i = tid; i < nbins; i += kTopkThreads) sh.hist[i] = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += kTopkThreads) {
-            const uint32_t k = key_at(i);
-            if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & (nbins - 1)], 1u);
+        for (int base = 0; base < n; base += kTopkThreads * kBatch) {
+            uint32_t kk[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) kk[u] = key_at(min(base + u * kTopkThreads + tid, n - 1));
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (base + u * kTopkThreads + tid < n && (kk[u] & pmask) == prefix)
+                    atomicAdd(&sh.hist[(kk[u] >> shift) & (nbins - 1)], 1u);
         }
         __syncthreads();
         block_find_desc<kTopkThreads>(sh.hist, nbins, (uint32_t)krem, sh.scan_tmp, &sh.sel_digit, &sh.sel_above);
@@ -192,11 +213,16 @@ __device__ void block_select(TopkShared& sh, const float* src, int n, int K, int
     const int seg = ((n + kTopkWaves - 1) / kTopkWaves + 63) & ~63;
     const int s0 = min(n, wave * seg), s1 = min(n, s0 + seg);
     int gt = 0, eq = 0;
-    for (int i0 = s0; i0 < s1; i0 += 64) {
-        const int i = i0 + lane;
-        const uint32_t k = i < s1 ? key_at(i) : 0u;
-        gt += __popcll(__ballot(i < s1 && k > tau));
-        eq += __popcll(__ballot(i < s1 && k == tau));
+    for (int i0 = s0; i0 < s1; i0 += 64 * kBatch) {
+        uint32_t kk[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) kk[u] = key_at(min(i0 + 64 * u + lane, n - 1));
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const bool in = i0 + 64 * u + lane < s1;
+            gt += __popcll(__ballot(in && kk[u] > tau));
+            eq += __popcll(__ballot(in && kk[u] == tau));
+        }
     }
     if (lane == 0) {
         sh.cnt_gt[wave] = gt;
@@ -216,18 +242,23 @@ __device__ void block_select(TopkShared& sh, const float* src, int n, int K, int
     __syncthreads();
     int run_eq = sh.base_eq[wave], run_sel = sh.base_sel[wave];
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int i0 = s0; i0 < s1; i0 += 64) {
-        const int i = i0 + lane;
-        const uint32_t k = i < s1 ? key_at(i) : 0u;
-        const bool is_gt = i < s1 && k > tau;
-        const bool is_eq = i < s1 && k == tau;
-        const uint64_t meq = __ballot(is_eq);
-        const int eq_rank = run_eq + __popcll(meq & below);
-        const bool sel = is_gt || (is_eq && eq_rank < krem);
-        const uint64_t msel = __ballot(sel);
-        if (sel) dst[run_sel + __popcll(msel & below)] = i;
-        run_eq += __popcll(meq);
-        run_sel += __popcll(msel);
+    for (int i0 = s0; i0 < s1; i0 += 64 * kBatch) {
+        uint32_t kk[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) kk[u] = key_at(min(i0 + 64 * u + lane, n - 1));
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = i0 + 64 * u + lane;
+            const bool is_gt = i < s1 && kk[u] > tau;
+            const bool is_eq = i < s1 && kk[u] == tau;
+            const uint64_t meq = __ballot(is_eq);
+            const int eq_rank = run_eq + __popcll(meq & below);
+            const bool sel = is_gt || (is_eq && eq_rank < krem);
+            const uint64_t msel = __ballot(sel);
+            if (sel) dst[run_sel + __popcll(msel & below)] = i;
+            run_eq += __popcll(meq);
+            run_sel += __popcll(msel);
+        }
     }
 }
 
@@ -307,9 +338,16 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a)
     const int c1 = min(n, c0 + kChunk);
     const SplitWs w = split_ws(a);
     const float* src = row_scores(a, b, t);
+    // all of this thread's keys are loaded before the first histogram update
+    constexpr int PER = kChunk / 256;
+    float v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[j] = src[min(c0 + (int)threadIdx.x + 256 * j, c1 - 1)];
     for (int i = threadIdx.x; i < kHistBins; i += 256) lh[i] = 0u;
     __syncthreads();
-    for (int i = c0 + threadIdx.x; i < c1; i += 256) atomicAdd(&lh[float_key(src[i]) >> 20], 1u);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (c0 + (int)threadIdx.x + 256 * j < c1) atomicAdd(&lh[float_key(v[j]) >> 20], 1u);
     __syncthreads();
     uint32_t* gh = w.hist + (size_t)blockIdx.y * kHistBins;
     for (int i = threadIdx.x; i < kHistBins; i += 256) {

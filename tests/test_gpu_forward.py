@@ -149,3 +149,48 @@ def test_forward_ragged_lengths(dsa, orc):
     idx, out, lse, _, _ = _run(dsa, wl, inp)
     rows = list(range(wl.rows))
     _check(orc, wl, _oracle_inputs(inp, wl, rows), rows, idx.cpu(), out.cpu(), lse.cpu())
+
+
+@pytest.mark.parametrize("name", ["decode_32k", "decode_128k_fp8", "prefill_4k"])
+def test_forward_graph_replay_matches_eager(dsa, name):
+    """dsa_forward captured in a HIP graph (as a serving loop would replay it) gives the
+    eager result on every replay, with eager work and synchronisation between replays."""
+    wl = get(name)
+    if wl.batch > 16:
+        wl = wl.replace(batch=16)
+    inp = make_inputs(wl, device=DEV)
+    s = dsa.DsaShape.of(wl)
+    k_idx, k_scale = _prepare(dsa, wl, inp)
+    B, T = wl.batch, wl.n_q
+    idx = torch.empty((B, T, wl.topk), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, T, wl.heads, wl.v_dim), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, T, wl.heads), dtype=torch.float32, device=DEV)
+    ws = torch.empty((dsa.forward_workspace_size(s),), dtype=torch.uint8, device=DEV)
+
+    def step():
+        dsa.forward(s, inp["q_idx"], inp["w"], k_idx, inp["q"], inp["kv"], inp["kv_len"], k_scale=k_scale,
+                    idx_out=idx, out=out, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (idx.clone(), out.clone(), lse.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        idx.fill_(-7)
+        out.zero_()
+        lse.zero_()
+        ws.fill_(0xAB)  # scratch holds garbage between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[0]), f"replay {rep}: idx"
+        assert torch.equal(out, ref[1]), f"replay {rep}: out"
+        assert torch.equal(lse, ref[2]), f"replay {rep}: lse"

@@ -17,10 +17,12 @@
 // Few long rows (decode): the row is split over 4096-entry chunks so the whole
 // GPU works on it.
 //   hist   : each chunk histograms the top 12 bits of its keys in LDS and adds
-//            the non-zero bins to the row's global histogram;
-//   filter : each chunk finds the bin d1 holding the K-th largest key from that
-//            histogram, appends keys above d1 to the row's "selected" list and
-//            keys in d1 to its "candidate" list (wave-aggregated atomics);
+//            the non-zero bins to the row's global histogram, and its sums over
+//            the top 6 bits to the row's 64-bin coarse histogram;
+//   filter : each chunk finds the bin d1 holding the K-th largest key (the
+//            coarse bin from 64 words, then the fine bin from that bin's 64
+//            words), appends keys above d1 to the row's "selected" list and keys
+//            in d1 to its "candidate" list (one reservation per workgroup);
 //   finish : one workgroup per row resolves the candidates in LDS (radix select
 //            on the low 20 bits, then smallest positions among equal keys),
 //            merges them with the selected list and sorts the K positions.
@@ -294,8 +296,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a)
 }
 
 // ------------------------------------------------------------ split path
+constexpr int kCoarse = 64;  // coarse bins: the top 6 key bits (64 fine bins each)
+
 struct SplitWs {
     uint32_t* hist;  // [rows][4096]
+    uint32_t* coarse;  // [rows][64]
     uint32_t* cnt;   // [rows][4]: selected count, candidate count
     int32_t* sel;    // [rows][K]
     uint2* cand;     // [rows][kCandCap] (key, position)
@@ -308,6 +313,8 @@ __device__ __forceinline__ SplitWs split_ws(const TopkArgs& a)
     SplitWs w;
     w.hist = (uint32_t*)p;
     p += rows * kHistBins * 4;
+    w.coarse = (uint32_t*)p;
+    p += rows * kCoarse * 4;
     w.cnt = (uint32_t*)p;
     p += rows * 4 * 4;
     w.sel = (int32_t*)p;
@@ -318,10 +325,10 @@ __device__ __forceinline__ SplitWs split_ws(const TopkArgs& a)
 
 size_t split_ws_bytes(size_t rows, int K)
 {
-    return rows * (kHistBins * 4 + 16 + (size_t)K * 4 + (size_t)kCandCap * 8);
+    return rows * ((kHistBins + kCoarse) * 4 + 16 + (size_t)K * 4 + (size_t)kCandCap * 8);
 }
 
-size_t split_zero_words(size_t rows) { return rows * (kHistBins + 4); }
+size_t split_zero_words(size_t rows) { return rows * (kHistBins + kCoarse + 4); }
 
 __global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* p, size_t n)
 {
@@ -354,6 +361,30 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a)
         const uint32_t v = lh[i];
         if (v) atomicAdd(&gh[i], v);
     }
+    // coarse bins: thread t sums fine bins [16t, 16t + 16), four threads per coarse bin
+    uint32_t cs = 0;
+#pragma unroll
+    for (int j = 0; j < kHistBins / 256; ++j) cs += lh[threadIdx.x * (kHistBins / 256) + j];
+    cs += __shfl_xor(cs, 1, 64);
+    cs += __shfl_xor(cs, 2, 64);
+    if ((threadIdx.x & 3) == 0 && cs) atomicAdd(&w.coarse[(size_t)blockIdx.y * kCoarse + threadIdx.x / 4], cs);
+}
+
+// Wave-level search over 64 bins held one per lane (bin = lane), from the top:
+// the lane whose bin holds the k-th largest element, and the count above it.
+__device__ __forceinline__ void wave_find_desc64(uint32_t h, uint32_t k, int& bin, uint32_t& above)
+{
+    const int lane = lane_id();
+    uint32_t incl = h;  // suffix sum over lanes >= lane
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_down(incl, off, 64);
+        if (lane + off < 64) incl += o;
+    }
+    const uint32_t excl = incl - h;
+    const uint64_t hit = __ballot(excl < k && incl >= k);
+    bin = hit ? (int)__builtin_ctzll(hit) : 0;
+    above = __shfl(excl, bin, 64);
 }
 
 // Inclusive scan over the 64 lanes of a wave.
@@ -372,11 +403,8 @@ constexpr int kFilterPer = kChunk / 256;  // keys per thread in the filter pass
 
 __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a)
 {
-    __shared__ uint32_t lh[kHistBins];
     __shared__ uint32_t sh_digit;
-    __shared__ int sh_above;
     __shared__ uint32_t wtot[2][4];
-    __shared__ uint32_t sh_tmp[4];
     __shared__ uint32_t gbase[2];
     int b, t, n;
     row_of(a, blockIdx.y, b, t, n);
@@ -387,16 +415,20 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a)
     const size_t row = blockIdx.y;
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const float* src = row_scores(a, b, t);
-    // keys of this thread: c0 + tid + 256 * j (loads in flight while the threshold is found)
+    // keys of this thread: c0 + tid + 256 * j, loaded while the threshold is found (reads
+    // past the chunk are clamped to its last key and ignored)
     uint32_t key[kFilterPer];
 #pragma unroll
-    for (int j = 0; j < kFilterPer; ++j) {
-        const int i = c0 + tid + 256 * j;
-        key[j] = i < c1 ? float_key(src[i]) : 0u;
+    for (int j = 0; j < kFilterPer; ++j) key[j] = float_key(src[min(c0 + tid + 256 * j, c1 - 1)]);
+    // the bin d1 of the K-th largest key: coarse bin first (64 words), then its 64 fine bins
+    if (wave == 0) {
+        int cb, fb;
+        uint32_t above_c, above_f;
+        wave_find_desc64(w.coarse[row * kCoarse + lane], (uint32_t)a.K, cb, above_c);
+        wave_find_desc64(w.hist[row * kHistBins + cb * 64 + lane], (uint32_t)a.K - above_c, fb, above_f);
+        if (lane == 0) sh_digit = (uint32_t)(cb * 64 + fb);
     }
-    for (int i = tid; i < kHistBins; i += 256) lh[i] = w.hist[row * kHistBins + i];
     __syncthreads();
-    block_find_desc<256>(lh, kHistBins, (uint32_t)a.K, sh_tmp, &sh_digit, &sh_above);
     const uint32_t d1 = sh_digit;
     uint32_t ns = 0, nc = 0;
 #pragma unroll

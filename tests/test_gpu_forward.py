@@ -194,3 +194,14 @@ def test_forward_graph_replay_matches_eager(dsa, name):
         assert torch.equal(idx, ref[0]), f"replay {rep}: idx"
         assert torch.equal(out, ref[1]), f"replay {rep}: out"
         assert torch.equal(lse, ref[2]), f"replay {rep}: lse"
+
+
+def test_forward_largest_cache_and_topk(dsa, orc):
+    """The largest supported shape: a 2^20-key cache and index_topk = 4096 (top-k over
+    256 chunks, positions that need all 20 bits, 16-way split MLA)."""
+    wl = get("decode_32k").replace(batch=1, max_kv=1 << 20, kv_len=1 << 20, topk=4096)
+    inp = make_inputs(wl, device=DEV)
+    announce("largest cache: 1 x 2^20 keys, K = 4096")
+    idx, out, lse, _, _ = _run(dsa, wl, inp)
+    assert int(idx.max()) >= 1 << 19  # positions that need the top position bit are selected
+    _check(orc, wl, _oracle_inputs(inp, wl, [0]), [0], idx.cpu(), out.cpu(), lse.cpu())

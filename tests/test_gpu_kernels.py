@@ -177,6 +177,7 @@ TOPK_CASES = [
     (3, 1, 20000, [20000, 2048, 1], 2048),
     (2, 1, 9000, [9000, 8500], 1000),     # K not a power of two
     (1, 1, 131072, [131072], 2048),
+    (2, 1, 70000, [70000, 5000], 4096),   # the largest K
 ]
 
 

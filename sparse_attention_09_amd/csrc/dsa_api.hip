@@ -117,7 +117,7 @@ dsa::TopkArgs topk_args(const dsa_shape* s, const float* scores, const int32_t* 
 }
 
 dsa::MlaArgs mla_args(const dsa_shape* s, const void* q, const void* kv, const int32_t* idx, const int32_t* kv_len,
-                      void* out, float* lse, float* part, int t_begin, int t_count, int n_split)
+                      void* out, float* lse, void* part, int t_begin, int t_count, int n_split)
 {
     dsa::MlaArgs a;
     a.B = s->batch;
@@ -144,7 +144,7 @@ dsa::MlaArgs mla_args(const dsa_shape* s, const void* q, const void* kv, const i
 size_t mla_ws(const dsa_shape* s, int t_count)
 {
     const int ns = dsa::mla_split_count(s->batch, t_count, s->heads, s->topk);
-    return dsa::mla_partial_bytes(s->batch, t_count, s->heads, s->v_dim, ns);
+    return dsa::mla_partial_bytes(s->mla_dtype, s->batch, t_count, s->heads, s->v_dim, ns);
 }
 
 // Workspace layout of dsa_forward for a query chunk of tc rows.  The top-k
@@ -282,12 +282,12 @@ DSA_EXPORT dsa_status dsa_sparse_mla_fwd(const dsa_shape* s, const void* q, cons
     DSA_TRY(ptr_ok(out, 16));
     if (lse && !aligned(lse, 4)) return DSA_ERR_ALIGN;
     const int ns = dsa::mla_split_count(s->batch, s->n_q, s->heads, s->topk);
-    const size_t need = dsa::mla_partial_bytes(s->batch, s->n_q, s->heads, s->v_dim, ns);
+    const size_t need = dsa::mla_partial_bytes(s->mla_dtype, s->batch, s->n_q, s->heads, s->v_dim, ns);
     if (need > 0) {
         if (!workspace || ws_bytes < need) return DSA_ERR_WORKSPACE;
         if (!aligned(workspace, 16)) return DSA_ERR_ALIGN;
     }
-    const dsa::MlaArgs a = mla_args(s, q, kv, idx, kv_len, out, lse, (float*)workspace, 0, s->n_q, ns);
+    const dsa::MlaArgs a = mla_args(s, q, kv, idx, kv_len, out, lse, workspace, 0, s->n_q, ns);
     return hip_status(dsa::launch_mla(s->mla_dtype, a, stream));
 }
 
@@ -359,7 +359,7 @@ DSA_EXPORT dsa_status dsa_forward(const dsa_shape* s, const void* q_idx, const f
     char* ws = (char*)workspace;
     int32_t* idx = own_idx ? (int32_t*)(ws + lay.idx) : idx_out;
     float* scores = (float*)(ws + lay.scores);
-    float* part = (float*)(ws + lay.part);
+    void* part = ws + lay.part;
     const void* qi = q_idx;
     const float* qsc = nullptr;
     if (s->idx_dtype == DSA_FP8_E4M3) {

@@ -47,7 +47,7 @@ struct MlaArgs {
     const int32_t* kv_len;  // [B]
     void* out;              // [B,T,H,Dv]
     float* lse;             // [B,T,H] or null
-    float* part;            // split partials (workspace) or null
+    void* part;             // split partials (workspace) or null
     int n_split;
 };
 
@@ -60,7 +60,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 bool mla_supported(int dtype, int Dqk, int Dv);
 int mla_split_count(int B, int t_count, int H, int K);
-size_t mla_partial_bytes(int B, int t_count, int H, int Dv, int n_split);
+size_t mla_partial_bytes(int dtype, int B, int t_count, int H, int Dv, int n_split);
 hipError_t launch_mla(int dtype, const MlaArgs& a, hipStream_t s);
 
 hipError_t launch_rotate_quant(int64_t rows, int dim, const void* x, int x_dtype, uint8_t* codes, float* scales,

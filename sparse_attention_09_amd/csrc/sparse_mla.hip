@@ -35,8 +35,15 @@ namespace dsa {
 namespace {
 
 constexpr int kTileKeys = 32;
-// A split partial row holds DV values, then m (log2 domain) and l, padded to 16 bytes.
-constexpr int kPartExtra = 4;
+// A split's partial result for one (query, head): its value row, then the running max m
+// (log2 domain) and sum l, padded to 16 bytes.  fp32 outputs keep the unnormalised
+// fp32 value row; bf16 outputs keep the row already divided by l, in bf16 (the final
+// output is bf16 too), which halves the partial traffic of split queries.
+template <int DT, int DV> struct PartRow {
+    static constexpr int vbytes = DV * (DT == kBF16 ? 2 : 4);
+    static constexpr int bytes = vbytes + 16;
+    static_assert(vbytes % 16 == 0, "row");
+};
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -317,16 +324,22 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
             }
         if (a.lse && half == 0 && kb == 0) a.lse[orow] = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
-        float* pr = a.part + (((size_t)rq * a.n_split + split) * a.H + head) * (DV + kPartExtra);
+        using P = PartRow<kBF16, DV>;
+        char* pr = (char*)a.part + (((size_t)rq * a.n_split + split) * a.H + head) * P::bytes;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t* dst = (uint16_t*)pr + C::VH * half + 4 * kb;
 #pragma unroll
         for (int v = 0; v < C::VT; ++v)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<f32x4*>(pr + C::VH * half + 32 * v + 8 * i + 4 * kb) =
-                    f32x4{st.o[v][4 * i], st.o[v][4 * i + 1], st.o[v][4 * i + 2], st.o[v][4 * i + 3]};
+            for (int i = 0; i < 4; ++i) {
+                u32x2 w2 = {pack_bf16x2(st.o[v][4 * i] * inv, st.o[v][4 * i + 1] * inv),
+                            pack_bf16x2(st.o[v][4 * i + 2] * inv, st.o[v][4 * i + 3] * inv)};
+                *reinterpret_cast<u32x2*>(dst + 32 * v + 8 * i) = w2;
+            }
         if (half == 0 && kb == 0) {
-            pr[DV] = st.m_run;
-            pr[DV + 1] = l_tot;
+            float* ml = (float*)(pr + P::vbytes);
+            ml[0] = st.m_run;
+            ml[1] = l_tot;
         }
     }
 }
@@ -454,7 +467,8 @@ __global__ __launch_bounds__(64) void mla_f32_kernel(MlaArgs a)
             *reinterpret_cast<f32x4*>((float*)a.out + orow * DV + 16 * v + 4 * g) = o[v] * inv;
         if (a.lse && g == 0) a.lse[orow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
-        float* pr = a.part + (((size_t)rq * a.n_split + split) * a.H + head) * (DV + kPartExtra);
+        using P = PartRow<kF32, DV>;
+        float* pr = (float*)((char*)a.part + (((size_t)rq * a.n_split + split) * a.H + head) * P::bytes);
 #pragma unroll
         for (int v = 0; v < C::VT; ++v) *reinterpret_cast<f32x4*>(pr + 16 * v + 4 * g) = o[v];
         if (g == 0) {
@@ -466,32 +480,41 @@ __global__ __launch_bounds__(64) void mla_f32_kernel(MlaArgs a)
 
 // ============================================================ split combine
 // One wave per (query, head): merge the split partials by log-sum-exp.  Lane sp
-// holds the weight of split sp; the value rows are read as float4.
+// holds the weight of split sp (for bf16 rows, whose values are already divided by
+// their own sum, the weight carries that sum); the value rows are read 4 at a time.
 template <int DT, int DV>
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a)
 {
+    using P = PartRow<DT, DV>;
     const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = lane_id();
     if (wid >= a.B * a.t_count * a.H) return;
     const int head = wid % a.H, rq = wid / a.H;
     const int b = rq / a.t_count, t = a.t_begin + rq % a.t_count;
     const size_t orow = ((size_t)b * a.T + t) * a.H + head;
-    constexpr int RS = DV + kPartExtra;
-    const float* base = a.part + ((size_t)rq * a.n_split * a.H + head) * RS;
-    const size_t sstride = (size_t)a.H * RS;
+    const char* base = (const char*)a.part + ((size_t)rq * a.n_split * a.H + head) * P::bytes;
+    const size_t sstride = (size_t)a.H * P::bytes;
     const int ns = a.n_split;
-    const float mi = lane < ns ? base[lane * sstride + DV] : -INFINITY;
-    const float li = lane < ns ? base[lane * sstride + DV + 1] : 0.f;
+    const float* ml = (const float*)(base + (size_t)(lane < ns ? lane : 0) * sstride + P::vbytes);
+    const float mi = lane < ns ? ml[0] : -INFINITY;
+    const float li = lane < ns ? ml[1] : 0.f;
     const float M = wave_max(mi);
     const float Mu = M == -INFINITY ? 0.f : M;
-    const float wi = lane < ns ? exp2f(mi - Mu) : 0.f;
-    const float Ls = wave_sum(wi * li);
+    const float ei = lane < ns ? exp2f(mi - Mu) : 0.f;
+    const float Ls = wave_sum(ei * li);
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    const float wi = DT == kBF16 ? ei * li : ei;  // weight of a stored value row
     for (int c = lane; c < DV / 4; c += 64) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int sp = 0; sp < ns; ++sp) {
             const float wsp = __shfl(wi, sp, 64);
-            acc += wsp * *reinterpret_cast<const f32x4*>(base + sp * sstride + 4 * c);
+            if constexpr (DT == kBF16) {
+                const u32x2 r = *reinterpret_cast<const u32x2*>(base + sp * sstride + 8 * c);
+                acc += wsp * f32x4{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xFFFF0000u),
+                                   __uint_as_float(r[1] << 16), __uint_as_float(r[1] & 0xFFFF0000u)};
+            } else {
+                acc += wsp * *reinterpret_cast<const f32x4*>(base + sp * sstride + 16 * c);
+            }
         }
         acc *= inv;
         if constexpr (DT == kBF16) {
@@ -554,10 +577,10 @@ int mla_split_count(int B, int t_count, int H, int K)
     return (int)(ns < 1 ? 1 : ns);
 }
 
-size_t mla_partial_bytes(int B, int t_count, int H, int Dv, int n_split)
+size_t mla_partial_bytes(int dtype, int B, int t_count, int H, int Dv, int n_split)
 {
     if (n_split <= 1) return 0;
-    return (size_t)B * t_count * n_split * H * (Dv + kPartExtra) * sizeof(float);
+    return (size_t)B * t_count * n_split * H * ((size_t)Dv * (dtype == kBF16 ? 2 : 4) + 16);
 }
 
 hipError_t launch_mla(int dtype, const MlaArgs& a, hipStream_t s)

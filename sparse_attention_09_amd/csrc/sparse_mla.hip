@@ -23,8 +23,10 @@
 // Thirty-two heads per wave halve the LDS bytes per MFMA flop against 16, and
 // the contraction split keeps two waves per SIMD.  Units of consecutive
 // queries go to one XCD, whose L2 then serves rows that neighbouring queries
-// share.  Splits write fp32 partials (unnormalised O, running max, running
-// sum) merged by a log-sum-exp combine kernel.
+// share.  Each workgroup writes one row per head (the output row, or for a
+// split its value row divided by its own softmax sum plus the running max and
+// sum), staged through LDS so that rows leave as whole contiguous writes; a
+// log-sum-exp combine kernel merges the splits.
 //
 // fp32 kernel (small shapes only): 16 heads per wave on 16x16x4 MFMA, the
 // gathered tile staged through registers.
@@ -260,28 +262,45 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
     const int j_end = min(a.K, j_begin + per);
     const int n_tiles = j_end > j_begin ? (j_end - j_begin + kTileKeys - 1) / kTileKeys : 0;
 
-    // Q^T operand: head `head`, contraction d in [HALF*half + SHARE*kb, + SHARE)
+    const char* kvb = (const char*)a.kv + (size_t)b * a.Lmax * C::ROWB;
+    const int32_t* idxr = a.idx + row * a.K;
+    // The split's index list is loaded first and Q behind it: loads complete in
+    // order, so waiting for the list leaves the Q loads in flight through the list
+    // set-up and the first gather.
+    // (unconditional loads, clamped into the list: a load under a branch would make
+    // the compiler wait for every load at the join)
+    constexpr int kListPer = kMaxListLen / 512;
+    const int n_list = n_tiles * kTileKeys;
+    const int j_last = max(j_end - 1, 0);
+    int raw[kListPer];
+#pragma unroll
+    for (int r = 0; r < kListPer; ++r) raw[r] = idxr[min(j_begin + tid + 512 * r, j_last)];
+    // Q^T operand: head `head`, contraction d in [HALF*half + SHARE*kb, + SHARE).  A
+    // column past the last head loads head 0 (finite values whose results are never
+    // written), so the loads are unconditional too.
     u32x4 qb[C::QS];
     {
         const char* src = (const char*)a.q + ((row * a.H + (head_ok ? head : 0)) * DQK) * 2 +
                           (C::HALF * half + C::SHARE * kb) * 2;
 #pragma unroll
-        for (int s = 0; s < C::QS; ++s) qb[s] = head_ok ? ld16(src + 16 * s) : u32x4{0, 0, 0, 0};
+        for (int s = 0; s < C::QS; ++s) qb[s] = ld16(src + 16 * s);
     }
-    const char* kvb = (const char*)a.kv + (size_t)b * a.Lmax * C::ROWB;
-    const int32_t* idxr = a.idx + row * a.K;
-    // the split's index list, sanitised (-1 = skip) and padded to whole tiles,
-    // plus a validity mask per tile
-    for (int j = tid; j < n_tiles * kTileKeys; j += 512) {
-        const int sk = valid_key(a, idxr, j_begin + j, j_end, L);
-        lidx[j] = sk < 0 ? 0 : sk;  // skipped entries fetch row 0; tmask masks them
-        const uint64_t bits = __ballot(sk >= 0);  // 64 consecutive entries = two tiles
-        if (lane == 0) {
+    // the list sanitised (skipped entries fetch row 0) and padded to whole tiles,
+    // plus a validity mask per tile; every slot is filled (the ones past the list
+    // as skipped), without branches, so the compiler keeps the early loads
+#pragma unroll
+    for (int r = 0; r < kListPer; ++r) {
+        const int j = tid + 512 * r;
+        const int s = raw[r];
+        const bool ok = j < n_list && j_begin + j < j_end && s >= 0 && s < L;
+        lidx[j] = ok ? s : 0;
+        const uint64_t bits = __ballot(ok);  // 64 consecutive entries = two tiles
+        if (lane == 0) {  // j is a multiple of 64 here, so both words lie inside tmask
             tmask[j / kTileKeys] = (uint32_t)bits;
-            if (j / kTileKeys + 1 < kMaxListLen / kTileKeys) tmask[j / kTileKeys + 1] = (uint32_t)(bits >> 32);
+            tmask[j / kTileKeys + 1] = (uint32_t)(bits >> 32);
         }
     }
-    __syncthreads();
+    barrier_lds();
 
     Bf16State<DQK, DV> st;
 #pragma unroll
@@ -308,39 +327,51 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
     }
 
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
-    if (!head_ok) return;
-    const size_t orow = row * a.H + head;
-    // lane holds value dims VH*half + 32*v + 8*i + 4*kb + jj (register 4*i + jj)
-    if (a.n_split == 1) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* dst = (uint16_t*)a.out + orow * DV + C::VH * half + 4 * kb;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (a.n_split == 1 && a.lse && head_ok && half == 0 && kb == 0)
+        a.lse[row * a.H + head] = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+
+    // One row per head: the normalised value row in bf16 (the output row, or a
+    // split's partial row followed by its fp32 m, l).  Rows are staged in the free
+    // tile buffers and written out whole, 16 contiguous bytes per lane: two rounds
+    // of 64 heads, the pair p of a round staging its 32 rows in buffer p % 2.
+    using P = PartRow<kBF16, DV>;
+    constexpr int SP = P::bytes;  // staged row pitch
+    static_assert(32 * SP <= C::BUF_CH * 16, "staging rows");
+    const bool part_out = a.n_split > 1;
+    const int hb0 = hb * kHeadsPerBlock;
+    const int heads_here = min(kHeadsPerBlock, a.H - hb0);
+    char* gbase = part_out ? (char*)a.part + (((size_t)rq * a.n_split + split) * a.H + hb0) * P::bytes
+                           : (char*)a.out + (row * a.H + hb0) * (size_t)(DV * 2);
+    const int grow = part_out ? P::bytes : DV * 2;  // bytes of a row in global memory
+    const int rch = grow / 16;
+    barrier_lds();  // every wave is done reading the last tile
+#pragma unroll 1
+    for (int round = 0; round < 2; ++round) {
+        if ((pair >> 1) == round) {
+            // lane holds value dims VH*half + 32*v + 8*i + 4*kb + jj (register 4*i + jj) of head `col`
+            char* sb = reinterpret_cast<char*>((pair & 1) ? tB : tA) + col * SP + (C::VH * half + 4 * kb) * 2;
 #pragma unroll
-        for (int v = 0; v < C::VT; ++v)
+            for (int v = 0; v < C::VT; ++v)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                u32x2 w2 = {pack_bf16x2(st.o[v][4 * i] * inv, st.o[v][4 * i + 1] * inv),
-                            pack_bf16x2(st.o[v][4 * i + 2] * inv, st.o[v][4 * i + 3] * inv)};
-                *reinterpret_cast<u32x2*>(dst + 32 * v + 8 * i) = w2;
-            }
-        if (a.lse && half == 0 && kb == 0) a.lse[orow] = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-    } else {
-        using P = PartRow<kBF16, DV>;
-        char* pr = (char*)a.part + (((size_t)rq * a.n_split + split) * a.H + head) * P::bytes;
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* dst = (uint16_t*)pr + C::VH * half + 4 * kb;
-#pragma unroll
-        for (int v = 0; v < C::VT; ++v)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                u32x2 w2 = {pack_bf16x2(st.o[v][4 * i] * inv, st.o[v][4 * i + 1] * inv),
-                            pack_bf16x2(st.o[v][4 * i + 2] * inv, st.o[v][4 * i + 3] * inv)};
-                *reinterpret_cast<u32x2*>(dst + 32 * v + 8 * i) = w2;
-            }
-        if (half == 0 && kb == 0) {
-            float* ml = (float*)(pr + P::vbytes);
-            ml[0] = st.m_run;
-            ml[1] = l_tot;
+                for (int i = 0; i < 4; ++i) {
+                    const u32x2 w2 = {pack_bf16x2(st.o[v][4 * i] * inv, st.o[v][4 * i + 1] * inv),
+                                      pack_bf16x2(st.o[v][4 * i + 2] * inv, st.o[v][4 * i + 3] * inv)};
+                    *reinterpret_cast<u32x2*>(sb + 2 * (32 * v + 8 * i)) = w2;
+                }
+            if (half == 0 && kb == 0)
+                *reinterpret_cast<f32x4*>(reinterpret_cast<char*>((pair & 1) ? tB : tA) + col * SP + P::vbytes) =
+                    f32x4{st.m_run, l_tot, 0.f, 0.f};
         }
+        barrier_lds();
+        const int h0 = 64 * round;
+        const int n = min(64, heads_here - h0) * rch;
+        for (int c = tid; c < n; c += 512) {
+            const int r = c / rch, k = c - r * rch;
+            const char* sb = reinterpret_cast<const char*>((r >> 5) ? tB : tA) + (r & 31) * SP + 16 * k;
+            st16(gbase + (size_t)(h0 + r) * grow + 16 * k, *reinterpret_cast<const u32x4*>(sb));
+        }
+        if (round == 0) barrier_lds();
     }
 }
 

@@ -93,14 +93,16 @@ constexpr int kHeadsPerBlock = 128;  // 4 wave pairs x 32 heads
 constexpr int kMaxListLen = 4096;    // longest index list a split holds in LDS
 
 // Issue this wave's direct loads of index-list tile [j0, j0 + 32) into LDS
-// buffer dst: position P holds row r = P / PCH, chunk P % PCH; the pad chunk
-// and the dummy tail past the tile fetch row 0, so every wave issues exactly
-// DMA_PER_WAVE loads.  lidx holds row 0 for skipped entries (masked by the
-// caller).  Load k of a wave is position P0 + 512 k, so (r, chunk) advance by a
-// constant step instead of a division per load, and the row address is a
-// 32-bit offset from the sequence's base.
+// buffer dst: position P holds row r = P / PCH, chunk P % PCH.  lrow holds the
+// byte offset of each listed row from the sequence's base (row 0 for skipped
+// entries, masked by the caller).  The pad chunk and the dummy tail past the
+// tile fetch any row of the tile, so every wave issues exactly DMA_PER_WAVE
+// loads.  Load k of a wave is position P0 + 512 k, so (r, chunk) advance by a
+// constant step instead of a division per load.  All row offsets are read from
+// LDS first, so the loads wait for one LDS round trip, not one per load.
 template <int DQK, int DV>
-__device__ __forceinline__ void gather_tile(const char* kvb, const int* lidx, int j0, int w, int lane, u32x4* dst)
+__device__ __forceinline__ void gather_tile(const char* kvb, const uint32_t* lrow, int j0, int w, int lane,
+                                            u32x4* dst)
 {
     using C = Bf16Cfg<DQK, DV>;
     constexpr int DR = 512 / C::PCH, DCH = 512 % C::PCH;
@@ -110,14 +112,11 @@ __device__ __forceinline__ void gather_tile(const char* kvb, const int* lidx, in
     const int wu = __builtin_amdgcn_readfirstlane(w);
     int r = (wu * 64 + ln) / C::PCH;
     int c = wu * 64 + ln - r * C::PCH;
+    uint32_t roff[C::DMA_PER_WAVE], coff[C::DMA_PER_WAVE];
 #pragma unroll
     for (int k = 0; k < C::DMA_PER_WAVE; ++k) {
-        const int u = wu + 8 * k;
-        const bool real = r < kTileKeys;
-        const int s = lidx[j0 + (real ? r : 0)];
-        const uint32_t off = (real ? (uint32_t)s * C::ROWB : 0u) + (c == C::CPR ? 0u : (uint32_t)c * 16u);
-        __builtin_amdgcn_global_load_lds(kvb + off, (__attribute__((address_space(3))) void*)(dst + u * 64), 16, 0,
-                                         0);
+        roff[k] = lrow[j0 + min(r, kTileKeys - 1)];
+        coff[k] = c == C::CPR ? 0u : (uint32_t)c * 16u;
         r += DR;
         c += DCH;
         if (c >= C::PCH) {
@@ -125,6 +124,10 @@ __device__ __forceinline__ void gather_tile(const char* kvb, const int* lidx, in
             ++r;
         }
     }
+#pragma unroll
+    for (int k = 0; k < C::DMA_PER_WAVE; ++k)
+        __builtin_amdgcn_global_load_lds(kvb + (roff[k] + coff[k]),
+                                         (__attribute__((address_space(3))) void*)(dst + (wu + 8 * k) * 64), 16, 0, 0);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads (whose vmcnt(0)
@@ -178,7 +181,11 @@ __device__ __forceinline__ void tile_compute(const u32x4* tile, uint32_t vmask, 
             tmax = fmaxf(tmax, sacc[e]);
         }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * zc;
+    {
+        // max with lane l ^ 32 on the gfx950 row swap (no LDS round trip)
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1])) * zc;
+    }
     // Lazy rescaling: the reference max m_run only moves when a logit exceeds
     // it by more than 8 (log2 units), so p <= 2^8 and O, l stay exact in fp32
     // while the rescale of O is rare.
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
     __shared__ __attribute__((aligned(16))) u32x4 tA[C::BUF_CH];
     __shared__ __attribute__((aligned(16))) u32x4 tB[C::BUF_CH];
     __shared__ float xbuf[8][16][64];
-    __shared__ int lidx[kMaxListLen];
+    __shared__ uint32_t lrow[kMaxListLen];
     __shared__ uint32_t tmask[kMaxListLen / kTileKeys];
 
     const int HB = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
@@ -293,7 +300,7 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
         const int j = tid + 512 * r;
         const int s = raw[r];
         const bool ok = j < n_list && j_begin + j < j_end && s >= 0 && s < L;
-        lidx[j] = ok ? s : 0;
+        lrow[j] = ok ? (uint32_t)s * C::ROWB : 0u;
         const uint64_t bits = __ballot(ok);  // 64 consecutive entries = two tiles
         if (lane == 0) {  // j is a multiple of 64 here, so both words lie inside tmask
             tmask[j / kTileKeys] = (uint32_t)bits;
@@ -312,18 +319,21 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
     const float zc = a.sm_scale * kLog2e;
 
     // tile `it` lives in buffer it % 2; each step issues tile it + 1 into the other buffer
-    if (n_tiles > 0) gather_tile<DQK, DV>(kvb, lidx, 0, w, lane, tA);
+    if (n_tiles > 0) gather_tile<DQK, DV>(kvb, lrow, 0, w, lane, tA);
 #pragma unroll 1
     for (int it = 0; it < n_tiles; it += 2) {
         barrier_lds_vm();
-        if (it + 1 < n_tiles) gather_tile<DQK, DV>(kvb, lidx, (it + 1) * kTileKeys, w, lane, tB);
+        // the tile's mask is read together with the next tile's row offsets
+        const uint32_t vmA = tmask[it];
+        if (it + 1 < n_tiles) gather_tile<DQK, DV>(kvb, lrow, (it + 1) * kTileKeys, w, lane, tB);
         __builtin_amdgcn_sched_barrier(0);
-        tile_compute<DQK, DV>(tA, tmask[it], qb, st, zc, xbuf, w, lane);
+        tile_compute<DQK, DV>(tA, vmA, qb, st, zc, xbuf, w, lane);
         if (it + 1 >= n_tiles) break;
         barrier_lds_vm();
-        if (it + 2 < n_tiles) gather_tile<DQK, DV>(kvb, lidx, (it + 2) * kTileKeys, w, lane, tA);
+        const uint32_t vmB = tmask[it + 1];
+        if (it + 2 < n_tiles) gather_tile<DQK, DV>(kvb, lrow, (it + 2) * kTileKeys, w, lane, tA);
         __builtin_amdgcn_sched_barrier(0);
-        tile_compute<DQK, DV>(tB, tmask[it + 1], qb, st, zc, xbuf, w, lane);
+        tile_compute<DQK, DV>(tB, vmB, qb, st, zc, xbuf, w, lane);
     }
 
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
@@ -512,11 +522,17 @@ __global__ __launch_bounds__(64) void mla_f32_kernel(MlaArgs a)
 // ============================================================ split combine
 // One wave per (query, head): merge the split partials by log-sum-exp.  Lane sp
 // holds the weight of split sp (for bf16 rows, whose values are already divided by
-// their own sum, the weight carries that sum); the value rows are read 4 at a time.
+// their own sum, the weight carries that sum).  Each lane owns 16-byte chunks of
+// the value row; the chunks of up to four splits are loaded before any is used,
+// the first batch together with the (m, l) pairs.
 template <int DT, int DV>
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a)
 {
     using P = PartRow<DT, DV>;
+    constexpr int EPC = DT == kBF16 ? 8 : 4;  // values per 16-byte chunk
+    constexpr int NCK = P::vbytes / 16;       // chunks per value row
+    constexpr int CPL = (NCK + 63) / 64;      // chunks per lane
+    constexpr int kBatch = 4;
     const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = lane_id();
     if (wid >= a.B * a.t_count * a.H) return;
@@ -526,33 +542,72 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a)
     const char* base = (const char*)a.part + ((size_t)rq * a.n_split * a.H + head) * P::bytes;
     const size_t sstride = (size_t)a.H * P::bytes;
     const int ns = a.n_split;
+
     const float* ml = (const float*)(base + (size_t)(lane < ns ? lane : 0) * sstride + P::vbytes);
-    const float mi = lane < ns ? ml[0] : -INFINITY;
-    const float li = lane < ns ? ml[1] : 0.f;
+    const float mi0 = ml[0], li0 = ml[1];
+    u32x4 v[kBatch][CPL];
+    auto load_batch = [&](int s0) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const char* rowp = base + (size_t)min(s0 + j, ns - 1) * sstride;
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                const int c = lane + 64 * k;
+                v[j][k] = (NCK % 64 == 0 || c < NCK) ? ld16(rowp + 16 * c) : u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    load_batch(0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the value loads ahead of the weight reductions
+
+    const float mi = lane < ns ? mi0 : -INFINITY;
+    const float li = lane < ns ? li0 : 0.f;
     const float M = wave_max(mi);
     const float Mu = M == -INFINITY ? 0.f : M;
     const float ei = lane < ns ? exp2f(mi - Mu) : 0.f;
     const float Ls = wave_sum(ei * li);
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    const float wi = DT == kBF16 ? ei * li : ei;  // weight of a stored value row
-    for (int c = lane; c < DV / 4; c += 64) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < ns; ++sp) {
-            const float wsp = __shfl(wi, sp, 64);
-            if constexpr (DT == kBF16) {
-                const u32x2 r = *reinterpret_cast<const u32x2*>(base + sp * sstride + 8 * c);
-                acc += wsp * f32x4{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xFFFF0000u),
-                                   __uint_as_float(r[1] << 16), __uint_as_float(r[1] & 0xFFFF0000u)};
-            } else {
-                acc += wsp * *reinterpret_cast<const f32x4*>(base + sp * sstride + 16 * c);
-            }
+    const float wi = (DT == kBF16 ? ei * li : ei) * inv;  // weight of a stored value row
+
+    float acc[CPL][EPC];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[k][e] = 0.f;
+    for (int s0 = 0;;) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            // split s0 + j's weight (zero past the last split) from its lane
+            const float wsp = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wi), min(s0 + j, 63)));
+            const float wj = s0 + j < ns ? wsp : 0.f;
+#pragma unroll
+            for (int k = 0; k < CPL; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t x = v[j][k][e];
+                    if constexpr (DT == kBF16) {
+                        acc[k][2 * e] = fmaf(wj, __uint_as_float(x << 16), acc[k][2 * e]);
+                        acc[k][2 * e + 1] = fmaf(wj, __uint_as_float(x & 0xFFFF0000u), acc[k][2 * e + 1]);
+                    } else {
+                        acc[k][e] = fmaf(wj, __uint_as_float(x), acc[k][e]);
+                    }
+                }
         }
-        acc *= inv;
+        s0 += kBatch;
+        if (s0 >= ns) break;
+        load_batch(s0);
+    }
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        const int c = lane + 64 * k;
+        if (NCK % 64 != 0 && c >= NCK) continue;
         if constexpr (DT == kBF16) {
-            const u32x2 w2 = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-            *reinterpret_cast<u32x2*>((uint16_t*)a.out + orow * DV + 4 * c) = w2;
+            const u32x4 w4 = {pack_bf16x2(acc[k][0], acc[k][1]), pack_bf16x2(acc[k][2], acc[k][3]),
+                              pack_bf16x2(acc[k][4], acc[k][5]), pack_bf16x2(acc[k][6], acc[k][7])};
+            st16((uint16_t*)a.out + orow * DV + 8 * c, w4);
         } else {
-            *reinterpret_cast<f32x4*>((float*)a.out + orow * DV + 4 * c) = acc;
+            st16((float*)a.out + orow * DV + 4 * c, u32x4{__float_as_uint(acc[k][0]), __float_as_uint(acc[k][1]),
+                                                          __float_as_uint(acc[k][2]), __float_as_uint(acc[k][3])});
         }
     }
     if (a.lse && lane == 0) a.lse[orow] = Ls > 0.f ? (Mu + log2f(Ls)) * kLn2 : -INFINITY;

@@ -94,6 +94,8 @@ dsa::IndexerArgs indexer_args(const dsa_shape* s, const void* q, const float* qs
     a.ld_t = s->max_kv;
     a.ld_b = (long long)t_count * s->max_kv;
     a.fill = fill;
+    a.zero = nullptr;
+    a.zero_words = 0;
     return a;
 }
 
@@ -373,9 +375,16 @@ DSA_EXPORT dsa_status dsa_forward(const dsa_shape* s, const void* q_idx, const f
     }
     for (int t0 = 0; t0 < s->n_q; t0 += tc) {
         const int cnt = (s->n_q - t0) < tc ? (s->n_q - t0) : tc;
-        const dsa::IndexerArgs ia = indexer_args(s, qi, qsc, w, k_idx, k_scale, kv_len, scores, t0, cnt, 0);
+        dsa::IndexerArgs ia = indexer_args(s, qi, qsc, w, k_idx, k_scale, kv_len, scores, t0, cnt, 0);
+        dsa::TopkArgs ta = topk_args(s, scores, kv_len, idx, part, t0, cnt);
+        // the indexer clears the top-k's counters, which saves the top-k a launch
+        const size_t zw = dsa::topk_zero_words(ta);
+        if (zw > 0) {
+            ia.zero = (uint32_t*)part;
+            ia.zero_words = (long long)zw;
+            ta.pre_zeroed = 1;
+        }
         if (dsa::launch_indexer(s->idx_dtype, ia, stream) != hipSuccess) return DSA_ERR_HIP;
-        const dsa::TopkArgs ta = topk_args(s, scores, kv_len, idx, part, t0, cnt);
         if (dsa::launch_topk(ta, stream) != hipSuccess) return DSA_ERR_HIP;
         const int ns = dsa::mla_split_count(s->batch, cnt, s->heads, s->topk);
         const dsa::MlaArgs ma = mla_args(s, q, kv, idx, kv_len, out, lse, part, t0, cnt, ns);

@@ -22,6 +22,8 @@ struct IndexerArgs {
     float* scores;
     long long ld_b, ld_t;
     int fill;               // write -inf for every s > p(t)
+    uint32_t* zero;         // optional: words [0, zero_words) are cleared by the launch
+    long long zero_words;   //   (a following top-k's counters, see topk_zero_words)
 };
 
 // Top-k over score rows laid out as in IndexerArgs; writes idx rows of the full
@@ -34,6 +36,7 @@ struct TopkArgs {
     const int32_t* kv_len;
     int32_t* idx;
     void* ws;               // topk_workspace_bytes(B, t_count, Lmax, K) bytes, 16-byte aligned
+    int pre_zeroed;         // the first topk_zero_words(*this) words of ws are already zero
 };
 
 // Sparse absorbed MLA for queries [t_begin, t_begin + t_count).
@@ -57,6 +60,9 @@ hipError_t launch_indexer(int dtype, const IndexerArgs& a, hipStream_t s);
 // Workspace of one top-k launch over B * t_count rows (0 when none is needed).
 size_t topk_workspace_bytes(int B, int t_count, int Lmax, int K);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// Words at the start of the workspace that the launch clears first (0 when none);
+// a preceding kernel on the same stream may clear them instead (pre_zeroed).
+size_t topk_zero_words(const TopkArgs& a);
 
 bool mla_supported(int dtype, int Dqk, int Dv);
 int mla_split_count(int B, int t_count, int H, int K);

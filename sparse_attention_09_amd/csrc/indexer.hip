@@ -104,6 +104,17 @@ __device__ __forceinline__ float head_sum(const f32x4 (&acc)[HT], const float (&
     return group4_sum(v);
 }
 
+// Clear the optional words a.zero[0, zero_words): a grid-stride loop over the
+// whole launch, run before any other work of the block.
+__device__ __forceinline__ void clear_words(const IndexerArgs& a)
+{
+    if (a.zero == nullptr) return;
+    const long long nthreads = (long long)gridDim.x * gridDim.y * gridDim.z * blockDim.x;
+    const long long id =
+        (((long long)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    for (long long i = id; i < a.zero_words; i += nthreads) a.zero[i] = 0u;
+}
+
 __device__ __forceinline__ int seq_len(const IndexerArgs& a, int b)
 {
     const int L = a.kv_len[b];
@@ -195,6 +206,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a)
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int b = blockIdx.z;
+    clear_words(a);
     const int L = seq_len(a, b);
 
     int tq[QPW], pq[QPW];
@@ -266,6 +278,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs a)
     const int wave = threadIdx.x >> 6;
     const int b = blockIdx.y;
     const int qb = gridDim.x - 1 - blockIdx.x;  // longest rows first
+    clear_words(a);
     const int L = seq_len(a, b);
     const int t_end = a.t_begin + a.t_count;
     const int t0 = a.t_begin + qb * QPB;

@@ -613,6 +613,11 @@ size_t topk_workspace_bytes(int B, int T, int Lmax, int K)
     return use_split(a) ? split_ws_bytes((size_t)B * T, K) : 0;
 }
 
+size_t topk_zero_words(const TopkArgs& a)
+{
+    return (a.t_count > 0 && a.B > 0 && use_split(a)) ? split_zero_words((size_t)a.B * a.t_count) : 0;
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s)
 {
     if (a.t_count <= 0 || a.B <= 0) return hipSuccess;
@@ -622,7 +627,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s)
         return hipGetLastError();
     }
     const size_t zw = split_zero_words(rows);
-    topk_zero_kernel<<<dim3((unsigned)std::min<size_t>((zw + 255) / 256, 1024)), 256, 0, s>>>((uint32_t*)a.ws, zw);
+    if (!a.pre_zeroed)
+        topk_zero_kernel<<<dim3((unsigned)std::min<size_t>((zw + 255) / 256, 1024)), 256, 0, s>>>((uint32_t*)a.ws, zw);
     const dim3 grid((a.Lmax + kChunk - 1) / kChunk, rows);
     topk_hist_kernel<<<grid, 256, 0, s>>>(a);
     topk_filter_kernel<<<grid, 256, 0, s>>>(a);

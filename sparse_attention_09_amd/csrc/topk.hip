@@ -43,9 +43,13 @@ constexpr int kChunk = 4096;          // entries per chunk of the split path
 constexpr int kCandCap = 16384;       // candidate buffer per row of the split path
 constexpr int kMaxK = 4096;
 
+constexpr int kLocalCand = 2048;  // keys of the threshold bin held for the last two passes
+
 struct TopkShared {
     uint32_t keys[kTopkStageMax];
     uint32_t hist[kHistBins];
+    uint32_t cand[kLocalCand];
+    int n_cand;
     int cnt_gt[kTopkWaves];
     int cnt_eq[kTopkWaves];
     int base_eq[kTopkWaves];
@@ -167,30 +171,16 @@ struct RowKeys {
 // the end are clamped to the last key and ignored.
 constexpr int kBatch = 8;
 
-__device__ void block_select(TopkShared& sh, const float* src, int n, int K, int32_t* dst)
+// Radix passes 1 and 2 (key bits 8..19, then 0..7) over keys key_at(0 .. n - 1),
+// counting only keys that match the prefix found so far.
+template <class KeyAt>
+__device__ __forceinline__ void radix_tail(TopkShared& sh, KeyAt key_at, int n, uint32_t& prefix, uint32_t& pmask,
+                                           int& krem)
 {
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const bool staged = n <= kTopkStageMax;
-    if (staged) {
-        for (int base = 0; base < n; base += kTopkThreads * kBatch) {
-            float v[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) v[u] = src[min(base + u * kTopkThreads + tid, n - 1)];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int i = base + u * kTopkThreads + tid;
-                if (i < n) sh.keys[i] = float_key(v[u]);
-            }
-        }
-        __syncthreads();
-    }
-    const RowKeys key_at{src, staged ? sh.keys : nullptr};
-
-    uint32_t prefix = 0, pmask = 0;
-    int krem = K;  // how many still to take among keys matching the prefix
+    const int tid = threadIdx.x;
 #pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    for (int pass = 1; pass < 3; ++pass) {
+        const int shift = pass == 1 ? 8 : 0;
         const int nbins = pass == 2 ? 256 : 4096;
         for (int i = tid; i < nbins; i += kTopkThreads) sh.hist[i] = 0;
         __syncthreads();
@@ -210,25 +200,157 @@ __device__ void block_select(TopkShared& sh, const float* src, int n, int K, int
         pmask |= (uint32_t)(nbins - 1) << shift;
         __syncthreads();
     }
-    const uint32_t tau = prefix;  // key of the K-th largest score; take krem keys equal to it
+}
 
-    const int seg = ((n + kTopkWaves - 1) / kTopkWaves + 63) & ~63;
-    const int s0 = min(n, wave * seg), s1 = min(n, s0 + seg);
-    int gt = 0, eq = 0;
-    for (int i0 = s0; i0 < s1; i0 += 64 * kBatch) {
-        uint32_t kk[kBatch];
+__device__ void block_select(TopkShared& sh, const float* src, int n, int K, int32_t* dst)
+{
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const bool staged = n <= kTopkStageMax;
+    // pass 0 (top 12 key bits) runs on the keys as they are loaded and staged
+    for (int i = tid; i < kHistBins; i += kTopkThreads) sh.hist[i] = 0;
+    if (tid == 0) sh.n_cand = 0;
+    __syncthreads();
+    for (int base = 0; base < n; base += kTopkThreads * kBatch) {
+        float v[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) kk[u] = key_at(min(i0 + 64 * u + lane, n - 1));
+        for (int u = 0; u < kBatch; ++u) v[u] = src[min(base + u * kTopkThreads + tid, n - 1)];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const bool in = i0 + 64 * u + lane < s1;
-            gt += __popcll(__ballot(in && kk[u] > tau));
-            eq += __popcll(__ballot(in && kk[u] == tau));
+            const int i = base + u * kTopkThreads + tid;
+            if (i < n) {
+                const uint32_t k = float_key(v[u]);
+                if (staged) sh.keys[i] = k;
+                atomicAdd(&sh.hist[k >> 20], 1u);
+            }
         }
     }
-    if (lane == 0) {
-        sh.cnt_gt[wave] = gt;
-        sh.cnt_eq[wave] = eq;
+    __syncthreads();
+    block_find_desc<kTopkThreads>(sh.hist, kHistBins, (uint32_t)K, sh.scan_tmp, &sh.sel_digit, &sh.sel_above);
+    int krem = K - sh.sel_above;  // how many still to take among keys matching the prefix
+    uint32_t prefix = sh.sel_digit << 20, pmask = 0xFFF00000u;
+    const int c0 = (int)sh.hist[sh.sel_digit];  // keys in the threshold bin
+    const RowKeys key_at{src, staged ? sh.keys : nullptr};
+
+    // output segments: wave w writes the selected positions of [w * seg, (w + 1) * seg)
+    const int seg = ((n + kTopkWaves - 1) / kTopkWaves + 63) & ~63;
+    const int s0 = min(n, wave * seg), s1 = min(n, s0 + seg);
+    uint32_t tau;  // key of the K-th largest score; take krem keys equal to it
+    if (c0 <= kLocalCand) {
+        // One scan (each wave over its own output segment) gathers the threshold
+        // bin's keys and positions (one append per wave and batch slot; positions go
+        // to hist[256 ..], which the remaining passes leave alone) and counts the
+        // segment's keys of higher bins.
+        if (tid < kTopkWaves) sh.cnt_eq[tid] = 0;
+        __syncthreads();  // (also: every thread has read the threshold bin's count)
+        uint32_t* cpos = sh.hist + 256;
+        const uint32_t top = prefix | 0x000FFFFFu;  // keys above the threshold bin exceed this
+        int gt = 0;
+        for (int i0 = s0; i0 < s1; i0 += 64 * kBatch) {
+            uint32_t kk[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) kk[u] = key_at(min(i0 + 64 * u + lane, n - 1));
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int i = i0 + 64 * u + lane;
+                const bool in = i < s1 && (kk[u] & pmask) == prefix;
+                const uint64_t m = __ballot(in);
+                if (m) {
+                    int at = 0;
+                    if (lane == 0) at = atomicAdd(&sh.n_cand, __popcll(m));
+                    at = __shfl(at, 0, 64);
+                    if (in) {
+                        const int r = at + __popcll(m & ((1ull << lane) - 1ull));
+                        sh.cand[r] = kk[u];
+                        cpos[r] = (uint32_t)i;
+                    }
+                }
+                gt += __popcll(__ballot(i < s1 && kk[u] > top));
+            }
+        }
+        if (lane == 0) sh.cnt_gt[wave] = gt;
+        __syncthreads();
+        // key bits 12..19, 6..11, 0..5 over the c0 gathered keys, by wave 0 alone:
+        // a wave's LDS operations complete in order, so its passes need no barriers
+        if (wave == 0) {
+#pragma unroll 1
+            for (int pass = 0; pass < 3; ++pass) {
+                const int shift = pass == 0 ? 12 : (pass == 1 ? 6 : 0);
+                const int nbins = pass == 0 ? 256 : 64;
+                const int per = nbins / 64;  // bins per lane: lane l holds [l * per, (l + 1) * per)
+                for (int bin = lane; bin < nbins; bin += 64) sh.hist[bin] = 0;
+                for (int c = lane; c < c0; c += 64) {
+                    const uint32_t k = sh.cand[c];
+                    if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & (nbins - 1)], 1u);
+                }
+                uint32_t hv[4], sum = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    hv[j] = j < per ? sh.hist[lane * per + j] : 0u;
+                    sum += hv[j];
+                }
+                uint32_t incl = sum;  // keys in this lane's bins and all higher ones
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t o = __shfl_down(incl, off, 64);
+                    if (lane + off < 64) incl += o;
+                }
+                const uint32_t excl = incl - sum;
+                int digit = 0;
+                uint32_t above = excl;
+                const bool mine = excl < (uint32_t)krem && incl >= (uint32_t)krem;
+                if (mine) {
+                    for (int j = per - 1; j >= 0; --j) {
+                        if (above + hv[j] >= (uint32_t)krem) {
+                            digit = lane * per + j;
+                            break;
+                        }
+                        above += hv[j];
+                    }
+                }
+                const int fl = __ffsll((unsigned long long)__ballot(mine)) - 1;
+                digit = __shfl(digit, fl, 64);
+                above = __shfl(above, fl, 64);
+                krem -= (int)above;
+                prefix |= (uint32_t)digit << shift;
+                pmask |= (uint32_t)(nbins - 1) << shift;
+            }
+            if (lane == 0) {
+                sh.sel_digit = prefix;
+                sh.sel_above = krem;
+            }
+        }
+        __syncthreads();
+        prefix = sh.sel_digit;
+        krem = sh.sel_above;
+        tau = prefix;
+        for (int c = tid; c < c0; c += kTopkThreads) {
+            const uint32_t k = sh.cand[c];
+            const int w = (int)cpos[c] / seg;
+            if (k > tau)
+                atomicAdd(&sh.cnt_gt[w], 1);
+            else if (k == tau)
+                atomicAdd(&sh.cnt_eq[w], 1);
+        }
+    } else {
+        __syncthreads();  // every thread has read the threshold bin's count
+        radix_tail(sh, key_at, n, prefix, pmask, krem);
+        tau = prefix;
+        int gt = 0, eq = 0;
+        for (int i0 = s0; i0 < s1; i0 += 64 * kBatch) {
+            uint32_t kk[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) kk[u] = key_at(min(i0 + 64 * u + lane, n - 1));
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const bool in = i0 + 64 * u + lane < s1;
+                gt += __popcll(__ballot(in && kk[u] > tau));
+                eq += __popcll(__ballot(in && kk[u] == tau));
+            }
+        }
+        if (lane == 0) {
+            sh.cnt_gt[wave] = gt;
+            sh.cnt_eq[wave] = eq;
+        }
     }
     __syncthreads();
     if (tid == 0) {

@@ -58,12 +58,13 @@ def _load():
             lib.orc_hadamard_matrix.argtypes = [I, P]
             lib.orc_rotate.argtypes = [L, I, P, P]
             lib.orc_rotate_quant.argtypes = [L, I, P, P, P]
+            lib.orc_quant.argtypes = [L, I, P, P, P]
             lib.orc_index_scores.argtypes = [I, I, I, I, I, P, P, P, P, L, P, I, P]
             lib.orc_index_scores_fp8.argtypes = [I, I, I, I, I, P, P, P, P, P, P, L, P, I, P]
             lib.orc_topk.argtypes = [I, I, I, I, P, L, P, P, P]
             lib.orc_sparse_mla.argtypes = [I, I, I, I, I, I, I, D, P, P, L, P, I, P, P, P]
             lib.orc_masked_dense_mla.argtypes = [I, I, I, I, I, I, I, D, P, P, P, L, P, I, P, P, P]
-            for f in ("orc_hadamard_matrix", "orc_rotate", "orc_rotate_quant", "orc_index_scores",
+            for f in ("orc_hadamard_matrix", "orc_rotate", "orc_rotate_quant", "orc_quant", "orc_index_scores",
                       "orc_index_scores_fp8", "orc_topk", "orc_sparse_mla", "orc_masked_dense_mla"):
                 getattr(lib, f).restype = None
             _lib = lib
@@ -171,6 +172,41 @@ def index_cache_append(k_new, kv_len, codes, scales):
                 codes[b, p] = c[0]
                 scales[b, p] = sc[0]
     return codes, scales
+
+
+def quant(x):
+    """Per-row e4m3 quantisation without rotation -> (codes uint8, scales f32).
+
+    The codec of ``rotate_quant`` (row scale amax / 448, codes of x * (448 / amax)
+    rounded to nearest even) applied to the rows as they are.  It serves the MLA
+    latent cache and queries when the attention runs on fp8 codes: the pages run
+    the indexer in FP8 and call FP8 a precision optimisation; the latent rows are
+    not rotated because their first v_dim columns are the values.
+    """
+    x = _f32(x)
+    D = x.shape[-1]
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    _load().orc_quant(x.size // D, D, _p(x), _p(codes), _p(scales))
+    return codes, scales
+
+
+def kv_rows_fp8(x) -> np.ndarray:
+    """The fp8 latent-cache row layout: per row, the D codes of ``quant``, then its
+    fp32 scale (little-endian) and 12 zero bytes -> uint8 [..., D + 16]."""
+    codes, scales = quant(x)
+    tail = np.zeros(codes.shape[:-1] + (16,), dtype=np.uint8)
+    tail[..., :4] = scales.astype("<f4").view(np.uint8).reshape(codes.shape[:-1] + (4,))
+    return np.concatenate([codes, tail], axis=-1)
+
+
+def sparse_mla_fp8(q_codes, q_scales, kv_codes, kv_scales, idx, sm_scale: float, rows=None,
+                   v_dim: int | None = None, T=None):
+    """Sparse MLA on fp8 operands: the attention of ``sparse_mla`` over the
+    dequantised queries decode(q_code) * q_scale and latent rows
+    decode(kv_code) * kv_scale (keys and values alike)."""
+    return sparse_mla(dequant(q_codes, q_scales).astype(np.float32), dequant(kv_codes, kv_scales).astype(np.float32),
+                      idx, sm_scale, rows=rows, v_dim=v_dim, T=T)
 
 
 def dequant(codes, scales) -> np.ndarray:

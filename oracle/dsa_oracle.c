@@ -173,6 +173,34 @@ void orc_rotate_quant(long rows, int D, const float* x, uint8_t* codes, float* s
     free(xr);
 }
 
+/* The same per-row e4m3 quantisation without the rotation, for the MLA
+ * latent cache and queries when the attention runs on fp8 codes.  The value
+ * columns of a latent row must stay in the latent basis, so no rotation is
+ * applied; every other step is the one of orc_rotate_quant. */
+void orc_quant(long rows, int D, const float* x, uint8_t* codes, float* scales)
+{
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r) {
+        const float* v = x + (size_t)r * D;
+        float amax = 0.0f;
+        for (int i = 0; i < D; ++i) {
+            float a = fabsf(v[i]);
+            if (a > amax)
+                amax = a;
+        }
+        if (amax == 0.0f) {
+            for (int i = 0; i < D; ++i)
+                codes[(size_t)r * D + i] = 0;
+            scales[r] = 1.0f;
+            continue;
+        }
+        float rcp = (float)(448.0 / (double)amax);
+        for (int i = 0; i < D; ++i)
+            codes[(size_t)r * D + i] = orc_e4m3_encode(v[i] * rcp);
+        scales[r] = (float)((double)amax / 448.0);
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Row lists.  A "row" is one query (b, t), numbered r = b * T + t; the  */
 /* i-th listed row is rows[i] (rows == NULL lists every row in order).  */

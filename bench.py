@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 METRIC = "DSA fwd queries/sec at L=32K/128K + % of MFMA peak / HBM GB/s"
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
-DEFAULT_STEPS = {"decode_32k": 100, "decode_128k_fp8": 100, "prefill_32k": 10, "prefill_4k": 50, "tiny_f32": 100}
+DEFAULT_STEPS = {"decode_32k": 100, "decode_128k_fp8": 100, "decode_128k_fp8_mla": 100, "prefill_32k": 10,
+                 "prefill_4k": 50, "tiny_f32": 100}
 
 
 def algorithmic(wl) -> dict:
@@ -40,7 +41,8 @@ def algorithmic(wl) -> dict:
     B, T, L, K = wl.batch, wl.n_q, wl.kv_len, wl.topk
     HI, DI, H, Dqk, Dv = wl.idx_heads, wl.idx_dim, wl.heads, wl.qk_dim, wl.v_dim
     ib = 1 if wl.idx_dtype == "fp8" else (4 if wl.idx_dtype == "f32" else 2)
-    mb = 4 if wl.mla_dtype == "f32" else 2
+    mb = 4 if wl.mla_dtype == "f32" else 2   # q and out element bytes (bf16 for the fp8 MLA)
+    row = Dqk * mb if wl.mla_dtype != "fp8" else Dqk + 4  # a gathered latent row (fp8: codes + scale)
     pairs = 0      # causal (query, key) pairs scored
     sel = 0        # selected (query, key) pairs attended
     for t in range(T):
@@ -54,10 +56,22 @@ def algorithmic(wl) -> dict:
     idx_bytes = key_bytes + B * T * HI * (DI * ib + 4 + (4 if wl.idx_dtype == "fp8" else 0)) + pairs * 4
     topk_bytes = pairs * 4 + B * T * K * 4
     mla_flops = 2.0 * sel * H * (Dqk + Dv)
-    gather = sel * Dqk * mb if T == 1 else B * L * Dqk * mb  # prefill rows come from L2 after first touch
+    gather = sel * row if T == 1 else B * L * row  # prefill rows come from L2 after first touch
     mla_bytes = gather + B * T * H * (Dqk * mb + Dv * mb + 4) + sel * 4
     return dict(indexer=dict(flops=idx_flops, bytes=idx_bytes), topk=dict(flops=0.0, bytes=topk_bytes),
                 mla=dict(flops=mla_flops, bytes=mla_bytes))
+
+
+def mfma_peak(wl, stage: str) -> float:
+    """Dense MFMA peak (TFLOP/s) of a stage.  The fp8 MLA runs q.k on fp8 MFMA and the
+    value sum on bf16 MFMA: its peak is the rate that does both shares in the time
+    they take at their own peaks."""
+    if stage == "indexer":
+        return PEAK_TFLOPS.get(wl.idx_dtype, PEAK_TFLOPS["bf16"])
+    if wl.mla_dtype == "fp8":
+        qk, pv = wl.qk_dim, wl.v_dim
+        return (qk + pv) / (qk / PEAK_TFLOPS["fp8"] + pv / PEAK_TFLOPS["bf16"])
+    return PEAK_TFLOPS.get(wl.mla_dtype, PEAK_TFLOPS["bf16"])
 
 
 def dominant(wl, stage_us: dict) -> tuple[str, dict]:
@@ -66,19 +80,22 @@ def dominant(wl, stage_us: dict) -> tuple[str, dict]:
     name = max(("indexer", "topk", "mla"), key=lambda k: stage_us.get(k, 0.0))
     us = stage_us[name]
     a = alg[name]
-    dt = wl.idx_dtype if name == "indexer" else wl.mla_dtype
     ai = a["flops"] / max(a["bytes"], 1.0)
-    ridge = PEAK_TFLOPS.get(dt, PEAK_TFLOPS["bf16"]) * 1e12 / (PEAK_HBM_GBS * 1e9)
+    peak = mfma_peak(wl, name)
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     if name != "topk" and ai > ridge:
         achieved = a["flops"] / (us * 1e-6) / 1e12
-        peak = PEAK_TFLOPS[dt]
-        return name, {"kernel": STAGE_KERNELS[name], "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+        return name, {"kernel": stage_kernel(wl, name), "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                       "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": recorded_traffic(wl, name),
                       "work_per_launch": a["flops"], "avg_launch_us": round(us, 2)}
     achieved = a["bytes"] / (us * 1e-6) / 1e9
-    return name, {"kernel": STAGE_KERNELS[name], "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+    return name, {"kernel": stage_kernel(wl, name), "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                   "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": recorded_traffic(wl, name),
                   "work_per_launch": a["bytes"], "avg_launch_us": round(us, 2)}
+
+
+def stage_kernel(wl, stage: str) -> str:
+    return STAGE_KERNELS["mla_fp8" if stage == "mla" and wl.mla_dtype == "fp8" else stage]
 
 
 def stage_fractions(wl, stage_us: dict) -> dict:
@@ -88,8 +105,7 @@ def stage_fractions(wl, stage_us: dict) -> dict:
     out = {}
     for name, us in stage_us.items():
         a = alg[name]
-        dt = wl.idx_dtype if name == "indexer" else wl.mla_dtype
-        peak_f = PEAK_TFLOPS.get(dt, PEAK_TFLOPS["bf16"])
+        peak_f = mfma_peak(wl, name)
         ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
         if name != "topk" and a["flops"] / max(a["bytes"], 1.0) > ridge:
             out[name] = {"bound": "mfma", "frac": round(a["flops"] / (us * 1e-6) / 1e12 / peak_f, 4)}
@@ -129,10 +145,25 @@ class Case:
             del inp["k_idx"], k_new
             q_codes, q_scale = dsa.rotate_quant_fp8(inp["q_idx"])
             self.q_codes, self.q_scale = q_codes, q_scale
+        self.kv_quant_us = None
+        if wl.mla_dtype == "fp8":
+            # the fp8 latent cache [B, L_max, D_qk + 16], quantised by the library, timed here
+            kv = inp["kv"]
+            rows = dsa.mla_kv_quant_fp8(kv)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 3
+            e0.record()
+            for _ in range(reps):
+                dsa.mla_kv_quant_fp8(kv, kv_rows=rows)
+            e1.record()
+            torch.cuda.synchronize()
+            self.kv_quant_us = e0.elapsed_time(e1) * 1000.0 / reps
+            inp["kv"] = rows
+            del kv
         dev = "cuda"
         B, T = wl.batch, wl.n_q
         self.idx = torch.empty((B, T, wl.topk), dtype=torch.int32, device=dev)
-        mdt = torch.float32 if wl.mla_dtype == "f32" else torch.bfloat16
+        mdt = torch.float32 if wl.mla_dtype == "f32" else torch.bfloat16  # bf16 for the fp8 MLA too
         self.out = torch.empty((B, T, wl.heads, wl.v_dim), dtype=mdt, device=dev)
         self.lse = torch.empty((B, T, wl.heads), dtype=torch.float32, device=dev)
         self.ws = torch.empty((dsa.forward_workspace_size(self.shape),), dtype=torch.uint8, device=dev)
@@ -162,7 +193,8 @@ def time_forward(dsa, torch, cases, steps, warmup):
 
 
 STAGE_KERNELS = {"indexer": "indexer", "topk": "topk (zero, hist, filter, finish) or topk_kernel",
-                 "mla": "mla_bf16_kernel + mla_combine_kernel"}
+                 "mla": "mla_bf16_kernel + mla_combine_kernel", "mla_fp8": "quant_rows_kernel (q) + mla_fp8_kernel + "
+                 "mla_combine_kernel"}
 
 
 def time_stages(dsa, torch, cases, reps):
@@ -311,7 +343,8 @@ def run(args) -> dict:
     res = {
         "metric": METRIC, "value": round(queries / (ms * 1e-3), 1), "unit": "queries/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": wl.mla_dtype if wl.idx_dtype != "fp8" else "fp8+bf16",
+        "vs_baseline": None,
+        "dtype": wl.mla_dtype if "fp8" not in (wl.idx_dtype, wl.mla_dtype) else "fp8+bf16",
         "data": "synthetic (seeded Gaussian, DeepSeek-V3.2 shapes)",
         "config": {"workload": wl.name, "batch": wl.batch, "queries_per_seq": wl.n_q, "context": wl.kv_len,
                    "index_heads": wl.idx_heads, "index_dim": wl.idx_dim, "topk": wl.topk, "heads": wl.heads,
@@ -334,6 +367,14 @@ def run(args) -> dict:
                                "avg_launch_us": round(cases[0].append_us, 2), "bound": "hbm",
                                "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": round(gbs / PEAK_HBM_GBS, 4), "work_per_launch": nbytes}
+    if cases[0].kv_quant_us is not None:
+        rows = wl.batch * wl.max_kv
+        nbytes = rows * (wl.qk_dim * 2 + wl.qk_dim + 16)  # bf16 rows in, fp8 cache rows out
+        gbs = nbytes / (cases[0].kv_quant_us * 1e-6) / 1e9
+        res["kv_cache_quant"] = {"kernel": "quant_rows_kernel (fp8 latent cache)", "rows": rows,
+                                 "avg_launch_us": round(cases[0].kv_quant_us, 2), "bound": "hbm",
+                                 "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": round(gbs / PEAK_HBM_GBS, 4), "work_per_launch": nbytes}
     del cases
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

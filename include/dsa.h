@@ -78,7 +78,7 @@ typedef struct {
     int32_t v_dim;      /* D_v  = kv_lora_rank (value = first D_v columns of a row) */
     float sm_scale;     /* softmax scale applied to q . k, finite and > 0; no default */
     int32_t idx_dtype;  /* DSA_F32 | DSA_BF16 | DSA_FP8_E4M3                         */
-    int32_t mla_dtype;  /* DSA_F32 | DSA_BF16                                        */
+    int32_t mla_dtype;  /* DSA_F32 | DSA_BF16 | DSA_FP8_E4M3                         */
 } dsa_shape;
 
 /*
@@ -86,7 +86,7 @@ typedef struct {
  *   indexer  idx_dtype F32: idx_dim in {32, 64, 128};  BF16 / FP8: idx_dim = 128;
  *            idx_heads 1..64 (padded internally to 16 or 64).
  *   MLA      (mla_dtype, qk_dim, v_dim) in {(F32, 80, 64), (BF16, 576, 512),
- *            (BF16, 192, 128)}; any heads >= 1 (padded to groups of 16).
+ *            (BF16, 192, 128), (FP8_E4M3, 576, 512)}; any heads >= 1.
  *   top-k    topk <= 4096, max_kv <= 1 << 20.
  */
 
@@ -125,7 +125,14 @@ dsa_status dsa_topk(const dsa_shape* shape, const float* scores, const int32_t* 
  *       z_j = sm_scale * q . kv[idx_j]
  *   lse [B,T,H] f32 out (may be NULL): natural-log log-sum-exp of z
  *   A (b,t) with no valid entry gets out = 0 and lse = -inf.
- *   workspace / ws_bytes: at least dsa_sparse_mla_workspace_size(shape) bytes. */
+ *   workspace / ws_bytes: at least dsa_sparse_mla_workspace_size(shape) bytes,
+ *   16-byte aligned (NULL allowed when the size is 0); scratch on entry and exit.
+ * FP8_E4M3 (the page's FP8 precision applied to the latent cache): kv is the
+ * fp8 latent cache of dsa_mla_kv_quant_fp8, uint8 [B,L_max,D_qk + 16] (per row the
+ * D_qk e4m3 codes, then the row's fp32 scale and 12 zero bytes); q is BF16 and is
+ * quantised per (b,t,h) row inside the call with the same codec; out is BF16.
+ * The logits are those of the dequantised operands, code * scale; the softmax
+ * weights are rounded to bf16 before the value sum. */
 size_t dsa_sparse_mla_workspace_size(const dsa_shape* shape);
 dsa_status dsa_sparse_mla_fwd(const dsa_shape* shape, const void* q, const void* kv,
                               const int32_t* idx, const int32_t* kv_len, void* out, float* lse,
@@ -158,8 +165,23 @@ dsa_status dsa_index_cache_append_fp8(int32_t batch, int32_t t_new, int32_t max_
                                       const void* k_new, int32_t x_dtype, const int32_t* kv_len,
                                       uint8_t* codes, float* scales, hipStream_t stream);
 
+/* Per-row e4m3 quantisation without rotation into fp8 latent-cache rows (the
+ * MLA operand of mla_dtype FP8_E4M3): amax = max|x|; if amax == 0 the codes are
+ * 0 and the scale 1, else codes = e4m3_rne(fp32(x * fp32(448 / amax))) and
+ * scale = fp32(amax / 448) -- the codec of dsa_rotate_quant_fp8 without the
+ * rotation, which would mix the value columns with the rope columns.
+ *   x       [rows, dim]  x_dtype (DSA_F32 or DSA_BF16), dim a multiple of 16, <= 1024
+ *   kv_rows [rows, dim + 16] uint8 out: the dim codes, the fp32 scale, 12 zero bytes.
+ *   Rows are independent, so a cache [B, L_max, dim + 16] is filled in one call
+ *   and new tokens are appended by pointing kv_rows at their first row.
+ * Errors: rows or dim <= 0 -> DSA_ERR_SHAPE; other dims -> DSA_ERR_UNSUPPORTED;
+ * other x_dtype -> DSA_ERR_DTYPE; NULL -> DSA_ERR_NULL; x or kv_rows not
+ * 16-byte aligned -> DSA_ERR_ALIGN. */
+dsa_status dsa_mla_kv_quant_fp8(int64_t rows, int32_t dim, const void* x, int32_t x_dtype,
+                                uint8_t* kv_rows, hipStream_t stream);
+
 /* The whole path: (fp8 only) rotate + quantise q_idx, index scores, top-k,
- * sparse MLA.
+ * (fp8 MLA only) quantise q, sparse MLA.
  *   q_idx  [B,T,H_I,D_I]: idx_dtype for F32/BF16; for FP8 it is the unrotated
  *          BF16 query, rotated and quantised inside the call
  *   w, kv_len, q, kv as above; k_idx / k_scale as in dsa_index_scores (for FP8

@@ -326,7 +326,8 @@ def forward(inp: dict, shape, rows=None, compact: bool = False) -> dict:
     ``inp`` holds q_idx, w, k_idx (raw, pre-rotation), q, kv, kv_len.  With
     ``compact`` the per-query tensors q_idx [n,H_I,D_I], w [n,H_I] and q [n,H,Dqk]
     hold only the listed rows.  With an fp8 indexer the oracle rotates and
-    quantises q_idx and k_idx itself.  Returns scores [n,Lmax] f32, idx [n,K] i32,
+    quantises q_idx and k_idx itself, and with an fp8 MLA it quantises q and kv
+    (``quant``, no rotation).  Returns scores [n,Lmax] f32, idx [n,K] i32,
     out [n,H,Dv] f64, lse [n,H] f64 and, for fp8, the codes and scales it used.
     """
     B, T = shape.batch, shape.n_q
@@ -341,6 +342,12 @@ def forward(inp: dict, shape, rows=None, compact: bool = False) -> dict:
     else:
         sc = index_scores(inp["q_idx"], inp["w"], inp["k_idx"], inp["kv_len"], rows=r, T=Tc)
     idx = topk(sc, inp["kv_len"], T, shape.topk, rows=r)
-    out, lse = sparse_mla(inp["q"], inp["kv"], idx, shape.sm_scale, rows=r, v_dim=shape.v_dim, T=Tc)
+    if getattr(shape, "mla_dtype", None) == "fp8":
+        mqc, mqs = quant(inp["q"])
+        kvc, kvs = quant(inp["kv"])
+        res.update(mla_q_codes=mqc, mla_q_scale=mqs, kv_codes=kvc, kv_scale=kvs)
+        out, lse = sparse_mla_fp8(mqc, mqs, kvc, kvs, idx, shape.sm_scale, rows=r, v_dim=shape.v_dim, T=Tc)
+    else:
+        out, lse = sparse_mla(inp["q"], inp["kv"], idx, shape.sm_scale, rows=r, v_dim=shape.v_dim, T=Tc)
     res.update(scores=sc, idx=idx, out=out, lse=lse, rows=r)
     return res

@@ -18,14 +18,13 @@ LIB_PATH = os.path.join(_PKG, "libdsa.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 _DT = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
-_TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16, FP8_E4M3: torch.uint8}
 
 STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_DTYPE", -4: "DSA_ERR_ALIGN",
           -5: "DSA_ERR_WORKSPACE", -6: "DSA_ERR_UNSUPPORTED", -7: "DSA_ERR_HIP"}
 
 EXPORTS = ["dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_workspace_size",
            "dsa_sparse_mla_fwd", "dsa_rotate_quant_fp8", "dsa_index_cache_append_fp8", "dsa_forward_workspace_size",
-           "dsa_forward_min_workspace_size", "dsa_forward", "dsa_status_string"]
+           "dsa_mla_kv_quant_fp8", "dsa_forward_min_workspace_size", "dsa_forward", "dsa_status_string"]
 
 
 class DsaError(RuntimeError):
@@ -86,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "dsa_sparse_mla_fwd": ([SP, P, P, P, P, P, P, P, SZ, P], I32),
             "dsa_rotate_quant_fp8": ([I64, I32, P, I32, P, P, P], I32),
             "dsa_index_cache_append_fp8": ([I32, I32, I32, I32, P, I32, P, P, P, P], I32),
+            "dsa_mla_kv_quant_fp8": ([I64, I32, P, I32, P, P], I32),
             "dsa_forward_workspace_size": ([SP], SZ),
             "dsa_forward_min_workspace_size": ([SP], SZ),
             "dsa_forward": ([SP, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
@@ -121,6 +121,11 @@ def _check(fn: str, st: int):
 
 def _empty(shape, dt, device):
     return torch.empty(shape, dtype=dt, device=device)
+
+
+def _out_dtype(shape: DsaShape):
+    """MLA output dtype: f32 for the f32 path, bf16 for the bf16 and fp8 paths."""
+    return torch.float32 if shape.mla_dtype == "f32" else torch.bfloat16
 
 
 def _view_u8(t):
@@ -166,8 +171,11 @@ def sparse_mla_workspace_size(shape: DsaShape) -> int:
 
 def sparse_mla_fwd(shape: DsaShape, q, kv, idx, kv_len, out=None, lse=None, want_lse=True, workspace=None,
                    stream=None):
-    """Sparse absorbed MLA -> (out [B,T,H,Dv], lse [B,T,H] f32)."""
-    dt = _TORCH_DT[_DT[shape.mla_dtype]]
+    """Sparse absorbed MLA -> (out [B,T,H,Dv], lse [B,T,H] f32).  For mla_dtype fp8, q is
+    bf16 and kv the fp8 latent cache of ``mla_kv_quant_fp8`` ([B, L_max, D_qk + 16] u8)."""
+    dt = _out_dtype(shape)
+    if shape.mla_dtype == "fp8":
+        kv = _view_u8(kv)
     if out is None:
         out = _empty((shape.batch, shape.n_q, shape.heads, shape.v_dim), dt, q.device)
     if lse is None and want_lse:
@@ -211,6 +219,19 @@ def index_cache_append_fp8(k_new, kv_len, codes, scales, stream=None):
     return codes, scales
 
 
+def mla_kv_quant_fp8(x, kv_rows=None, stream=None):
+    """Per-row e4m3 quantisation (no rotation) of x [..., dim] into fp8 latent-cache
+    rows [..., dim + 16] u8: the codes, the fp32 row scale, 12 zero bytes."""
+    dim = x.shape[-1]
+    rows = x.numel() // dim
+    xt = {torch.float32: F32, torch.bfloat16: BF16}[x.dtype]
+    if kv_rows is None:
+        kv_rows = _empty(tuple(x.shape[:-1]) + (dim + 16,), torch.uint8, x.device)
+    _check("dsa_mla_kv_quant_fp8", lib().dsa_mla_kv_quant_fp8(rows, dim, _ptr(x), xt, _ptr(kv_rows),
+                                                               _stream(stream)))
+    return kv_rows
+
+
 def forward_workspace_size(shape: DsaShape) -> int:
     return int(lib().dsa_forward_workspace_size(ctypes.byref(shape.c())))
 
@@ -225,10 +246,12 @@ def forward(shape: DsaShape, q_idx, w, k_idx, q, kv, kv_len, k_scale=None, idx_o
     dev = q.device
     if shape.idx_dtype == "fp8":
         k_idx = _view_u8(k_idx)
+    if shape.mla_dtype == "fp8":
+        kv = _view_u8(kv)
     if idx_out is None and want_idx:
         idx_out = _empty((shape.batch, shape.n_q, shape.topk), torch.int32, dev)
     if out is None:
-        out = _empty((shape.batch, shape.n_q, shape.heads, shape.v_dim), _TORCH_DT[_DT[shape.mla_dtype]], dev)
+        out = _empty((shape.batch, shape.n_q, shape.heads, shape.v_dim), _out_dtype(shape), dev)
     if lse is None and want_lse:
         lse = _empty((shape.batch, shape.n_q, shape.heads), torch.float32, dev)
     if workspace is None:

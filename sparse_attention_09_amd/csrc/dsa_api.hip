@@ -51,7 +51,7 @@ dsa_status check_mla_shape(const dsa_shape* s)
     if (s->heads <= 0 || s->qk_dim <= 0 || s->v_dim <= 0 || s->topk <= 0) return DSA_ERR_SHAPE;
     if (s->v_dim > s->qk_dim) return DSA_ERR_SHAPE;
     if (!isfinite(s->sm_scale) || !(s->sm_scale > 0.f)) return DSA_ERR_SHAPE;
-    if (s->mla_dtype != DSA_F32 && s->mla_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (s->mla_dtype != DSA_F32 && s->mla_dtype != DSA_BF16 && s->mla_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
     if (s->topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
     if (!dsa::mla_supported(s->mla_dtype, s->qk_dim, s->v_dim)) return DSA_ERR_UNSUPPORTED;
     return DSA_OK;
@@ -118,8 +118,8 @@ dsa::TopkArgs topk_args(const dsa_shape* s, const float* scores, const int32_t* 
     return a;
 }
 
-dsa::MlaArgs mla_args(const dsa_shape* s, const void* q, const void* kv, const int32_t* idx, const int32_t* kv_len,
-                      void* out, float* lse, void* part, int t_begin, int t_count, int n_split)
+dsa::MlaArgs mla_args(const dsa_shape* s, const void* q, const float* q_scale, const void* kv, const int32_t* idx,
+                      const int32_t* kv_len, void* out, float* lse, void* part, int t_begin, int t_count, int n_split)
 {
     dsa::MlaArgs a;
     a.B = s->batch;
@@ -133,6 +133,7 @@ dsa::MlaArgs mla_args(const dsa_shape* s, const void* q, const void* kv, const i
     a.t_count = t_count;
     a.sm_scale = s->sm_scale;
     a.q = q;
+    a.q_scale = q_scale;
     a.kv = kv;
     a.idx = idx;
     a.kv_len = kv_len;
@@ -149,11 +150,42 @@ size_t mla_ws(const dsa_shape* s, int t_count)
     return dsa::mla_partial_bytes(s->mla_dtype, s->batch, t_count, s->heads, s->v_dim, ns);
 }
 
+// fp8 MLA: bytes of the queries' e4m3 codes and of their row scales (all T queries).
+size_t mla_qcode_bytes(const dsa_shape* s) { return align_up((size_t)s->batch * s->n_q * s->heads * s->qk_dim); }
+size_t mla_qscale_bytes(const dsa_shape* s) { return align_up((size_t)s->batch * s->n_q * s->heads * sizeof(float)); }
+
+// Workspace of dsa_sparse_mla_fwd: (fp8) query codes and scales, then the split partials.
+struct MlaLayout {
+    size_t qcodes = 0, qscale = 0, part = 0, total = 0;
+};
+
+MlaLayout mla_layout(const dsa_shape* s)
+{
+    MlaLayout l;
+    size_t off = 0;
+    if (s->mla_dtype == DSA_FP8_E4M3) {
+        l.qcodes = off;
+        off += mla_qcode_bytes(s);
+        l.qscale = off;
+        off += mla_qscale_bytes(s);
+    }
+    l.part = off;
+    l.total = off + mla_ws(s, s->n_q);
+    return l;
+}
+
+// Quantise the bf16 queries [B,T,H,D_qk] of an fp8 MLA into codes and row scales.
+hipError_t quant_mla_queries(const dsa_shape* s, const void* q, uint8_t* codes, float* scales, hipStream_t stream)
+{
+    const int64_t rows = (int64_t)s->batch * s->n_q * s->heads;
+    return dsa::launch_quant_rows(rows, s->qk_dim, q, DSA_BF16, codes, s->qk_dim, scales, 0, stream);
+}
+
 // Workspace layout of dsa_forward for a query chunk of tc rows.  The top-k
 // scratch and the MLA split partials share one region: on one stream the top-k
 // of a chunk has finished before its MLA starts.
 struct FwdLayout {
-    size_t qcodes = 0, qscale = 0, idx = 0, scores = 0, part = 0, total = 0;
+    size_t qcodes = 0, qscale = 0, mqcodes = 0, mqscale = 0, idx = 0, scores = 0, part = 0, total = 0;
 };
 
 FwdLayout fwd_layout(const dsa_shape* s, int tc, bool own_idx)
@@ -166,6 +198,12 @@ FwdLayout fwd_layout(const dsa_shape* s, int tc, bool own_idx)
         off += align_up(BT * s->idx_heads * s->idx_dim);
         l.qscale = off;
         off += align_up(BT * s->idx_heads * sizeof(float));
+    }
+    if (s->mla_dtype == DSA_FP8_E4M3) {
+        l.mqcodes = off;
+        off += mla_qcode_bytes(s);
+        l.mqscale = off;
+        off += mla_qscale_bytes(s);
     }
     if (own_idx) {
         l.idx = off;
@@ -268,7 +306,7 @@ DSA_EXPORT dsa_status dsa_topk(const dsa_shape* s, const float* scores, const in
 DSA_EXPORT size_t dsa_sparse_mla_workspace_size(const dsa_shape* s)
 {
     if (check_common(s) != DSA_OK || check_mla_shape(s) != DSA_OK) return 0;
-    return mla_ws(s, s->n_q);
+    return mla_layout(s).total;
 }
 
 DSA_EXPORT dsa_status dsa_sparse_mla_fwd(const dsa_shape* s, const void* q, const void* kv, const int32_t* idx,
@@ -284,12 +322,22 @@ DSA_EXPORT dsa_status dsa_sparse_mla_fwd(const dsa_shape* s, const void* q, cons
     DSA_TRY(ptr_ok(out, 16));
     if (lse && !aligned(lse, 4)) return DSA_ERR_ALIGN;
     const int ns = dsa::mla_split_count(s->batch, s->n_q, s->heads, s->topk);
-    const size_t need = dsa::mla_partial_bytes(s->mla_dtype, s->batch, s->n_q, s->heads, s->v_dim, ns);
-    if (need > 0) {
-        if (!workspace || ws_bytes < need) return DSA_ERR_WORKSPACE;
+    const MlaLayout lay = mla_layout(s);
+    if (lay.total > 0) {
+        if (!workspace || ws_bytes < lay.total) return DSA_ERR_WORKSPACE;
         if (!aligned(workspace, 16)) return DSA_ERR_ALIGN;
     }
-    const dsa::MlaArgs a = mla_args(s, q, kv, idx, kv_len, out, lse, workspace, 0, s->n_q, ns);
+    char* ws = (char*)workspace;
+    const void* qm = q;
+    const float* qms = nullptr;
+    if (s->mla_dtype == DSA_FP8_E4M3) {
+        uint8_t* qc = (uint8_t*)(ws + lay.qcodes);
+        float* qs = (float*)(ws + lay.qscale);
+        if (quant_mla_queries(s, q, qc, qs, stream) != hipSuccess) return DSA_ERR_HIP;
+        qm = qc;
+        qms = qs;
+    }
+    const dsa::MlaArgs a = mla_args(s, qm, qms, kv, idx, kv_len, out, lse, ws ? ws + lay.part : nullptr, 0, s->n_q, ns);
     return hip_status(dsa::launch_mla(s->mla_dtype, a, stream));
 }
 
@@ -318,6 +366,17 @@ DSA_EXPORT dsa_status dsa_index_cache_append_fp8(int32_t batch, int32_t t_new, i
     DSA_TRY(ptr_ok(scales, 4));
     return hip_status(dsa::launch_cache_append(batch, t_new, max_kv, dim, k_new, x_dtype, kv_len, codes, scales,
                                                stream));
+}
+
+DSA_EXPORT dsa_status dsa_mla_kv_quant_fp8(int64_t rows, int32_t dim, const void* x, int32_t x_dtype,
+                                           uint8_t* kv_rows, hipStream_t stream)
+{
+    if (rows <= 0 || dim <= 0) return DSA_ERR_SHAPE;
+    if (x_dtype != DSA_F32 && x_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (dim % 16 != 0 || dim > 1024) return DSA_ERR_UNSUPPORTED;
+    DSA_TRY(ptr_ok(x, 16));
+    DSA_TRY(ptr_ok(kv_rows, 16));
+    return hip_status(dsa::launch_quant_rows(rows, dim, x, x_dtype, kv_rows, (int64_t)dim + 16, nullptr, 1, stream));
 }
 
 DSA_EXPORT size_t dsa_forward_workspace_size(const dsa_shape* s)
@@ -373,6 +432,15 @@ DSA_EXPORT dsa_status dsa_forward(const dsa_shape* s, const void* q_idx, const f
         qi = qc;
         qsc = qs;
     }
+    const void* qm = q;
+    const float* qms = nullptr;
+    if (s->mla_dtype == DSA_FP8_E4M3) {
+        uint8_t* qc = (uint8_t*)(ws + lay.mqcodes);
+        float* qs = (float*)(ws + lay.mqscale);
+        if (quant_mla_queries(s, q, qc, qs, stream) != hipSuccess) return DSA_ERR_HIP;
+        qm = qc;
+        qms = qs;
+    }
     for (int t0 = 0; t0 < s->n_q; t0 += tc) {
         const int cnt = (s->n_q - t0) < tc ? (s->n_q - t0) : tc;
         dsa::IndexerArgs ia = indexer_args(s, qi, qsc, w, k_idx, k_scale, kv_len, scores, t0, cnt, 0);
@@ -387,7 +455,7 @@ DSA_EXPORT dsa_status dsa_forward(const dsa_shape* s, const void* q_idx, const f
         if (dsa::launch_indexer(s->idx_dtype, ia, stream) != hipSuccess) return DSA_ERR_HIP;
         if (dsa::launch_topk(ta, stream) != hipSuccess) return DSA_ERR_HIP;
         const int ns = dsa::mla_split_count(s->batch, cnt, s->heads, s->topk);
-        const dsa::MlaArgs ma = mla_args(s, q, kv, idx, kv_len, out, lse, part, t0, cnt, ns);
+        const dsa::MlaArgs ma = mla_args(s, qm, qms, kv, idx, kv_len, out, lse, part, t0, cnt, ns);
         if (dsa::launch_mla(s->mla_dtype, ma, stream) != hipSuccess) return DSA_ERR_HIP;
     }
     return DSA_OK;

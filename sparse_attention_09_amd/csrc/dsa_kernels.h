@@ -44,8 +44,9 @@ struct MlaArgs {
     int B, T, Lmax, H, Dqk, Dv, K;
     int t_begin, t_count;
     float sm_scale;
-    const void* q;          // [B,T,H,Dqk]
-    const void* kv;         // [B,Lmax,Dqk]
+    const void* q;          // [B,T,H,Dqk] (e4m3 codes for the fp8 kernel)
+    const float* q_scale;   // [B,T,H] row scales of the fp8 codes, else null
+    const void* kv;         // [B,Lmax,Dqk] (fp8: [B,Lmax,Dqk + 16] cache rows, codes then scale)
     const int32_t* idx;     // [B,T,K]
     const int32_t* kv_len;  // [B]
     void* out;              // [B,T,H,Dv]
@@ -71,6 +72,11 @@ hipError_t launch_mla(int dtype, const MlaArgs& a, hipStream_t s);
 
 hipError_t launch_rotate_quant(int64_t rows, int dim, const void* x, int x_dtype, uint8_t* codes, float* scales,
                                hipStream_t s);
+// Per-row e4m3 quantisation without rotation (dim a multiple of 16, at most 1024):
+// codes at codes + row * cpitch; the scale to scales[row], or with tail into the
+// 16 bytes after the codes (fp32 scale, 12 zero bytes).
+hipError_t launch_quant_rows(int64_t rows, int dim, const void* x, int x_dtype, uint8_t* codes, int64_t cpitch,
+                             float* scales, int tail, hipStream_t s);
 // Rotate + quantise rows [B, t_new, dim] into cache rows kv_len[b] - t_new + t of [B, max_kv, dim].
 hipError_t launch_cache_append(int batch, int t_new, int max_kv, int dim, const void* x, int x_dtype,
                                const int32_t* kv_len, uint8_t* codes, float* scales, hipStream_t s);

@@ -1,4 +1,5 @@
-// quant.hip -- Hadamard rotation + e4m3 quantisation of indexer operands.
+// quant.hip -- e4m3 quantisation: Hadamard-rotated indexer operands, and the
+// unrotated MLA latent rows and queries of the fp8 attention.
 //
 // DeepSeek-V3.2 model documentation, "DeepSeek Sparse Attention (DSA)", item 1:
 // the reference indexer runs in FP8 after an orthogonal Hadamard transform of
@@ -138,6 +139,71 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(int64_t rows, const v
     }
 }
 
+// Per-row e4m3 quantisation without rotation (the codec above on the rows as
+// they are).  One wave per row; lane li holds the 8-element chunks li and li + 64
+// (rows of up to 1024 elements).  Codes go to codes + row * cpitch; the row scale
+// to scales[row], or with `tail` into the 16 bytes after the row's codes (fp32
+// scale, then 12 zero bytes: the fp8 latent-cache row layout).
+template <int XT>
+__global__ __launch_bounds__(256) void quant_rows_kernel(int64_t rows, int dim, const void* x, uint8_t* codes,
+                                                         int64_t cpitch, float* scales, int tail)
+{
+    const int lane = lane_id(), nch = dim / 8;
+    const int64_t n_waves = (int64_t)gridDim.x * 4;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += n_waves) {
+        float xf[2][8];
+        float amax = 0.f;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int c = lane + 64 * k;
+            if (c < nch) {
+                if constexpr (XT == kBF16) {
+                    const u32x4 raw = ld16((const uint16_t*)x + row * dim + 8 * c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        xf[k][2 * e] = __uint_as_float(raw[e] << 16);
+                        xf[k][2 * e + 1] = __uint_as_float(raw[e] & 0xFFFF0000u);
+                    }
+                } else {
+                    const u32x4 r0 = ld16((const float*)x + row * dim + 8 * c);
+                    const u32x4 r1 = ld16((const float*)x + row * dim + 8 * c + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        xf[k][e] = __uint_as_float(r0[e]);
+                        xf[k][4 + e] = __uint_as_float(r1[e]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xf[k][e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(xf[k][e]));
+        }
+        amax = wave_max(amax);
+        const bool zero = amax == 0.f;
+        const float r = zero ? 0.f : 448.f / amax;
+        uint8_t* crow = codes + row * cpitch;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int c = lane + 64 * k;
+            if (c >= nch) continue;
+            uint32_t packed[2] = {0u, 0u};
+            if (!zero)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) packed[e >> 2] |= (uint32_t)e4m3_encode(xf[k][e] * r) << (8 * (e & 3));
+            *reinterpret_cast<u32x2*>(crow + 8 * c) = u32x2{packed[0], packed[1]};
+        }
+        if (lane == 0) {
+            const float sc = zero ? 1.f : amax / 448.f;
+            if (tail)
+                st16(crow + dim, u32x4{__float_as_uint(sc), 0u, 0u, 0u});
+            else
+                scales[row] = sc;
+        }
+    }
+}
+
 template <int DIM>
 hipError_t launch_dim(int64_t rows, const void* x, int xt, uint8_t* codes, float* scales, RowMap map, hipStream_t s)
 {
@@ -171,6 +237,19 @@ hipError_t launch_rotate_quant(int64_t rows, int dim, const void* x, int x_dtype
                                hipStream_t s)
 {
     return launch_map(rows, dim, x, x_dtype, codes, scales, RowMap{nullptr, 0, 0}, s);
+}
+
+hipError_t launch_quant_rows(int64_t rows, int dim, const void* x, int x_dtype, uint8_t* codes, int64_t cpitch,
+                             float* scales, int tail, hipStream_t s)
+{
+    if (rows <= 0) return hipSuccess;
+    if (dim <= 0 || dim % 16 != 0 || dim > 1024) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)std::min<int64_t>((rows + 3) / 4, 8192));
+    if (x_dtype == kBF16)
+        quant_rows_kernel<kBF16><<<grid, 256, 0, s>>>(rows, dim, x, codes, cpitch, scales, tail);
+    else
+        quant_rows_kernel<kF32><<<grid, 256, 0, s>>>(rows, dim, x, codes, cpitch, scales, tail);
+    return hipGetLastError();
 }
 
 hipError_t launch_cache_append(int batch, int t_new, int max_kv, int dim, const void* x, int x_dtype,

@@ -50,6 +50,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c)
 {
@@ -100,11 +102,10 @@ constexpr int kMaxListLen = 4096;    // longest index list a split holds in LDS
 // loads.  Load k of a wave is position P0 + 512 k, so (r, chunk) advance by a
 // constant step instead of a division per load.  All row offsets are read from
 // LDS first, so the loads wait for one LDS round trip, not one per load.
-template <int DQK, int DV>
+template <class C>
 __device__ __forceinline__ void gather_tile(const char* kvb, const uint32_t* lrow, int j0, int w, int lane,
                                             u32x4* dst)
 {
-    using C = Bf16Cfg<DQK, DV>;
     constexpr int DR = 512 / C::PCH, DCH = 512 % C::PCH;
     // an opaque lane id keeps the per-lane addresses out of the loop's live set
     int ln = lane;
@@ -231,6 +232,61 @@ __device__ __forceinline__ void tile_compute(const u32x4* tile, uint32_t vmask, 
     }
 }
 
+// Epilogue shared by the bf16 and fp8 kernels.  One row per head: the
+// normalised value row in bf16 (the output row, or a split's partial row followed
+// by its fp32 m, l).  Rows are staged in the free tile buffers and written out
+// whole, 16 contiguous bytes per lane: two rounds of 64 heads, the pair p of a
+// round staging its 32 rows in buffer p % 2.
+template <int DQK, int DV, class C>
+__device__ __forceinline__ void mla_write_rows(const MlaArgs& a, const Bf16State<DQK, DV>& st, u32x4* tA, u32x4* tB,
+                                               int hb, size_t row, int rq, int split, int head, bool head_ok,
+                                               int pair, int half, int col, int kb, int tid)
+{
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (a.n_split == 1 && a.lse && head_ok && half == 0 && kb == 0)
+        a.lse[row * a.H + head] = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+
+    using P = PartRow<kBF16, DV>;
+    constexpr int SP = P::bytes;  // staged row pitch
+    static_assert(32 * SP <= C::BUF_CH * 16, "staging rows");
+    const bool part_out = a.n_split > 1;
+    const int hb0 = hb * kHeadsPerBlock;
+    const int heads_here = min(kHeadsPerBlock, a.H - hb0);
+    char* gbase = part_out ? (char*)a.part + (((size_t)rq * a.n_split + split) * a.H + hb0) * P::bytes
+                           : (char*)a.out + (row * a.H + hb0) * (size_t)(DV * 2);
+    const int grow = part_out ? P::bytes : DV * 2;  // bytes of a row in global memory
+    const int rch = grow / 16;
+    barrier_lds();  // every wave is done reading the last tile
+#pragma unroll 1
+    for (int round = 0; round < 2; ++round) {
+        if ((pair >> 1) == round) {
+            // lane holds value dims VH*half + 32*v + 8*i + 4*kb + jj (register 4*i + jj) of head `col`
+            char* sb = reinterpret_cast<char*>((pair & 1) ? tB : tA) + col * SP + (C::VH * half + 4 * kb) * 2;
+#pragma unroll
+            for (int v = 0; v < C::VT; ++v)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u32x2 w2 = {pack_bf16x2(st.o[v][4 * i] * inv, st.o[v][4 * i + 1] * inv),
+                                      pack_bf16x2(st.o[v][4 * i + 2] * inv, st.o[v][4 * i + 3] * inv)};
+                    *reinterpret_cast<u32x2*>(sb + 2 * (32 * v + 8 * i)) = w2;
+                }
+            if (half == 0 && kb == 0)
+                *reinterpret_cast<f32x4*>(reinterpret_cast<char*>((pair & 1) ? tB : tA) + col * SP + P::vbytes) =
+                    f32x4{st.m_run, l_tot, 0.f, 0.f};
+        }
+        barrier_lds();
+        const int h0 = 64 * round;
+        const int n = min(64, heads_here - h0) * rch;
+        for (int c = tid; c < n; c += 512) {
+            const int r = c / rch, k = c - r * rch;
+            const char* sb = reinterpret_cast<const char*>((r >> 5) ? tB : tA) + (r & 31) * SP + 16 * k;
+            st16(gbase + (size_t)(h0 + r) * grow + 16 * k, *reinterpret_cast<const u32x4*>(sb));
+        }
+        if (round == 0) barrier_lds();
+    }
+}
+
 // One 512-thread workgroup (8 waves, two per SIMD) owns a (query, split of the
 // index list) unit and 128 heads.  Wave w = (pair w/2, half w%2): heads
 // 32*(w/2).., contraction half and value half w%2.  Two LDS tile buffers named
@@ -267,7 +323,8 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
     const int per = ((a.K + a.n_split - 1) / a.n_split + kTileKeys - 1) / kTileKeys * kTileKeys;
     const int j_begin = split * per;
     const int j_end = min(a.K, j_begin + per);
-    const int n_tiles = j_end > j_begin ? (j_end - j_begin + kTileKeys - 1) / kTileKeys : 0;
+    // an empty sequence (L = 0) has no row to gather, not even the stand-in row 0
+    const int n_tiles = (j_end > j_begin && L > 0) ? (j_end - j_begin + kTileKeys - 1) / kTileKeys : 0;
 
     const char* kvb = (const char*)a.kv + (size_t)b * a.Lmax * C::ROWB;
     const int32_t* idxr = a.idx + row * a.K;
@@ -319,70 +376,248 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
     const float zc = a.sm_scale * kLog2e;
 
     // tile `it` lives in buffer it % 2; each step issues tile it + 1 into the other buffer
-    if (n_tiles > 0) gather_tile<DQK, DV>(kvb, lrow, 0, w, lane, tA);
+    if (n_tiles > 0) gather_tile<C>(kvb, lrow, 0, w, lane, tA);
 #pragma unroll 1
     for (int it = 0; it < n_tiles; it += 2) {
         barrier_lds_vm();
         // the tile's mask is read together with the next tile's row offsets
         const uint32_t vmA = tmask[it];
-        if (it + 1 < n_tiles) gather_tile<DQK, DV>(kvb, lrow, (it + 1) * kTileKeys, w, lane, tB);
+        if (it + 1 < n_tiles) gather_tile<C>(kvb, lrow, (it + 1) * kTileKeys, w, lane, tB);
         __builtin_amdgcn_sched_barrier(0);
         tile_compute<DQK, DV>(tA, vmA, qb, st, zc, xbuf, w, lane);
         if (it + 1 >= n_tiles) break;
         barrier_lds_vm();
         const uint32_t vmB = tmask[it + 1];
-        if (it + 2 < n_tiles) gather_tile<DQK, DV>(kvb, lrow, (it + 2) * kTileKeys, w, lane, tA);
+        if (it + 2 < n_tiles) gather_tile<C>(kvb, lrow, (it + 2) * kTileKeys, w, lane, tA);
         __builtin_amdgcn_sched_barrier(0);
         tile_compute<DQK, DV>(tB, vmB, qb, st, zc, xbuf, w, lane);
     }
 
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (a.n_split == 1 && a.lse && head_ok && half == 0 && kb == 0)
-        a.lse[row * a.H + head] = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    mla_write_rows<DQK, DV, C>(a, st, tA, tB, hb, row, rq, split, head, head_ok, pair, half, col, kb, tid);
+}
 
-    // One row per head: the normalised value row in bf16 (the output row, or a
-    // split's partial row followed by its fp32 m, l).  Rows are staged in the free
-    // tile buffers and written out whole, 16 contiguous bytes per lane: two rounds
-    // of 64 heads, the pair p of a round staging its 32 rows in buffer p % 2.
-    using P = PartRow<kBF16, DV>;
-    constexpr int SP = P::bytes;  // staged row pitch
-    static_assert(32 * SP <= C::BUF_CH * 16, "staging rows");
-    const bool part_out = a.n_split > 1;
-    const int hb0 = hb * kHeadsPerBlock;
-    const int heads_here = min(kHeadsPerBlock, a.H - hb0);
-    char* gbase = part_out ? (char*)a.part + (((size_t)rq * a.n_split + split) * a.H + hb0) * P::bytes
-                           : (char*)a.out + (row * a.H + hb0) * (size_t)(DV * 2);
-    const int grow = part_out ? P::bytes : DV * 2;  // bytes of a row in global memory
-    const int rch = grow / 16;
-    barrier_lds();  // every wave is done reading the last tile
-#pragma unroll 1
-    for (int round = 0; round < 2; ++round) {
-        if ((pair >> 1) == round) {
-            // lane holds value dims VH*half + 32*v + 8*i + 4*kb + jj (register 4*i + jj) of head `col`
-            char* sb = reinterpret_cast<char*>((pair & 1) ? tB : tA) + col * SP + (C::VH * half + 4 * kb) * 2;
+// ================================================================ fp8 kernel
+// The bf16 kernel's structure on e4m3 operands: the latent cache rows and the
+// queries as codes with one fp32 scale per row.  A cache row is DQK codes and
+// then 16 bytes holding its scale, so the gather brings the scale with the row.
+//   - QK^T runs on the 32x32x64 f8f6f4 MFMA (twice the bf16 rate): wave half 0
+//     takes dims [0, D0), half 1 [D0, DQK), in 64-deep steps; both operands hold
+//     32 consecutive dims per lane, so the contraction order inside a step is
+//     the same for both.  Logit = S * k_scale[key] * q_scale[head] * sm_scale.
+//   - PV stays on bf16 MFMA (e4m3 weights would cost up to 6% per weight).  The
+//     8-bit transpose load gives a lane 8 keys of one value column (inside a
+//     16-lane group, lane i receives byte j from the address of lane 2j + i/8,
+//     at offset i%8), which convert exactly to bf16; the weights carry the key
+//     scale, P'[key, head] = p * k_scale[key].
+template <int DQK, int DV>
+struct Fp8Cfg {
+    static constexpr int ROWB = DQK + 16;       // bytes of a cache row (codes + scale)
+    static constexpr int CPR = ROWB / 16;       // 16-byte chunks per row, scale chunk included
+    static constexpr int PCH = CPR;             // LDS pitch in chunks (odd: conflict-free 16-byte columns)
+    static constexpr int PITCH = PCH * 16;
+    static constexpr int TILE_CH = kTileKeys * PCH;
+    static constexpr int DMA_PER_WAVE = (TILE_CH + 511) / 512;
+    static constexpr int STAGE_CH = kTileKeys * (DV * 2 + 16) / 16;  // the epilogue's 32 staged rows
+    static constexpr int BUF_CH = DMA_PER_WAVE * 512 > STAGE_CH ? DMA_PER_WAVE * 512 : STAGE_CH;
+    static constexpr int D0 = ((DQK / 64 + 1) / 2) * 64;        // dims of wave half 0
+    static constexpr int NS0 = D0 / 64, NS1 = (DQK - D0) / 64;  // 64-deep steps of each half
+    static constexpr int VH = DV / 2;
+    static constexpr int VT = VH / 32;
+    static_assert(DQK % 64 == 0 && DV % 64 == 0 && DV <= DQK && CPR % 2 == 1, "shape");
+};
+
+__device__ __forceinline__ f32x16 mfma32_fp8(const i32x8& a, const i32x8& b, f32x16 c)
+{
+    // formats 0/0: both operands OCP e4m3; unit block scales (127 = 2^0)
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <int DQK, int DV>
+__device__ __forceinline__ void tile_compute8(const u32x4* tile, uint32_t vmask,
+                                              const i32x8 (&qb)[Fp8Cfg<DQK, DV>::NS0], float zch,
+                                              Bf16State<DQK, DV>& st, float (*xbuf)[16][64], int w, int lane)
+{
+    using C = Fp8Cfg<DQK, DV>;
+    asm volatile("" : "+v"(lane));  // lane-derived addresses are recomputed per tile, not kept live
+    const int col = lane & 31, kb = lane >> 5, half = w & 1;
+    const char* tb = reinterpret_cast<const char*>(tile);
+    f32x16 sacc;
 #pragma unroll
-            for (int v = 0; v < C::VT; ++v)
+    for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+    const char* kr = tb + col * C::PITCH + (half ? C::D0 : 0) + 32 * kb;
+    const int ns = half ? C::NS1 : C::NS0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x2 w2 = {pack_bf16x2(st.o[v][4 * i] * inv, st.o[v][4 * i + 1] * inv),
-                                      pack_bf16x2(st.o[v][4 * i + 2] * inv, st.o[v][4 * i + 3] * inv)};
-                    *reinterpret_cast<u32x2*>(sb + 2 * (32 * v + 8 * i)) = w2;
-                }
-            if (half == 0 && kb == 0)
-                *reinterpret_cast<f32x4*>(reinterpret_cast<char*>((pair & 1) ? tB : tA) + col * SP + P::vbytes) =
-                    f32x4{st.m_run, l_tot, 0.f, 0.f};
+    for (int s = 0; s < C::NS0; ++s) {
+        if (s < ns) {
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(kr + 64 * s);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(kr + 64 * s + 16);
+            const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            sacc = mfma32_fp8(a, qb[s], sacc);
         }
-        barrier_lds();
-        const int h0 = 64 * round;
-        const int n = min(64, heads_here - h0) * rch;
-        for (int c = tid; c < n; c += 512) {
-            const int r = c / rch, k = c - r * rch;
-            const char* sb = reinterpret_cast<const char*>((r >> 5) ? tB : tA) + (r & 31) * SP + 16 * k;
-            st16(gbase + (size_t)(h0 + r) * grow + 16 * k, *reinterpret_cast<const u32x4*>(sb));
-        }
-        if (round == 0) barrier_lds();
     }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xbuf[w][e][lane] = sacc[e];
+    barrier_lds();
+    // lane holds keys 8*i + 4*kb + j (register 4*i + j) of head `col`; the key
+    // scales sit after each row's codes in the tile
+    float ks[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        ks[e] = *reinterpret_cast<const float*>(tb + (8 * (e >> 2) + 4 * kb + (e & 3)) * C::PITCH + DQK);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int key = 8 * (e >> 2) + 4 * kb + (e & 3);
+        const float sv = (sacc[e] + xbuf[w ^ 1][e][lane]) * ks[e];
+        sacc[e] = ((vmask >> key) & 1u) ? sv : -INFINITY;
+        tmax = fmaxf(tmax, sacc[e]);
+    }
+    {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1])) * zch;
+    }
+    if (__ballot(tmax > st.m_run + 8.f)) {
+        const float m_new = fmaxf(st.m_run, tmax);
+        const float alpha = st.m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+        st.l_run *= alpha;
+#pragma unroll
+        for (int v = 0; v < C::VT; ++v) st.o[v] *= alpha;
+        st.m_run = m_new;
+    }
+    const float m_use = st.m_run == -INFINITY ? 0.f : st.m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        sacc[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e], zch, -m_use));
+        psum += sacc[e];
+    }
+    st.l_run += psum;
+    // transpose-load roles: this lane supplies, for element j = (lane % 16) / 2 of
+    // its 16-lane group, the row of key(j) and the column half (lane & 1)
+    const int li = lane & 15, gh = (lane >> 4) & 1;
+    const int jj = li >> 1;
+    const int krow = (jj < 4 ? 4 * kb + jj : 8 + 4 * kb + (jj - 4));
+    const char* vsrc = tb + krow * C::PITCH + C::VH * half + 16 * gh + 8 * (li & 1);
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+        u32x4 pb;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            pb[t] = pack_bf16x2(sacc[8 * step + 2 * t] * ks[8 * step + 2 * t],
+                                sacc[8 * step + 2 * t + 1] * ks[8 * step + 2 * t + 1]);
+#pragma unroll
+        for (int v = 0; v < C::VT; ++v) {
+            typedef int v2i __attribute__((ext_vector_type(2)));
+            const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) v2i*)(vsrc + 16 * step * C::PITCH + 32 * v));
+            const f32x2 a01 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[0], false);
+            const f32x2 a23 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[0], true);
+            const f32x2 a45 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[1], false);
+            const f32x2 a67 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[1], true);
+            const u32x4 va = {pack_bf16x2(a01[0], a01[1]), pack_bf16x2(a23[0], a23[1]),
+                              pack_bf16x2(a45[0], a45[1]), pack_bf16x2(a67[0], a67[1])};
+            st.o[v] = mfma32_bf16(va, pb, st.o[v]);
+        }
+    }
+}
+
+// Same work unit, waves, list set-up, gather pipeline and epilogue as the bf16 kernel.
+template <int DQK, int DV>
+__global__ __launch_bounds__(512) void mla_fp8_kernel(MlaArgs a)
+{
+    using C = Fp8Cfg<DQK, DV>;
+    __shared__ __attribute__((aligned(16))) u32x4 tA[C::BUF_CH];
+    __shared__ __attribute__((aligned(16))) u32x4 tB[C::BUF_CH];
+    __shared__ float xbuf[8][16][64];
+    __shared__ uint32_t lrow[kMaxListLen];
+    __shared__ uint32_t tmask[kMaxListLen / kTileKeys];
+
+    const int HB = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    const int n_units = a.B * a.t_count * a.n_split * HB;
+    const int unit = xcd_unit(blockIdx.x, n_units);
+    if (unit >= n_units) return;
+    const int hb = unit % HB;
+    const int split = (unit / HB) % a.n_split;
+    const int rq = unit / HB / a.n_split;
+    const int b = rq / a.t_count;
+    const int t = a.t_begin + rq % a.t_count;
+    const size_t row = (size_t)b * a.T + t;
+    const int L = min(a.kv_len[b], a.Lmax);
+
+    const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    const int pair = w >> 1, half = w & 1;
+    const int col = lane & 31, kb = lane >> 5;
+    const int head = hb * kHeadsPerBlock + pair * 32 + col;
+    const bool head_ok = head < a.H;
+
+    const int per = ((a.K + a.n_split - 1) / a.n_split + kTileKeys - 1) / kTileKeys * kTileKeys;
+    const int j_begin = split * per;
+    const int j_end = min(a.K, j_begin + per);
+    // an empty sequence (L = 0) has no row to gather, not even the stand-in row 0
+    const int n_tiles = (j_end > j_begin && L > 0) ? (j_end - j_begin + kTileKeys - 1) / kTileKeys : 0;
+
+    const char* kvb = (const char*)a.kv + (size_t)b * a.Lmax * C::ROWB;
+    const int32_t* idxr = a.idx + row * a.K;
+    constexpr int kListPer = kMaxListLen / 512;
+    const int n_list = n_tiles * kTileKeys;
+    const int j_last = max(j_end - 1, 0);
+    int raw[kListPer];
+#pragma unroll
+    for (int r = 0; r < kListPer; ++r) raw[r] = idxr[min(j_begin + tid + 512 * r, j_last)];
+    // Q^T operand: head `head`, dims [D0 * half + 64 s + 32 kb, + 32) of step s
+    // (half 1 reloads its last step for the unused fifth, so every load is valid)
+    const size_t qrow = row * a.H + (head_ok ? head : 0);
+    i32x8 qb[C::NS0];
+    {
+        const char* src = (const char*)a.q + qrow * DQK + (half ? C::D0 : 0) + 32 * kb;
+        const int ns = half ? C::NS1 : C::NS0;
+#pragma unroll
+        for (int s = 0; s < C::NS0; ++s) {
+            const char* p = src + 64 * min(s, ns - 1);
+            const u32x4 lo = ld16(p), hi = ld16(p + 16);
+            qb[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+    }
+    const float zch = a.sm_scale * kLog2e * a.q_scale[qrow];
+#pragma unroll
+    for (int r = 0; r < kListPer; ++r) {
+        const int j = tid + 512 * r;
+        const int s = raw[r];
+        const bool ok = j < n_list && j_begin + j < j_end && s >= 0 && s < L;
+        lrow[j] = ok ? (uint32_t)s * C::ROWB : 0u;
+        const uint64_t bits = __ballot(ok);
+        if (lane == 0) {  // j is a multiple of 64 here, so both words lie inside tmask
+            tmask[j / kTileKeys] = (uint32_t)bits;
+            tmask[j / kTileKeys + 1] = (uint32_t)(bits >> 32);
+        }
+    }
+    barrier_lds();
+
+    Bf16State<DQK, DV> st;
+#pragma unroll
+    for (int v = 0; v < C::VT; ++v)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st.o[v][e] = 0.f;
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+
+    if (n_tiles > 0) gather_tile<C>(kvb, lrow, 0, w, lane, tA);
+#pragma unroll 1
+    for (int it = 0; it < n_tiles; it += 2) {
+        barrier_lds_vm();
+        const uint32_t vmA = tmask[it];
+        if (it + 1 < n_tiles) gather_tile<C>(kvb, lrow, (it + 1) * kTileKeys, w, lane, tB);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_compute8<DQK, DV>(tA, vmA, qb, zch, st, xbuf, w, lane);
+        if (it + 1 >= n_tiles) break;
+        barrier_lds_vm();
+        const uint32_t vmB = tmask[it + 1];
+        if (it + 2 < n_tiles) gather_tile<C>(kvb, lrow, (it + 2) * kTileKeys, w, lane, tA);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_compute8<DQK, DV>(tB, vmB, qb, zch, st, xbuf, w, lane);
+    }
+    mla_write_rows<DQK, DV, C>(a, st, tA, tB, hb, row, rq, split, head, head_ok, pair, half, col, kb, tid);
 }
 
 // ================================================================ fp32 kernel
@@ -633,6 +868,16 @@ hipError_t launch_bf16(const MlaArgs& a, hipStream_t s)
 }
 
 template <int DQK, int DV>
+hipError_t launch_fp8(const MlaArgs& a, hipStream_t s)
+{
+    const int HB = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    const long long units = (long long)a.B * a.t_count * a.n_split * HB;
+    mla_fp8_kernel<DQK, DV><<<dim3((unsigned)(8 * ((units + 7) / 8))), 512, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_combine<kBF16, DV>(a, s);
+}
+
+template <int DQK, int DV>
 hipError_t launch_f32(const MlaArgs& a, hipStream_t s)
 {
     const int HG = (a.H + 15) / 16;
@@ -648,6 +893,7 @@ bool mla_supported(int dtype, int Dqk, int Dv)
 {
     if (dtype == kF32) return Dqk == 80 && Dv == 64;
     if (dtype == kBF16) return (Dqk == 576 && Dv == 512) || (Dqk == 192 && Dv == 128);
+    if (dtype == kFP8) return Dqk == 576 && Dv == 512;
     return false;
 }
 
@@ -666,13 +912,14 @@ int mla_split_count(int B, int t_count, int H, int K)
 size_t mla_partial_bytes(int dtype, int B, int t_count, int H, int Dv, int n_split)
 {
     if (n_split <= 1) return 0;
-    return (size_t)B * t_count * n_split * H * ((size_t)Dv * (dtype == kBF16 ? 2 : 4) + 16);
+    return (size_t)B * t_count * n_split * H * ((size_t)Dv * (dtype == kF32 ? 4 : 2) + 16);
 }
 
 hipError_t launch_mla(int dtype, const MlaArgs& a, hipStream_t s)
 {
     if (a.t_count <= 0 || a.B <= 0) return hipSuccess;
     if (dtype == kF32) return launch_f32<80, 64>(a, s);
+    if (dtype == kFP8) return launch_fp8<576, 512>(a, s);
     if (a.Dqk == 192) return launch_bf16<192, 128>(a, s);
     return launch_bf16<576, 512>(a, s);
 }

@@ -91,8 +91,20 @@ def test_topk_and_mla_reject_bad_arguments(dsa):
     assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == -2
     s = _shape(dsa, qk_dim=320, v_dim=256)
     assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == -6
+    s = _shape(dsa, mla_dtype="fp8", qk_dim=192, v_dim=128)
+    assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == -6
+    cs = _shape(dsa).c()
+    cs.mla_dtype = 7
+    assert L.dsa_sparse_mla_fwd(ctypes.byref(cs), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == -3
+    # the fp8 path quantises the queries into the workspace, so it always needs one
     s = _shape(dsa, mla_dtype="fp8")
-    assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == -3
+    need = dsa.sparse_mla_workspace_size(s)
+    assert need >= 2 * 4 * 128 * (576 + 4)
+    assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == -5
+    assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1, None) == -5
+    assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 8, need, None) == -4
+    sb = _shape(dsa, mla_dtype="bf16")
+    assert dsa.sparse_mla_workspace_size(sb) < need
     for bad_scale in (float("nan"), 0.0, -0.07):
         s = _shape(dsa, sm_scale=bad_scale)
         assert L.dsa_sparse_mla_fwd(ctypes.byref(s.c()), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == -2
@@ -138,6 +150,19 @@ def test_cache_append_rejects_bad_arguments(dsa):
     assert f(2, 1, 16, 128, FAKE + 4, 1, FAKE, FAKE, FAKE, None) == -4
     assert f(2, 1, 16, 128, FAKE, 1, FAKE, FAKE + 8, FAKE, None) == -4
     assert L.dsa_rotate_quant_fp8(4, 128, FAKE + 4, 1, FAKE, FAKE, None) == -4
+
+
+def test_mla_kv_quant_rejects_bad_arguments(dsa):
+    f = dsa.lib().dsa_mla_kv_quant_fp8
+    assert f(0, 576, FAKE, 1, FAKE, None) == -2
+    assert f(4, 0, FAKE, 1, FAKE, None) == -2
+    assert f(4, 584, FAKE, 1, FAKE, None) == -6
+    assert f(4, 1040, FAKE, 1, FAKE, None) == -6
+    assert f(4, 576, FAKE, 2, FAKE, None) == -3
+    assert f(4, 576, None, 1, FAKE, None) == -1
+    assert f(4, 576, FAKE, 1, None, None) == -1
+    assert f(4, 576, FAKE + 8, 1, FAKE, None) == -4
+    assert f(4, 576, FAKE, 0, FAKE + 4, None) == -4
 
 
 def test_forward_workspace_sizes_and_checks(dsa):

@@ -1,7 +1,8 @@
 """GPU parity of each entry point against the CPU oracle (same seeded inputs).
 
 Entry points: dsa_rotate_quant_fp8, dsa_index_scores, dsa_topk,
-dsa_sparse_mla_fwd, all called through the C ABI.  Integer-valued inputs make
+dsa_sparse_mla_fwd (bf16, f32 and fp8), dsa_mla_kv_quant_fp8, all called
+through the C ABI.  Integer-valued inputs make
 the indexer exact on both sides (bit-for-bit comparison); Gaussian inputs are
 compared at the dtype tolerance; top-k is compared exactly on shared score rows.
 """
@@ -214,7 +215,7 @@ def _mla_case(B, T, H, Dqk, Dv, Lmax, lens, K, dt, seed, kind="topk"):
             n = max(0, min(K, p + 1))
             perm = torch.randperm(max(p + 1, 1), generator=g)[:n]
             idx[b, t, :n] = perm.int()
-            if kind == "messy" and K >= 8:
+            if kind in ("messy", "poison") and K >= 8:
                 idx[b, t, 0] = idx[b, t, 1]          # a duplicate
                 idx[b, t, 2] = lens[b] + 5           # out of range -> skipped
                 idx[b, t, 3] = -7                    # negative -> skipped
@@ -229,13 +230,23 @@ MLA_CASES = [
     (1, 40, 128, 576, 512, 1000, [1000], 256, "bf16", "messy"),
     (2, 5, 20, 192, 128, 600, [600, 300], 128, "bf16", "topk"),
     (3, 2, 128, 576, 512, 64, [64, 2, 1], 32, "bf16", "topk"),
+    # rows past kv_len hold NaN (one sequence is empty): they must never be read
+    (3, 2, 128, 576, 512, 80, [80, 0, 1], 32, "bf16", "poison"),
 ]
+
+
+def _poison_rows(kv, lens, value):
+    for b, L in enumerate(lens):
+        kv[b, L:] = value
 
 
 @pytest.mark.parametrize("case", MLA_CASES)
 def test_sparse_mla_against_oracle(dsa, orc, case):
     B, T, H, Dqk, Dv, Lmax, lens, K, dt, kind = case
     q, kv, idx, kl = _mla_case(B, T, H, Dqk, Dv, Lmax, lens, K, dt, seed=B * 1000 + T + H, kind=kind)
+    if kind == "poison":
+        _poison_rows(kv, lens, float("nan"))
+    announce(f"sparse_mla {case}")
     sm = Dqk ** -0.5
     s = shape_of(dsa, batch=B, n_q=T, max_kv=Lmax, heads=H, qk_dim=Dqk, v_dim=Dv, topk=K, sm_scale=sm,
                  mla_dtype=dt)
@@ -256,3 +267,77 @@ def test_sparse_mla_against_oracle(dsa, orc, case):
     err = rel_rowmax(out[live], ro[live])
     assert err.max() < TOL[dt], err.max()
     assert np.abs(lse[live] - rl[live]).max() < TOL[dt] * max(1.0, np.abs(rl[live]).max())
+
+
+# ------------------------------------------------ fp8 latent cache and fp8 MLA
+@pytest.mark.parametrize("dim,xdt", [(576, torch.bfloat16), (576, torch.float32), (16, torch.bfloat16),
+                                     (512, torch.bfloat16), (1024, torch.float32)])
+def test_mla_kv_quant_rows_exact(dsa, orc, dim, xdt):
+    """fp8 latent-cache rows: codes, scale and zero pad bit-identical to the oracle's."""
+    g = torch.Generator().manual_seed(dim + 7)
+    x = torch.randn(3, 37, dim, generator=g) * torch.exp(2 * torch.randn(3, 37, 1, generator=g))
+    x[0, 5] = 0.0                  # zero row: codes 0, scale 1
+    x[1, 2, 3] = 1e4               # one dominant entry
+    x[2, 9] = torch.randint(-3, 4, (dim,), generator=g).float() * 64  # few distinct values
+    x = x.to(xdt)
+    announce(f"mla_kv_quant dim={dim} {xdt}")
+    got = dsa.mla_kv_quant_fp8(x.to(DEV)).cpu().numpy()
+    assert np.array_equal(got, orc.kv_rows_fp8(x))
+
+
+def test_mla_kv_quant_appends_into_a_cache(dsa, orc):
+    """Pointing kv_rows at row p of a cache writes rows p.. only."""
+    g = torch.Generator().manual_seed(5)
+    cache = torch.full((2, 50, 592), 0xCD, dtype=torch.uint8, device=DEV)
+    x = torch.randn(3, 576, generator=g).to(torch.bfloat16)
+    announce("mla_kv_quant append")
+    dsa.mla_kv_quant_fp8(x.to(DEV), kv_rows=cache[1, 10:13])
+    c = cache.cpu().numpy()
+    assert np.array_equal(c[1, 10:13], orc.kv_rows_fp8(x))
+    keep = np.ones((2, 50), dtype=bool)
+    keep[1, 10:13] = False
+    assert np.all(c[keep] == 0xCD)
+
+
+MLA_FP8_CASES = [
+    # B, T, H, Lmax, lens, K, kind
+    (4, 1, 128, 4096, [4096, 3000, 2048, 700], 2048, "topk"),   # decode: the list is split, then combined
+    (1, 40, 128, 1000, [1000], 256, "messy"),
+    (3, 2, 128, 64, [64, 2, 1], 32, "topk"),
+    (2, 3, 20, 300, [300, 150], 96, "topk"),                     # a partial head block
+    (1, 2, 200, 128, [128], 64, "topk"),                         # two head blocks
+    (3, 2, 128, 80, [80, 0, 1], 32, "poison"),                   # rows past kv_len are NaN bytes
+]
+
+
+@pytest.mark.parametrize("case", MLA_FP8_CASES)
+def test_sparse_mla_fp8_against_oracle(dsa, orc, case):
+    """fp8 MLA on cache rows from dsa_mla_kv_quant_fp8 (bit-checked above) against the
+    oracle on its own codes of the same inputs.  Both sides attend over the same
+    dequantised values, so the tolerance is the bf16 path's (bf16 weights and output)."""
+    B, T, H, Lmax, lens, K, kind = case
+    q, kv, idx, kl = _mla_case(B, T, H, 576, 512, Lmax, lens, K, "bf16", seed=B * 977 + T + H, kind=kind)
+    sm = 192 ** -0.5
+    s = shape_of(dsa, batch=B, n_q=T, max_kv=Lmax, heads=H, topk=K, sm_scale=sm, mla_dtype="fp8")
+    announce(f"sparse_mla fp8 {case}")
+    rows = dsa.mla_kv_quant_fp8(kv.to(DEV))
+    if kind == "poison":
+        _poison_rows(rows, lens, 0xFF)  # e4m3 NaN codes and a NaN scale
+    out, lse = dsa.sparse_mla_fwd(s, q.to(DEV), rows, idx.to(DEV), kl.to(DEV))
+    assert out.dtype == torch.bfloat16
+    out = out.float().cpu().numpy().reshape(B * T, H, 512)
+    lse = lse.cpu().numpy().reshape(B * T, H)
+    ix = idx.clone().reshape(B * T, K)
+    for r in range(B * T):
+        L = lens[r // T]
+        ix[r][(ix[r] >= L) | (ix[r] < 0)] = -1
+    qc, qs = orc.quant(q)
+    kc, ks = orc.quant(kv)
+    ro, rl = orc.sparse_mla_fp8(qc, qs, kc, ks, ix, sm, v_dim=512)
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(lse), empty)
+    assert np.all(out[empty] == 0)
+    live = ~empty
+    err = rel_rowmax(out[live], ro[live])
+    assert err.max() < TOL["bf16"], err.max()
+    assert np.abs(lse[live] - rl[live]).max() < TOL["bf16"] * max(1.0, np.abs(rl[live]).max())

@@ -1,4 +1,4 @@
-"""Synthetic DSA workloads: shapes of the five measured/checked configurations
+"""Synthetic DSA workloads: shapes of the measured/checked configurations
 and the seeded input generators that both the HIP path and the CPU oracle
 consume.  Nothing here computes any step of the method."""
 from .configs import WORKLOADS, Workload, get  # noqa: F401

@@ -28,7 +28,7 @@ class Workload:
     v_dim: int          # kv_lora_rank
     sm_scale: float
     idx_dtype: str      # "f32" | "bf16" | "fp8"
-    mla_dtype: str      # "f32" | "bf16"
+    mla_dtype: str      # "f32" | "bf16" | "fp8" (e4m3 latent cache and queries, bf16 output)
     heavy_frac: float = 0.0       # share of key positions whose index-key and kv rows are scaled by 4
     lognormal_sigma: float = 0.0  # per-token row scale exp(sigma * z)
     seed: int = 0
@@ -65,9 +65,14 @@ WORKLOADS = {
         mla_dtype="bf16", lognormal_sigma=0.5,
         description="decode, fp8 e4m3 indexer behind a Hadamard rotation, bf16 MLA, 16 x context 131072",
         **V32),
+    "decode_128k_fp8_mla": Workload(
+        name="decode_128k_fp8_mla", batch=16, n_q=1, max_kv=131072, kv_len=131072, idx_dtype="fp8",
+        mla_dtype="fp8", lognormal_sigma=0.5,
+        description="decode, fp8 indexer and fp8 e4m3 latent cache for the MLA, 16 x context 131072",
+        **V32),
 }
 
-ORDER = ["tiny_f32", "prefill_4k", "decode_32k", "prefill_32k", "decode_128k_fp8"]
+ORDER = ["tiny_f32", "prefill_4k", "decode_32k", "prefill_32k", "decode_128k_fp8", "decode_128k_fp8_mla"]
 
 
 def get(name: str) -> Workload:

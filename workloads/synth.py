@@ -14,7 +14,8 @@ q and kv is multiplied by exp(sigma * z_pos), one z per position (a query
 uses the factor of its own position kv_len - T + t).
 
 With an fp8 indexer, q_idx and k_idx are still returned in bf16, before any
-rotation; the rotation and quantisation belong to the method.
+rotation; with an fp8 MLA, q and kv are returned in bf16 as well: the
+quantisation belongs to the method.
 """
 from __future__ import annotations
 
@@ -43,7 +44,7 @@ def make_inputs(wl, device="cpu", seqs=None, kv_len=None, seed=None, with_mla=Tr
     seed = wl.seed if seed is None else seed
     seqs = list(range(wl.batch)) if seqs is None else list(seqs)
     idt = _DT["bf16" if wl.idx_dtype == "fp8" else wl.idx_dtype]
-    mdt = _DT[wl.mla_dtype]
+    mdt = _DT["bf16" if wl.mla_dtype == "fp8" else wl.mla_dtype]
     T, Lmax = wl.n_q, wl.max_kv
     lens = [wl.kv_len] * len(seqs) if kv_len is None else list(kv_len)
     out = {k: [] for k in ("q_idx", "w", "k_idx", "q", "kv")}

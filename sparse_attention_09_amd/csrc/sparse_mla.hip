@@ -396,6 +396,727 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
     mla_write_rows<DQK, DV, C>(a, st, tA, tB, hb, row, rq, split, head, head_ok, pair, half, col, kb, tid);
 }
 
+// ================================================================ wide bf16 kernel
+// One 256-thread workgroup (four waves, one per SIMD) per (query, split, 128
+// heads).  Wave w owns heads 32w .. 32w + 31 over the whole contraction and the
+// whole value row: no logits are exchanged between waves and no softmax is
+// computed twice.  With one wave per SIMD the softmax's VALU work issues
+// beside the MFMAs of the same wave (a 32x32x16 MFMA hides about four VALU
+// instructions there, while at two waves per SIMD with VGPR accumulators the
+// two add up).  The value accumulators (DV x 32 heads per wave) take the
+// accumulation registers.  Three LDS tile buffers keep two gathers in flight.
+// The gathers are issued from inline asm, so the compiler's tracking of direct
+// LDS loads cannot turn them into a full wait before every LDS read; the waits
+// on them are explicit (vmcnt counts a wave's loads in issue order).
+template <int DQK, int DV>
+struct WideCfg {
+    static constexpr int NT = 256;                 // threads per workgroup
+    static constexpr int NW = NT / 64;
+    static constexpr int ROWB = DQK * 2;
+    static constexpr int CPR = DQK / 8;
+    static constexpr int PCH = CPR + 1;            // odd pitch in chunks: conflict-free 16-byte columns
+    static constexpr int PITCH = PCH * 16;
+    static constexpr int TILE_CH = kTileKeys * PCH;
+    static constexpr int DMA = (TILE_CH + NT - 1) / NT;  // direct loads per wave per tile
+    static constexpr int BUF_CH = DMA * NT;
+    static constexpr int NBUF = 3;
+    static constexpr int QS = DQK / 16;            // 32x32x16 steps over the contraction
+    static constexpr int HQ = DQK / 2;             // contraction share of a lane half
+    static constexpr int VT = DV / 32;             // 32-row value tiles
+    static constexpr int K_AHEAD = 4;              // key reads in flight ahead of the logit MFMAs
+    static constexpr int V_AHEAD = 4;              // value reads in flight ahead of the value MFMAs
+    static_assert(DQK % 32 == 0 && DV % 32 == 0 && DV <= DQK, "shape");
+};
+
+// The logits' 32x32x16 bf16 MFMAs, written as asm so that their accumulator stays
+// in VGPRs (the softmax reads it) while the compiler gives the value
+// accumulators every AGPR; left to itself it puts both in AGPRs and spills.
+// The compiler does not see these as MFMAs: wait_mfma_acc() covers the hazard
+// before other instructions read the result.
+__device__ __forceinline__ void mfma32_bf16_vfirst(u32x4 a, u32x4 b, f32x16& acc)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_bf16_vacc(u32x4 a, u32x4 b, f32x16& acc)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// 18 wait states: more than a 32x32x16 MFMA's result needs before other
+// instructions may read its destination.  Taking the result as an operand keeps
+// every later reader after the wait.
+__device__ __forceinline__ void wait_mfma_acc(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 1" : "+v"(x)); }
+
+// The wide kernel's softmax keeps a per-head reference m (log2 domain) instead
+// of the running maximum: p = 2^(z - m) stays below 2^kWideSlack, far inside
+// fp32 and bf16 range.  A logit more than kWideSlack above m (never on the
+// first valid tile, which sets m) restarts the unit from its first tile with
+// the raised reference, so the value accumulators are never rescaled by VALU
+// code inside the tile loop, which would make the compiler move them out of
+// the AGPRs on every iteration.
+constexpr float kWideSlack = 64.f;
+
+template <int DQK, int DV>
+struct WideState {
+    f32x16 o[WideCfg<DQK, DV>::VT];
+    float m_run, l_run;
+};
+
+// Direct loads of index-list tile [j0, j0 + 32) into LDS, as gather_tile but for
+// NT threads and issued from asm: gather_offsets reads the row offsets of this
+// lane's DMA loads from LDS, gather_issue issues load k (M0 holds the wave's LDS
+// destination).
+template <class C>
+__device__ __forceinline__ void gather_offsets(const uint32_t* lrow, int j0, int w, int lane, uint32_t (&off)[C::DMA])
+{
+    constexpr int DR = C::NT / C::PCH, DCH = C::NT % C::PCH;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    int r = (wu * 64 + ln) / C::PCH;
+    int c = wu * 64 + ln - r * C::PCH;
+#pragma unroll
+    for (int k = 0; k < C::DMA; ++k) {
+        off[k] = lrow[j0 + min(r, kTileKeys - 1)] + (c == C::CPR ? 0u : (uint32_t)c * 16u);
+        r += DR;
+        c += DCH;
+        if (c >= C::PCH) {
+            c -= C::PCH;
+            ++r;
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void gather_issue(const char* kvb, uint32_t off, u32x4* dst, int w, int k)
+{
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) u32x4*)(dst + (wu + C::NW * k) * 64));
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(kvb), "{m0}"(lds) : "memory");
+}
+
+template <class C>
+__device__ __forceinline__ void gather_tile_asm(const char* kvb, const uint32_t* lrow, int j0, int w, int lane,
+                                                u32x4* dst)
+{
+    uint32_t off[C::DMA];
+    gather_offsets<C>(lrow, j0, w, lane, off);
+#pragma unroll
+    for (int k = 0; k < C::DMA; ++k) gather_issue<C>(kvb, off[k], dst, w, k);
+}
+
+// A gather carried out by the tile computation: its loads are issued one at a
+// time between the logit MFMAs, so that they queue behind no other wave's burst
+// and the wave keeps issuing MFMAs meanwhile.  Load k's row offset is read from
+// LDS a few MFMAs before it is issued; (r, c) step through this lane's
+// positions as in gather_offsets.
+template <class C>
+struct PendingGather {
+    const char* kvb;
+    u32x4* dst;
+    const uint32_t* lrow;  // entry j0 of the tile's list
+    int r, c;
+    bool active;
+    __device__ __forceinline__ void start(int w, int lane)
+    {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int wu = __builtin_amdgcn_readfirstlane(w);
+        r = (wu * 64 + ln) / C::PCH;
+        c = wu * 64 + ln - r * C::PCH;
+    }
+    __device__ __forceinline__ uint32_t next_offset()
+    {
+        constexpr int DR = C::NT / C::PCH, DCH = C::NT % C::PCH;
+        const uint32_t off = lrow[min(r, kTileKeys - 1)] + (c == C::CPR ? 0u : (uint32_t)c * 16u);
+        r += DR;
+        c += DCH;
+        if (c >= C::PCH) {
+            c -= C::PCH;
+            ++r;
+        }
+        return off;
+    }
+};
+
+// Wait until at most N direct loads of this wave are outstanding and its LDS
+// traffic is done, then s_barrier.
+template <int N>
+__device__ __forceinline__ void barrier_vm()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+// One 32-key tile for one wave: S^T[32 keys x 32 heads] = K . Q^T over the whole
+// contraction, online softmax, O^T[DV x 32 heads] += V^T . P^T.  The LDS reads
+// feeding the MFMAs go in groups of four steps, the next group's reads issued
+// before the current group's MFMAs, with a scheduling barrier between groups:
+// without it the compiler hoists every read of the tile and spills the queries.
+template <int DQK, int DV>
+__device__ __forceinline__ bool tile_compute_wide(const u32x4* tile, uint32_t vmask,
+                                                  const u32x4 (&qb)[WideCfg<DQK, DV>::QS], WideState<DQK, DV>& st,
+                                                  float zc, int lane, int w, PendingGather<WideCfg<DQK, DV>>& pg)
+{
+    using C = WideCfg<DQK, DV>;
+    constexpr int GAP = C::QS / C::DMA;  // logit steps between two loads of the pending gather
+    static_assert(GAP >= 1, "gather spacing");
+    constexpr int DK = C::K_AHEAD, DVW = C::V_AHEAD;
+    asm volatile("" : "+v"(lane));
+    const int col = lane & 31, kb = lane >> 5;
+    const char* tb = reinterpret_cast<const char*>(tile);
+    f32x16 sacc;
+    const char* kr = tb + col * C::PITCH + C::HQ * kb * 2;
+    {
+        // rolling window: the read for step s + DK is issued before the MFMA of step s
+        uint32_t goff = 0;
+        u32x4 kw[DK];
+#pragma unroll
+        for (int j = 0; j < DK; ++j) kw[j] = *reinterpret_cast<const u32x4*>(kr + 16 * j);
+#pragma unroll
+        for (int st_ = 0; st_ < C::QS; ++st_) {
+            const u32x4 ka = kw[st_ % DK];
+            if (st_ + DK < C::QS) kw[st_ % DK] = *reinterpret_cast<const u32x4*>(kr + 16 * (st_ + DK));
+            if (st_ == 0)
+                mfma32_bf16_vfirst(ka, qb[0], sacc);
+            else
+                mfma32_bf16_vacc(ka, qb[st_], sacc);
+            if (st_ % GAP == 0 && st_ / GAP < C::DMA) goff = pg.next_offset();
+            if (st_ % GAP == GAP - 1 && st_ / GAP < C::DMA && pg.active)
+                gather_issue<C>(pg.kvb, goff, pg.dst, w, st_ / GAP);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_mfma_acc(sacc);
+    // lane holds keys 8*i + 4*kb + j (register 4*i + j) of head `col`
+    float tmax = -INFINITY;
+    if (vmask == 0xFFFFFFFFu) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sacc[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int key = 8 * (e >> 2) + 4 * kb + (e & 3);
+            sacc[e] = ((vmask >> key) & 1u) ? sacc[e] : -INFINITY;
+            tmax = fmaxf(tmax, sacc[e]);
+        }
+    }
+    {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1])) * zc;
+    }
+    if (__ballot(tmax > st.m_run + kWideSlack)) {
+        // a head with no valid key so far takes this tile's maximum (its sums are
+        // zero); a head whose reference is exceeded by more than the slack needs
+        // a restart, and this tile's value sum is skipped
+        const bool over = __ballot(st.m_run != -INFINITY && tmax > st.m_run + kWideSlack) != 0;
+        if (tmax > st.m_run + kWideSlack) st.m_run = tmax;
+        if (over) return true;
+    }
+    const float m_use = st.m_run == -INFINITY ? 0.f : st.m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        sacc[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e], zc, -m_use));
+        psum += sacc[e];
+    }
+    st.l_run += psum;
+    // transpose-load roles: this lane supplies row 8*(2*step+i') + 4*kbv + jr, column vb + 4*qc
+    const int grp = lane >> 4, m16 = lane & 15;
+    const int kbv = grp >> 1, vb = 16 * (grp & 1);
+    const int jr = m16 >> 2, qc = m16 & 3;
+    const char* r0 = tb + (4 * kbv + jr) * C::PITCH + (vb + 4 * qc) * 2;
+    u32x4 pb[2];
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+        pb[step][0] = pack_bf16x2(sacc[8 * step + 0], sacc[8 * step + 1]);
+        pb[step][1] = pack_bf16x2(sacc[8 * step + 2], sacc[8 * step + 3]);
+        pb[step][2] = pack_bf16x2(sacc[8 * step + 4], sacc[8 * step + 5]);
+        pb[step][3] = pack_bf16x2(sacc[8 * step + 6], sacc[8 * step + 7]);
+    }
+    // MFMA n = step * VT + v reads rows 16*step + (0 | 8) + ..., columns 32*v + ...
+    auto ld_pair = [&](int n, u32x4& x) {
+        const int step = n / C::VT, v = n % C::VT;
+        const char* p0 = r0 + 16 * step * C::PITCH + 64 * v;
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(p0 + 8 * C::PITCH));
+        const u32x2 y0 = __builtin_bit_cast(u32x2, x0);
+        const u32x2 y1 = __builtin_bit_cast(u32x2, x1);
+        x = u32x4{y0[0], y0[1], y1[0], y1[1]};
+    };
+    constexpr int NPV = 2 * C::VT;
+    u32x4 vw[DVW];
+#pragma unroll
+    for (int j = 0; j < DVW; ++j) ld_pair(j, vw[j]);
+#pragma unroll
+    for (int n = 0; n < NPV; ++n) {
+        const u32x4 va = vw[n % DVW];
+        if (n + DVW < NPV) ld_pair(n + DVW, vw[n % DVW]);
+        st.o[n % C::VT] = mfma32_bf16(va, pb[n / C::VT], st.o[n % C::VT]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return false;
+}
+
+// Epilogue of the wide kernels: one row per head (the normalised value row in
+// bf16, or a split's partial row followed by its fp32 m, l), stored straight from
+// registers.  A lane holds dims 32*v + 8*i + 4*kb + jj (register 4*i + jj) of
+// head `col`; trading half of them with lane ^ 32 leaves lane (col, 0) with dims
+// 32*v + [0, 8) and + [16, 24), lane (col, 1) with + [8, 16) and + [24, 32), so
+// every store is 16 contiguous bytes.
+template <int DQK, int DV, class C>
+__device__ __forceinline__ void mla_write_rows_wide(const MlaArgs& a, const WideState<DQK, DV>& st, size_t row,
+                                                    int rq, int split, int head, bool head_ok, int kb)
+{
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (a.n_split == 1 && a.lse && head_ok && kb == 0)
+        a.lse[row * a.H + head] = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    using P = PartRow<kBF16, DV>;
+    const bool part_out = a.n_split > 1;
+    const size_t hrow = head_ok ? (size_t)head : 0;
+    char* rowp = part_out ? (char*)a.part + (((size_t)rq * a.n_split + split) * a.H + hrow) * P::bytes
+                          : (char*)a.out + (row * a.H + hrow) * (size_t)(DV * 2);
+#pragma unroll
+    for (int v = 0; v < C::VT; ++v) {
+        uint32_t d[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            d[2 * i] = pack_bf16x2(st.o[v][4 * i] * inv, st.o[v][4 * i + 1] * inv);
+            d[2 * i + 1] = pack_bf16x2(st.o[v][4 * i + 2] * inv, st.o[v][4 * i + 3] * inv);
+        }
+#pragma unroll
+        for (int x = 0; x < 8; x += 4)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) {
+                const uint32_t send = kb ? d[x + y] : d[x + y + 2];
+                const uint32_t got = (uint32_t)__shfl_xor((int)send, 32, 64);
+                if (kb)
+                    d[x + y] = got;
+                else
+                    d[x + y + 2] = got;
+            }
+        if (head_ok) {
+            st16(rowp + 2 * (32 * v + 8 * kb), u32x4{d[0], d[1], d[2], d[3]});
+            st16(rowp + 2 * (32 * v + 16 + 8 * kb), u32x4{d[4], d[5], d[6], d[7]});
+        }
+    }
+    if (part_out && head_ok && kb == 0)
+        *reinterpret_cast<f32x4*>(rowp + P::vbytes) = f32x4{st.m_run, l_tot, 0.f, 0.f};
+}
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
+{
+    using C = WideCfg<DQK, DV>;
+    __shared__ __attribute__((aligned(16))) u32x4 tiles[C::NBUF * C::BUF_CH];
+    __shared__ uint32_t lrow[kMaxListLen];
+    __shared__ uint32_t tmask[kMaxListLen / kTileKeys];
+    // restart requests: a wave raising one during tile `it` writes slot it & 1,
+    // which every wave reads after the next barrier (before anyone can write that
+    // slot again, two tiles later)
+    __shared__ int restart_flags[2];
+    volatile int* restart = restart_flags;
+
+    const int HB = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    const int n_units = a.B * a.t_count * a.n_split * HB;
+    const int unit = xcd_unit(blockIdx.x, n_units);
+    if (unit >= n_units) return;
+    const int hb = unit % HB;
+    const int split = (unit / HB) % a.n_split;
+    const int rq = unit / HB / a.n_split;
+    const int b = rq / a.t_count;
+    const int t = a.t_begin + rq % a.t_count;
+    const size_t row = (size_t)b * a.T + t;
+    const int L = min(a.kv_len[b], a.Lmax);
+
+    const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    if (tid < 2) restart[tid] = 0;
+    const int col = lane & 31, kb = lane >> 5;
+    const int head = hb * kHeadsPerBlock + w * 32 + col;
+    const bool head_ok = head < a.H;
+
+    const int per = ((a.K + a.n_split - 1) / a.n_split + kTileKeys - 1) / kTileKeys * kTileKeys;
+    const int j_begin = split * per;
+    const int j_end = min(a.K, j_begin + per);
+    // an empty sequence (L = 0) has no row to gather, not even the stand-in row 0
+    const int n_tiles = (j_end > j_begin && L > 0) ? (j_end - j_begin + kTileKeys - 1) / kTileKeys : 0;
+
+    const char* kvb = (const char*)a.kv + (size_t)b * a.Lmax * C::ROWB;
+    const int32_t* idxr = a.idx + row * a.K;
+    constexpr int kListPer = kMaxListLen / C::NT;
+    const int n_list = n_tiles * kTileKeys;
+    const int j_last = max(j_end - 1, 0);
+    int raw[kListPer];
+#pragma unroll
+    for (int r = 0; r < kListPer; ++r) raw[r] = idxr[min(j_begin + tid + C::NT * r, j_last)];
+    // Q^T operand: lane (col, kb) holds dims [HQ * kb + 8 s, + 8) of head `col` at step s
+    const uint16_t* qsrc = (const uint16_t*)a.q + (row * a.H + (head_ok ? head : 0)) * DQK + C::HQ * kb;
+    u32x4 qb[C::QS];
+#pragma unroll
+    for (int s = 0; s < C::QS; ++s) qb[s] = ld16(qsrc + 8 * s);
+#pragma unroll
+    for (int r = 0; r < kListPer; ++r) {
+        const int j = tid + C::NT * r;
+        const int s = raw[r];
+        const bool ok = j < n_list && j_begin + j < j_end && s >= 0 && s < L;
+        lrow[j] = ok ? (uint32_t)s * C::ROWB : 0u;
+        const uint64_t bits = __ballot(ok);
+        if (lane == 0) {  // j is a multiple of 64 here, so both words lie inside tmask
+            tmask[j / kTileKeys] = (uint32_t)bits;
+            tmask[j / kTileKeys + 1] = (uint32_t)(bits >> 32);
+        }
+    }
+    // the queries have arrived before the first gather is issued (the waits the
+    // compiler places for them cannot see the asm loads and would drain those too)
+#pragma unroll
+    for (int s = 0; s < C::QS; ++s) asm volatile("" : "+v"(qb[s]));
+    barrier_lds();
+
+    WideState<DQK, DV> st;
+#pragma unroll
+    for (int v = 0; v < C::VT; ++v)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st.o[v][e] = 0.f;
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+    const float zc = a.sm_scale * kLog2e;
+
+#pragma unroll 1
+    for (;;) {
+        if (n_tiles > 0) gather_tile_asm<C>(kvb, lrow, 0, w, lane, tiles);
+        if (n_tiles > 1) gather_tile_asm<C>(kvb, lrow, kTileKeys, w, lane, tiles + C::BUF_CH);
+        int cur = 0;
+#pragma unroll 1
+        for (int it = 0; it < n_tiles; ++it) {
+            // tile `it` has landed everywhere and every wave is done with the buffer
+            // it computed two tiles ago, which the gather below refills
+            if (it + 1 < n_tiles)
+                barrier_vm<C::DMA>();
+            else
+                barrier_vm<0>();
+            if (it > 0 && restart[(it - 1) & 1]) break;  // read after the barrier: the same for every wave
+            const uint32_t vm = tmask[it];
+            const int nxt = cur == 0 ? 2 : cur - 1;  // (cur + 2) % 3
+            PendingGather<C> pg;
+            pg.kvb = kvb;
+            pg.dst = tiles + nxt * C::BUF_CH;
+            pg.lrow = lrow + min(it + 2, n_tiles - 1) * kTileKeys;
+            pg.active = it + 2 < n_tiles;
+            pg.start(w, lane);
+            if (tile_compute_wide<DQK, DV>(tiles + cur * C::BUF_CH, vm, qb, st, zc, lane, w, pg) && lane == 0)
+                restart[it & 1] = 1;
+            cur = cur == 2 ? 0 : cur + 1;
+        }
+        barrier_vm<0>();  // no gather in flight, every flag write visible
+        if (!(restart[0] | restart[1])) break;
+        // a reference was raised: start the unit over (the references are kept)
+        barrier_lds();
+        if (tid < 2) restart[tid] = 0;
+#pragma unroll
+        for (int v = 0; v < C::VT; ++v)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st.o[v][e] = 0.f;
+        st.l_run = 0.f;
+    }
+    mla_write_rows_wide<DQK, DV, C>(a, st, row, rq, split, head, head_ok, kb);
+}
+
+// ================================================================ wide fp8 kernel
+// The wide kernel on the fp8 latent cache: a row is 576 e4m3 codes and its
+// scale chunk (592 bytes), q arrives as codes with one scale per (query, head).
+// Per 32-key tile a wave reads half the LDS bytes of the bf16 kernel: q.k runs on
+// the 32x32x64 f8f6f4 MFMA (two 16-byte reads per 64-deep step), and the value
+// operand comes from one 8-bit transpose read per MFMA, converted to bf16 by
+// v_cvt_scalef32_pk_bf16_fp8 (scale 1: exact, e4m3 has three mantissa bits).
+template <int DQK, int DV>
+struct Fp8WideCfg {
+    static constexpr int NT = 256;
+    static constexpr int NW = NT / 64;
+    static constexpr int ROWB = DQK + 16;          // codes + scale chunk
+    static constexpr int CPR = ROWB / 16;
+    static constexpr int PCH = CPR;                // odd pitch in chunks
+    static constexpr int PITCH = PCH * 16;
+    static constexpr int TILE_CH = kTileKeys * PCH;
+    static constexpr int DMA = (TILE_CH + NT - 1) / NT;
+    static constexpr int BUF_CH = DMA * NT;
+    static constexpr int NBUF = 4;                 // three gathers in flight; room to stage 64 output rows
+    static constexpr int QS = DQK / 64;            // 32x32x64 steps
+    static constexpr int VT = DV / 32;
+    static constexpr int V_AHEAD = 4;              // value reads in flight ahead of the value MFMAs
+    static_assert(DQK % 64 == 0 && DV % 32 == 0 && DV <= DQK && CPR % 2 == 1, "shape");
+};
+
+// f8f6f4 32x32x64 MFMA (both operands e4m3, unit block scales in `one` = 127)
+// accumulating in VGPRs, as asm for the same reason as the bf16 logits.
+__device__ __forceinline__ void mfma32_fp8_vfirst(const i32x8& a, const i32x8& b, int one, f32x16& acc)
+{
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
+                 : "=&v"(acc) : "v"(a), "v"(b), "v"(one));
+}
+__device__ __forceinline__ void mfma32_fp8_vacc(const i32x8& a, const i32x8& b, int one, f32x16& acc)
+{
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                 : "+v"(acc) : "v"(a), "v"(b), "v"(one));
+}
+// 24 wait states: more than the 16-pass f8f6f4 MFMA's result needs.
+__device__ __forceinline__ void wait_mfma16_acc(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x)); }
+
+template <int DQK, int DV>
+__device__ __forceinline__ bool tile_compute_fp8w(const u32x4* tile, uint32_t vmask,
+                                                  const i32x8 (&qb)[Fp8WideCfg<DQK, DV>::QS], WideState<DQK, DV>& st,
+                                                  float zch, int lane, int w, float* kscol,
+                                                  PendingGather<Fp8WideCfg<DQK, DV>>& pg)
+{
+    using C = Fp8WideCfg<DQK, DV>;
+    asm volatile("" : "+v"(lane));
+    const int col = lane & 31, kb = lane >> 5;
+    const char* tb = reinterpret_cast<const char*>(tile);
+    // key scales: lane l reads key l % 32's scale into this wave's column, then
+    // takes keys 8*i + 4*kb .. + 3 with one 16-byte read per i
+    const float ksl = *reinterpret_cast<const float*>(tb + col * C::PITCH + DQK);
+    if (kb == 0) kscol[col] = ksl;
+    f32x16 sacc;
+    const int one = 127;
+    const char* kr = tb + col * C::PITCH + 32 * kb;
+    {
+        constexpr int GAP = (C::QS * 2) / C::DMA;  // half-steps between gather loads
+        static_assert(GAP >= 2, "gather spacing");
+        uint32_t goff = 0;
+        i32x8 kw[2];
+        auto ldk = [&](int s) {
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(kr + 64 * s);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(kr + 64 * s + 16);
+            return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        };
+        kw[0] = ldk(0);
+        kw[1] = ldk(1);
+#pragma unroll
+        for (int s = 0; s < C::QS; ++s) {
+            const i32x8 ka = kw[s & 1];
+            if (s + 2 < C::QS) kw[s & 1] = ldk(s + 2);
+            if (s == 0)
+                mfma32_fp8_vfirst(ka, qb[0], one, sacc);
+            else
+                mfma32_fp8_vacc(ka, qb[s], one, sacc);
+            // the pending gather: load k's row offset is read at half-step GAP * k
+            // and the load issued at half-step GAP * k + GAP - 1
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int hs = 2 * s + h;
+                if (hs % GAP == 0 && hs / GAP < C::DMA) goff = pg.next_offset();
+                if (hs % GAP == GAP - 1 && hs / GAP < C::DMA && pg.active)
+                    gather_issue<C>(pg.kvb, goff, pg.dst, w, hs / GAP);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_mfma16_acc(sacc);
+    float ks[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(kscol + 8 * i + 4 * kb);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ks[4 * i + j] = k4[j];
+    }
+    // lane holds keys 8*i + 4*kb + j (register 4*i + j) of head `col`
+    float tmax = -INFINITY;
+    if (vmask == 0xFFFFFFFFu) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            sacc[e] *= ks[e];
+            tmax = fmaxf(tmax, sacc[e]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int key = 8 * (e >> 2) + 4 * kb + (e & 3);
+            sacc[e] = ((vmask >> key) & 1u) ? sacc[e] * ks[e] : -INFINITY;
+            tmax = fmaxf(tmax, sacc[e]);
+        }
+    }
+    {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1])) * zch;
+    }
+    if (__ballot(tmax > st.m_run + kWideSlack)) {
+        const bool over = __ballot(st.m_run != -INFINITY && tmax > st.m_run + kWideSlack) != 0;
+        if (tmax > st.m_run + kWideSlack) st.m_run = tmax;
+        if (over) return true;
+    }
+    const float m_use = st.m_run == -INFINITY ? 0.f : st.m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        sacc[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e], zch, -m_use));
+        psum += sacc[e];
+    }
+    st.l_run += psum;
+    // value weights carry the key scale: P'[key, head] = p * k_scale[key]
+    u32x4 pb[2];
+#pragma unroll
+    for (int step = 0; step < 2; ++step)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            pb[step][t] = pack_bf16x2(sacc[8 * step + 2 * t] * ks[8 * step + 2 * t],
+                                      sacc[8 * step + 2 * t + 1] * ks[8 * step + 2 * t + 1]);
+    // transpose-load roles: this lane supplies, for element j = (lane % 16) / 2 of
+    // its 16-lane group, the row of key(j) and the column half (lane & 1)
+    const int li = lane & 15, gh = (lane >> 4) & 1;
+    const int jj = li >> 1;
+    const int krow = (jj < 4 ? 4 * kb + jj : 8 + 4 * kb + (jj - 4));
+    const char* vsrc = tb + krow * C::PITCH + 16 * gh + 8 * (li & 1);
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    constexpr int NPV = 2 * C::VT;
+    constexpr int DVW = C::V_AHEAD;
+    auto ldv = [&](int n) {
+        const int step = n / C::VT, v = n % C::VT;
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(vsrc + 16 * step * C::PITCH + 32 * v));
+    };
+    v2i vw[DVW];
+#pragma unroll
+    for (int j = 0; j < DVW; ++j) vw[j] = ldv(j);
+#pragma unroll
+    for (int n = 0; n < NPV; ++n) {
+        const v2i raw = vw[n % DVW];
+        if (n + DVW < NPV) vw[n % DVW] = ldv(n + DVW);
+        const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)raw[0], 1.f, false);
+        const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)raw[0], 1.f, true);
+        const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)raw[1], 1.f, false);
+        const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)raw[1], 1.f, true);
+        const u32x4 va = {__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
+                          __builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, a3)};
+        st.o[n % C::VT] = mfma32_bf16(va, pb[n / C::VT], st.o[n % C::VT]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return false;
+}
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256) void mla_fp8w_kernel(MlaArgs a)
+{
+    using C = Fp8WideCfg<DQK, DV>;
+    __shared__ __attribute__((aligned(16))) u32x4 tiles[C::NBUF * C::BUF_CH];
+    __shared__ uint32_t lrow[kMaxListLen];
+    __shared__ uint32_t tmask[kMaxListLen / kTileKeys];
+    __shared__ __attribute__((aligned(16))) float kscols[C::NW][kTileKeys];
+    __shared__ int restart_flags[2];
+    volatile int* restart = restart_flags;
+
+    const int HB = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    const int n_units = a.B * a.t_count * a.n_split * HB;
+    const int unit = xcd_unit(blockIdx.x, n_units);
+    if (unit >= n_units) return;
+    const int hb = unit % HB;
+    const int split = (unit / HB) % a.n_split;
+    const int rq = unit / HB / a.n_split;
+    const int b = rq / a.t_count;
+    const int t = a.t_begin + rq % a.t_count;
+    const size_t row = (size_t)b * a.T + t;
+    const int L = min(a.kv_len[b], a.Lmax);
+
+    const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+    if (tid < 2) restart[tid] = 0;
+    const int col = lane & 31, kb = lane >> 5;
+    const int head = hb * kHeadsPerBlock + w * 32 + col;
+    const bool head_ok = head < a.H;
+
+    const int per = ((a.K + a.n_split - 1) / a.n_split + kTileKeys - 1) / kTileKeys * kTileKeys;
+    const int j_begin = split * per;
+    const int j_end = min(a.K, j_begin + per);
+    const int n_tiles = (j_end > j_begin && L > 0) ? (j_end - j_begin + kTileKeys - 1) / kTileKeys : 0;
+
+    const char* kvb = (const char*)a.kv + (size_t)b * a.Lmax * C::ROWB;
+    const int32_t* idxr = a.idx + row * a.K;
+    constexpr int kListPer = kMaxListLen / C::NT;
+    const int n_list = n_tiles * kTileKeys;
+    const int j_last = max(j_end - 1, 0);
+    int raw[kListPer];
+#pragma unroll
+    for (int r = 0; r < kListPer; ++r) raw[r] = idxr[min(j_begin + tid + C::NT * r, j_last)];
+    // Q^T operand: lane (col, kb) holds the codes of dims [64 s + 32 kb, + 32) of head `col`
+    const size_t qrow = row * a.H + (head_ok ? head : 0);
+    i32x8 qb[C::QS];
+    {
+        const char* src = (const char*)a.q + qrow * DQK + 32 * kb;
+#pragma unroll
+        for (int s = 0; s < C::QS; ++s) {
+            const u32x4 lo = ld16(src + 64 * s), hi = ld16(src + 64 * s + 16);
+            qb[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+    }
+    const float zch = a.sm_scale * kLog2e * a.q_scale[qrow];
+#pragma unroll
+    for (int r = 0; r < kListPer; ++r) {
+        const int j = tid + C::NT * r;
+        const int s = raw[r];
+        const bool ok = j < n_list && j_begin + j < j_end && s >= 0 && s < L;
+        lrow[j] = ok ? (uint32_t)s * C::ROWB : 0u;
+        const uint64_t bits = __ballot(ok);
+        if (lane == 0) {
+            tmask[j / kTileKeys] = (uint32_t)bits;
+            tmask[j / kTileKeys + 1] = (uint32_t)(bits >> 32);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < C::QS; ++s) asm volatile("" : "+v"(qb[s]));
+    barrier_lds();
+
+    WideState<DQK, DV> st;
+#pragma unroll
+    for (int v = 0; v < C::VT; ++v)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st.o[v][e] = 0.f;
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+    constexpr int AHEAD = C::NBUF - 1;
+
+#pragma unroll 1
+    for (;;) {
+#pragma unroll
+        for (int g = 0; g < AHEAD; ++g)
+            if (g < n_tiles) gather_tile_asm<C>(kvb, lrow, g * kTileKeys, w, lane, tiles + g * C::BUF_CH);
+        int cur = 0;
+#pragma unroll 1
+        for (int it = 0; it < n_tiles; ++it) {
+            // tile `it` has landed everywhere (the gathers of the next min(AHEAD - 1,
+            // n_tiles - 1 - it) tiles may still be in flight) and every wave is done
+            // with the buffer computed in the previous iteration, refilled below
+            const int later = min(AHEAD - 1, n_tiles - 1 - it);
+            if (later >= 2)
+                barrier_vm<2 * C::DMA>();
+            else if (later == 1)
+                barrier_vm<C::DMA>();
+            else
+                barrier_vm<0>();
+            if (it > 0 && restart[(it - 1) & 1]) break;
+            const uint32_t vm = tmask[it];
+            const int nxt = cur == 0 ? C::NBUF - 1 : cur - 1;  // (cur + AHEAD) % NBUF
+            PendingGather<C> pg;
+            pg.kvb = kvb;
+            pg.dst = tiles + nxt * C::BUF_CH;
+            pg.lrow = lrow + min(it + AHEAD, n_tiles - 1) * kTileKeys;
+            pg.active = it + AHEAD < n_tiles;
+            pg.start(w, lane);
+            if (tile_compute_fp8w<DQK, DV>(tiles + cur * C::BUF_CH, vm, qb, st, zch, lane, w, kscols[w], pg) &&
+                lane == 0)
+                restart[it & 1] = 1;
+            cur = cur == C::NBUF - 1 ? 0 : cur + 1;
+        }
+        barrier_vm<0>();
+        if (!(restart[0] | restart[1])) break;
+        barrier_lds();
+        if (tid < 2) restart[tid] = 0;
+#pragma unroll
+        for (int v = 0; v < C::VT; ++v)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st.o[v][e] = 0.f;
+        st.l_run = 0.f;
+    }
+    mla_write_rows_wide<DQK, DV, C>(a, st, row, rq, split, head, head_ok, kb);
+}
+
 // ================================================================ fp8 kernel
 // The bf16 kernel's structure on e4m3 operands: the latent cache rows and the
 // queries as codes with one fp32 scale per row.  A cache row is DQK codes and
@@ -868,11 +1589,35 @@ hipError_t launch_bf16(const MlaArgs& a, hipStream_t s)
 }
 
 template <int DQK, int DV>
+hipError_t launch_wide(const MlaArgs& a, hipStream_t s)
+{
+    const int HB = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    const long long units = (long long)a.B * a.t_count * a.n_split * HB;
+    mla_wide_kernel<DQK, DV><<<dim3((unsigned)(8 * ((units + 7) / 8))), 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_combine<kBF16, DV>(a, s);
+}
+
+// Tiles of one split's index list.  The wide kernels win on long lists; on the
+// short lists of split decode their one-wave-per-SIMD prologue (twice the q
+// loads per wave) costs more than they save.
+int split_tiles(const MlaArgs& a)
+{
+    const int per = (a.K + a.n_split - 1) / a.n_split;
+    return (per + kTileKeys - 1) / kTileKeys;
+}
+constexpr int kWideMinTiles = 8;
+
+template <int DQK, int DV>
 hipError_t launch_fp8(const MlaArgs& a, hipStream_t s)
 {
     const int HB = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
     const long long units = (long long)a.B * a.t_count * a.n_split * HB;
-    mla_fp8_kernel<DQK, DV><<<dim3((unsigned)(8 * ((units + 7) / 8))), 512, 0, s>>>(a);
+    const dim3 grid((unsigned)(8 * ((units + 7) / 8)));
+    if (split_tiles(a) >= kWideMinTiles)
+        mla_fp8w_kernel<DQK, DV><<<grid, 256, 0, s>>>(a);
+    else
+        mla_fp8_kernel<DQK, DV><<<grid, 512, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : launch_combine<kBF16, DV>(a, s);
 }
@@ -921,6 +1666,7 @@ hipError_t launch_mla(int dtype, const MlaArgs& a, hipStream_t s)
     if (dtype == kF32) return launch_f32<80, 64>(a, s);
     if (dtype == kFP8) return launch_fp8<576, 512>(a, s);
     if (a.Dqk == 192) return launch_bf16<192, 128>(a, s);
+    if (split_tiles(a) >= kWideMinTiles) return launch_wide<576, 512>(a, s);
     return launch_bf16<576, 512>(a, s);
 }
 

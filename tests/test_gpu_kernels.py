@@ -232,6 +232,14 @@ MLA_CASES = [
     (3, 2, 128, 576, 512, 64, [64, 2, 1], 32, "bf16", "topk"),
     # rows past kv_len hold NaN (one sequence is empty): they must never be read
     (3, 2, 128, 576, 512, 80, [80, 0, 1], 32, "bf16", "poison"),
+    # lists of eight or more tiles per split take the one-wave-per-SIMD kernel:
+    # two splits + combine; one split with lse; a partial second head block;
+    # duplicates and skipped entries
+    (1, 128, 128, 576, 512, 1024, [1024], 512, "bf16", "topk"),
+    (1, 300, 128, 576, 512, 2048, [2048], 384, "bf16", "topk"),
+    (1, 256, 200, 576, 512, 600, [600], 320, "bf16", "topk"),
+    (1, 256, 128, 576, 512, 900, [900], 288, "bf16", "messy"),
+    (2, 64, 128, 576, 512, 700, [700, 0], 512, "bf16", "poison"),
 ]
 
 
@@ -307,6 +315,10 @@ MLA_FP8_CASES = [
     (2, 3, 20, 300, [300, 150], 96, "topk"),                     # a partial head block
     (1, 2, 200, 128, [128], 64, "topk"),                         # two head blocks
     (3, 2, 128, 80, [80, 0, 1], 32, "poison"),                   # rows past kv_len are NaN bytes
+    # eight or more tiles per split: the one-wave-per-SIMD fp8 kernel
+    (1, 128, 128, 1024, [1024], 512, "topk"),                    # two splits + combine
+    (1, 256, 200, 600, [600], 320, "messy"),                     # one split, partial head block
+    (2, 64, 128, 700, [700, 0], 512, "poison"),
 ]
 
 
@@ -341,3 +353,43 @@ def test_sparse_mla_fp8_against_oracle(dsa, orc, case):
     err = rel_rowmax(out[live], ro[live])
     assert err.max() < TOL["bf16"], err.max()
     assert np.abs(lse[live] - rl[live]).max() < TOL["bf16"] * max(1.0, np.abs(rl[live]).max())
+
+
+@pytest.mark.parametrize("T", [1, 256])
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_sparse_mla_large_logit_jumps(dsa, orc, dt, T):
+    """Later tiles whose logits exceed every earlier one by far more than the
+    kernels' softmax reference slack (2^64 and 2^8 in log2 units): the result must
+    still be the oracle's.  Queries are all ones; the listed rows are small random
+    values except three rows, in tiles 2, 5 and 9 of the first query's list, whose
+    logits are about 100, 200 and 300 (natural log units) above the rest.  T = 1
+    splits each list in three (short-list kernels), T = 256 keeps whole 12-tile
+    lists (one-wave-per-SIMD kernels, whose restart path this takes)."""
+    g = torch.Generator().manual_seed(31)
+    B, H, L, K, D, Dv = 2, 128, 512, 384, 576, 512
+    q = torch.ones(B, T, H, D)
+    q[:, :, 1::2] *= 0.5                       # two groups of heads with different logit scales
+    kv = torch.randn(B, L, D, generator=g) * 0.05
+    idx = torch.stack([torch.randperm(L, generator=g)[:K] for _ in range(B * T)]).int().reshape(B, T, K)
+    sm = 1.0 / 24.0
+    for b in range(B):
+        for tile, c in ((2, 100.0), (5, 200.0), (9, 300.0)):
+            r = int(idx[b, 0, 32 * tile + 7])
+            kv[b, r] = c / (sm * D) + 0.02 * torch.randn(D, generator=g)
+    q, kv = q.to(torch.bfloat16), kv.to(torch.bfloat16)
+    kl = torch.full((B,), L, dtype=torch.int32)
+    s = shape_of(dsa, batch=B, n_q=T, max_kv=L, heads=H, topk=K, sm_scale=sm, mla_dtype=dt)
+    announce(f"sparse_mla large logit jumps {dt}")
+    if dt == "fp8":
+        out, lse = dsa.sparse_mla_fwd(s, q.to(DEV), dsa.mla_kv_quant_fp8(kv.to(DEV)), idx.to(DEV), kl.to(DEV))
+        qc, qs = orc.quant(q)
+        kc, ks = orc.quant(kv)
+        ro, rl = orc.sparse_mla_fp8(qc, qs, kc, ks, idx.reshape(B * T, K), sm, v_dim=Dv)
+    else:
+        out, lse = dsa.sparse_mla_fwd(s, q.to(DEV), kv.to(DEV), idx.to(DEV), kl.to(DEV))
+        ro, rl = orc.sparse_mla(q, kv, idx.reshape(B * T, K), sm, v_dim=Dv)
+    out = out.float().cpu().numpy().reshape(B * T, H, Dv)
+    lse = lse.cpu().numpy().reshape(B * T, H)
+    err = rel_rowmax(out, ro)
+    assert err.max() < TOL["bf16"], err.max()
+    assert np.abs(lse - rl).max() < TOL["bf16"] * np.abs(rl).max()

@@ -95,7 +95,7 @@ def dominant(wl, stage_us: dict) -> tuple[str, dict]:
 
 
 def stage_kernel(wl, stage: str) -> str:
-    return STAGE_KERNELS["mla_fp8" if stage == "mla" and wl.mla_dtype == "fp8" else stage]
+    return mla_kernels(wl) if stage == "mla" else STAGE_KERNELS[stage]
 
 
 def stage_fractions(wl, stage_us: dict) -> dict:
@@ -192,9 +192,23 @@ def time_forward(dsa, torch, cases, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
-STAGE_KERNELS = {"indexer": "indexer", "topk": "topk (zero, hist, filter, finish) or topk_kernel",
-                 "mla": "mla_bf16_kernel + mla_combine_kernel", "mla_fp8": "quant_rows_kernel (q) + mla_fp8_kernel + "
-                 "mla_combine_kernel"}
+STAGE_KERNELS = {"indexer": "indexer", "topk": "topk (zero, hist, filter, finish) or topk_kernel"}
+
+
+def mla_kernels(wl) -> str:
+    """The kernels dsa_sparse_mla_fwd launches for this shape: the library splits the index
+    list until about 256 workgroups exist (at most K/128 and 16 splits) and takes the
+    one-wave-per-SIMD kernels when a split's list has 8 or more 32-key tiles."""
+    units = wl.batch * wl.n_q * ((wl.heads + 127) // 128)
+    ns = max(1, min(-(-256 // units), max(wl.topk // 128, 1), 16))
+    wide = -(-(-(-wl.topk // ns)) // 32) >= 8
+    if wl.mla_dtype == "fp8":
+        name = "quant_rows_kernel (q) + " + ("mla_fp8w_kernel" if wide else "mla_fp8_kernel")
+    elif wl.mla_dtype == "f32":
+        name = "mla_f32_kernel"
+    else:
+        name = "mla_wide_kernel" if wide and wl.qk_dim == 576 else "mla_bf16_kernel"
+    return name + (" + mla_combine_kernel" if ns > 1 else "")
 
 
 def time_stages(dsa, torch, cases, reps):

@@ -64,8 +64,10 @@ def _load():
             lib.orc_topk.argtypes = [I, I, I, I, P, L, P, P, P]
             lib.orc_sparse_mla.argtypes = [I, I, I, I, I, I, I, D, P, P, L, P, I, P, P, P]
             lib.orc_masked_dense_mla.argtypes = [I, I, I, I, I, I, I, D, P, P, P, L, P, I, P, P, P]
+            lib.orc_sparse_mla_bwd.argtypes = [I, I, I, I, I, I, I, D, P, P, P, L, P, I, P, P, P]
             for f in ("orc_hadamard_matrix", "orc_rotate", "orc_rotate_quant", "orc_quant", "orc_index_scores",
-                      "orc_index_scores_fp8", "orc_topk", "orc_sparse_mla", "orc_masked_dense_mla"):
+                      "orc_index_scores_fp8", "orc_topk", "orc_sparse_mla", "orc_masked_dense_mla",
+                      "orc_sparse_mla_bwd"):
                 getattr(lib, f).restype = None
             _lib = lib
     return _lib
@@ -298,6 +300,42 @@ def sparse_mla(q, kv, idx, sm_scale: float, rows=None, v_dim: int | None = None,
     _load().orc_sparse_mla(B, T, Lmax, H, Dqk, Dv, K, float(sm_scale), _p(q), _p(kv), len(r), _p(r),
                            int(compact), _p(ix), _p(out), _p(lse))
     return out, lse
+
+
+def sparse_mla_bwd(q, kv, dout, idx, sm_scale: float, rows=None, v_dim: int | None = None, T=None):
+    """Gradients of L = sum(dout * out) for the attention of ``sparse_mla``:
+    q [B,T,H,Dqk], kv [B,Lmax,Dqk], dout [B,T,H,Dv], idx [n_rows,K] (entries < 0
+    skipped, an index listed twice counts twice) -> (dq [n_rows,H,Dqk] f64,
+    dkv [B,Lmax,Dqk] f64, summed over the listed rows).  With ``T`` given, q and
+    dout hold only the listed rows ([n_rows,H,·]).
+
+    The page calls DSA trainable (DeepSeek-V3.2 model documentation, model
+    description); these are the chain-rule gradients of the softmax attention
+    over the selected set: dP_j = dO.v_j, D = dO.O, dz_j = p_j (dP_j - D),
+    dq = sm sum_j dz_j k_j, dkv[idx_j] += sm dz_j q, and += p_j dO on the value
+    columns.
+    """
+    q = _f32(q)
+    kv = _f32(kv)
+    do = _f32(dout)
+    ix = _i32(idx)
+    compact = T is not None
+    B = kv.shape[0]
+    if compact:
+        _, H, Dqk = q.shape
+    else:
+        _, T, H, Dqk = q.shape
+    Lmax = kv.shape[1]
+    Dv = Dqk if v_dim is None else v_dim
+    assert do.shape[-1] == Dv and do.shape[-2] == H
+    r = _rows(rows, B * T)
+    K = ix.shape[-1]
+    ix = ix.reshape(len(r), K)
+    dq = np.empty((len(r), H, Dqk), dtype=np.float64)
+    dkv = np.zeros((B, Lmax, Dqk), dtype=np.float64)
+    _load().orc_sparse_mla_bwd(B, T, Lmax, H, Dqk, Dv, K, float(sm_scale), _p(q), _p(kv), _p(do), len(r), _p(r),
+                               int(compact), _p(ix), _p(dq), _p(dkv))
+    return dq, dkv
 
 
 def masked_dense_mla(q, kv, kv_len, idx, sm_scale: float, rows=None, v_dim: int | None = None):

@@ -393,6 +393,103 @@ void orc_sparse_mla(int B, int T, int Lmax, int H, int Dqk, int Dv, int K, doubl
     }
 }
 
+/* Backward of the sparse MLA.  The page calls DSA trainable; for the loss
+ * L = sum over the listed rows, heads and value dims of dO * O it returns the
+ * gradients with respect to q and kv.  With z_j = sm q . k_j over the listed
+ * entries j (k_j = row idx_j, v_j its first Dv columns), p = softmax(z) and
+ * O = sum_j p_j v_j:
+ *   dP_j = dO . v_j,   D = dO . O,   dz_j = p_j (dP_j - D),
+ *   dq   = sm sum_j dz_j k_j,
+ *   dkv[idx_j] += sm dz_j q  (all Dqk columns)  +  p_j dO  (first Dv columns);
+ * an index listed twice contributes twice.  dq [n_rows, H, Dqk]; dkv
+ * [B, Lmax, Dqk] is accumulated into (the caller zeroes it). */
+void orc_sparse_mla_bwd(int B, int T, int Lmax, int H, int Dqk, int Dv, int K, double sm,
+                        const float* q, const float* kv, const float* dout, long n_rows, const long* rows,
+                        int compact, const int* idx, double* dq, double* dkv)
+{
+    (void)B;
+#pragma omp parallel
+    {
+        double* z = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        double* pr = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        double* o = (double*)malloc(sizeof(double) * (size_t)Dv);
+        double* g = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1) * Dqk);
+#pragma omp for schedule(dynamic, 1)
+        for (long i = 0; i < n_rows; ++i) {
+            long r = row_at(i, rows);
+            long b = r / T;
+            const int* ir = idx + (size_t)i * K;
+            const float* kvb = kv + (size_t)b * Lmax * Dqk;
+            for (size_t u = 0; u < (size_t)K * Dqk; ++u)
+                g[u] = 0.0;
+            for (int h = 0; h < H; ++h) {
+                const size_t qi = (size_t)(compact ? i : r) * H + h;
+                const float* qh = q + qi * Dqk;
+                const float* doh = dout + qi * Dv;
+                double* dqh = dq + ((size_t)i * H + h) * Dqk;
+                for (int d = 0; d < Dqk; ++d)
+                    dqh[d] = 0.0;
+                double m = -INFINITY;
+                for (int j = 0; j < K; ++j) {
+                    if (ir[j] < 0) continue;
+                    const float* row = kvb + (size_t)ir[j] * Dqk;
+                    double dot = 0.0;
+                    for (int d = 0; d < Dqk; ++d)
+                        dot += (double)qh[d] * (double)row[d];
+                    z[j] = sm * dot;
+                    if (z[j] > m) m = z[j];
+                }
+                if (m == -INFINITY) continue;
+                double Z = 0.0;
+                for (int j = 0; j < K; ++j) {
+                    if (ir[j] < 0) continue;
+                    pr[j] = exp(z[j] - m);
+                    Z += pr[j];
+                }
+                for (int e = 0; e < Dv; ++e)
+                    o[e] = 0.0;
+                for (int j = 0; j < K; ++j) {
+                    if (ir[j] < 0) continue;
+                    pr[j] /= Z;
+                    const float* row = kvb + (size_t)ir[j] * Dqk;
+                    for (int e = 0; e < Dv; ++e)
+                        o[e] += pr[j] * (double)row[e];
+                }
+                double Dsum = 0.0;
+                for (int e = 0; e < Dv; ++e)
+                    Dsum += (double)doh[e] * o[e];
+                for (int j = 0; j < K; ++j) {
+                    if (ir[j] < 0) continue;
+                    const float* row = kvb + (size_t)ir[j] * Dqk;
+                    double dp = 0.0;
+                    for (int e = 0; e < Dv; ++e)
+                        dp += (double)doh[e] * (double)row[e];
+                    const double dz = pr[j] * (dp - Dsum);
+                    double* gj = g + (size_t)j * Dqk;
+                    for (int d = 0; d < Dqk; ++d) {
+                        dqh[d] += sm * dz * (double)row[d];
+                        gj[d] += sm * dz * (double)qh[d];
+                    }
+                    for (int e = 0; e < Dv; ++e)
+                        gj[e] += pr[j] * (double)doh[e];
+                }
+            }
+#pragma omp critical
+            for (int j = 0; j < K; ++j) {
+                if (ir[j] < 0) continue;
+                double* dst = dkv + ((size_t)b * Lmax + ir[j]) * Dqk;
+                const double* gj = g + (size_t)j * Dqk;
+                for (int d = 0; d < Dqk; ++d)
+                    dst[d] += gj[d];
+            }
+        }
+        free(z);
+        free(pr);
+        free(o);
+        free(g);
+    }
+}
+
 /* Second formulation (the additive-mask form): dense logits over every
  * s = 0..p, plus a mask that is 0 on the selected s and -inf elsewhere,
  * then a softmax over all of them.  Must agree with orc_sparse_mla. */

@@ -180,6 +180,42 @@ dsa_status dsa_index_cache_append_fp8(int32_t batch, int32_t t_new, int32_t max_
 dsa_status dsa_mla_kv_quant_fp8(int64_t rows, int32_t dim, const void* x, int32_t x_dtype,
                                 uint8_t* kv_rows, hipStream_t stream);
 
+/* Backward of the sparse MLA (the page calls DSA trainable): for the forward of
+ * dsa_sparse_mla_fwd and the gradient dout of its output,
+ *   p_j = exp(z_j - lse),  dP_j = dout . v_j,  D = dout . out = sum_j p_j dP_j,
+ *   dz_j = p_j (dP_j - D),  dq = sm_scale sum_j dz_j k_j,
+ *   dkv[idx_j] += sm_scale dz_j q  (all D_qk columns)  +  p_j dout  (first D_v columns);
+ * an index listed twice contributes twice; skipped entries contribute nothing.
+ * D is summed from the recomputed p and dP (not read from the rounded output, whose
+ * error would dominate dz where the softmax is concentrated), so the forward
+ * output itself is not an argument.
+ *   mla_dtype BF16 only, (qk_dim, v_dim) in {(576, 512), (192, 128)}, heads 1..128.
+ *   q, kv, idx, kv_len as for dsa_sparse_mla_fwd; lse [B,T,H] f32 is that call's
+ *   log-sum-exp for the same inputs; dout [B,T,H,D_v] BF16.
+ *   dq  [B,T,H,D_qk] f32 out (every row written).
+ *   dkv [B,L_max,D_qk] f32: cleared first unless accumulate_dkv != 0, in which
+ *       case the gradients are added to what it holds (fp32 atomics: the order of
+ *       the additions, and so the last bits, vary from run to run).
+ *   workspace (256-byte aligned): dsa_sparse_mla_bwd_workspace_size(shape) bytes
+ *   run every query in one pass; any size >= dsa_sparse_mla_bwd_min_workspace_size
+ *   works, the queries then being processed in the largest chunk of ceil(T / 2^k)
+ *   queries whose buffers fit (per query about K * round_up(H, 16) * 8 bytes of
+ *   p and dP plus the transposed q and dout); both size calls return 0 for a shape
+ *   this call rejects.
+ * Errors: sizes as dsa_sparse_mla_fwd checks them -> DSA_ERR_SHAPE; mla_dtype not
+ * BF16 -> DSA_ERR_DTYPE; other (qk_dim, v_dim) or heads -> DSA_ERR_UNSUPPORTED; NULL
+ * pointers -> DSA_ERR_NULL; q, kv, dout, dq or dkv not 16-byte aligned, idx, kv_len
+ * or lse not 4-byte aligned, workspace not 256-byte aligned -> DSA_ERR_ALIGN;
+ * workspace NULL or below the minimum -> DSA_ERR_WORKSPACE; a failed launch ->
+ * DSA_ERR_HIP. */
+size_t dsa_sparse_mla_bwd_workspace_size(const dsa_shape* shape);
+size_t dsa_sparse_mla_bwd_min_workspace_size(const dsa_shape* shape);
+dsa_status dsa_sparse_mla_bwd(const dsa_shape* shape, const void* q, const void* kv,
+                              const int32_t* idx, const int32_t* kv_len,
+                              const float* lse, const void* dout, float* dq, float* dkv,
+                              int32_t accumulate_dkv, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
 /* The whole path: (fp8 only) rotate + quantise q_idx, index scores, top-k,
  * (fp8 MLA only) quantise q, sparse MLA.
  *   q_idx  [B,T,H_I,D_I]: idx_dtype for F32/BF16; for FP8 it is the unrotated

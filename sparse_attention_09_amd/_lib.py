@@ -24,7 +24,8 @@ STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_DTY
 
 EXPORTS = ["dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_workspace_size",
            "dsa_sparse_mla_fwd", "dsa_rotate_quant_fp8", "dsa_index_cache_append_fp8", "dsa_forward_workspace_size",
-           "dsa_mla_kv_quant_fp8", "dsa_forward_min_workspace_size", "dsa_forward", "dsa_status_string"]
+           "dsa_mla_kv_quant_fp8", "dsa_forward_min_workspace_size", "dsa_forward", "dsa_status_string",
+           "dsa_sparse_mla_bwd_workspace_size", "dsa_sparse_mla_bwd_min_workspace_size", "dsa_sparse_mla_bwd"]
 
 
 class DsaError(RuntimeError):
@@ -86,6 +87,9 @@ def lib() -> ctypes.CDLL:
             "dsa_rotate_quant_fp8": ([I64, I32, P, I32, P, P, P], I32),
             "dsa_index_cache_append_fp8": ([I32, I32, I32, I32, P, I32, P, P, P, P], I32),
             "dsa_mla_kv_quant_fp8": ([I64, I32, P, I32, P, P], I32),
+            "dsa_sparse_mla_bwd_workspace_size": ([SP], SZ),
+            "dsa_sparse_mla_bwd_min_workspace_size": ([SP], SZ),
+            "dsa_sparse_mla_bwd": ([SP, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
             "dsa_forward_workspace_size": ([SP], SZ),
             "dsa_forward_min_workspace_size": ([SP], SZ),
             "dsa_forward": ([SP, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
@@ -230,6 +234,32 @@ def mla_kv_quant_fp8(x, kv_rows=None, stream=None):
     _check("dsa_mla_kv_quant_fp8", lib().dsa_mla_kv_quant_fp8(rows, dim, _ptr(x), xt, _ptr(kv_rows),
                                                                _stream(stream)))
     return kv_rows
+
+
+def sparse_mla_bwd_workspace_size(shape: DsaShape) -> int:
+    return int(lib().dsa_sparse_mla_bwd_workspace_size(ctypes.byref(shape.c())))
+
+
+def sparse_mla_bwd_min_workspace_size(shape: DsaShape) -> int:
+    return int(lib().dsa_sparse_mla_bwd_min_workspace_size(ctypes.byref(shape.c())))
+
+
+def sparse_mla_bwd(shape: DsaShape, q, kv, idx, kv_len, lse, dout, dq=None, dkv=None, accumulate_dkv=False,
+                   workspace=None, stream=None):
+    """Backward of sparse_mla_fwd -> (dq [B,T,H,Dqk] f32, dkv [B,L_max,Dqk] f32)."""
+    dev = q.device
+    if dq is None:
+        dq = _empty((shape.batch, shape.n_q, shape.heads, shape.qk_dim), torch.float32, dev)
+    if dkv is None:
+        dkv = _empty((shape.batch, shape.max_kv, shape.qk_dim), torch.float32, dev)
+    if workspace is None:
+        workspace = _empty((max(1, sparse_mla_bwd_workspace_size(shape)),), torch.uint8, dev)
+    cs = shape.c()
+    _check("dsa_sparse_mla_bwd", lib().dsa_sparse_mla_bwd(ctypes.byref(cs), _ptr(q), _ptr(kv), _ptr(idx),
+                                                           _ptr(kv_len), _ptr(lse), _ptr(dout),
+                                                           _ptr(dq), _ptr(dkv), int(bool(accumulate_dkv)),
+                                                           _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dkv
 
 
 def forward_workspace_size(shape: DsaShape) -> int:

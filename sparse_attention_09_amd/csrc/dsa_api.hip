@@ -16,6 +16,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxTopk = 4096;
+constexpr int kMaxMlaSplit = 16;  // most list splits of one query (mla_split_count)
 constexpr int kMaxKv = 1 << 20;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -243,6 +244,41 @@ size_t min_forward_ws(const dsa_shape* s, bool own_idx)
     return best;
 }
 
+// Workspace of dsa_sparse_mla_bwd for a query chunk of tc rows.
+struct BwdLayout {
+    size_t Dd = 0, qT = 0, dT = 0, P = 0, DP = 0, total = 0;
+};
+
+int bwd_heads_padded(const dsa_shape* s) { return (s->heads + 15) / 16 * 16; }
+
+BwdLayout bwd_layout(const dsa_shape* s, int tc)
+{
+    BwdLayout l;
+    const size_t rows = (size_t)s->batch * tc, Hp = (size_t)bwd_heads_padded(s);
+    size_t off = 0;
+    l.Dd = off;
+    off += align_up(rows * kMaxMlaSplit * Hp * sizeof(float));
+    l.qT = off;
+    off += align_up(rows * s->qk_dim * Hp * 2);
+    l.dT = off;
+    off += align_up(rows * s->v_dim * Hp * 2);
+    l.P = off;
+    off += align_up(rows * s->topk * Hp * sizeof(float));
+    l.DP = off;
+    off += align_up(rows * s->topk * Hp * sizeof(float));
+    l.total = off;
+    return l;
+}
+
+dsa_status check_bwd_shape(const dsa_shape* s)
+{
+    DSA_TRY(check_common(s));
+    DSA_TRY(check_mla_shape(s));
+    if (s->mla_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (!dsa::mla_bwd_supported(s->mla_dtype, s->qk_dim, s->v_dim, s->heads)) return DSA_ERR_UNSUPPORTED;
+    return DSA_OK;
+}
+
 }  // namespace
 
 DSA_EXPORT const char* dsa_status_string(dsa_status st)
@@ -377,6 +413,74 @@ DSA_EXPORT dsa_status dsa_mla_kv_quant_fp8(int64_t rows, int32_t dim, const void
     DSA_TRY(ptr_ok(x, 16));
     DSA_TRY(ptr_ok(kv_rows, 16));
     return hip_status(dsa::launch_quant_rows(rows, dim, x, x_dtype, kv_rows, (int64_t)dim + 16, nullptr, 1, stream));
+}
+
+DSA_EXPORT size_t dsa_sparse_mla_bwd_workspace_size(const dsa_shape* s)
+{
+    if (check_bwd_shape(s) != DSA_OK) return 0;
+    return bwd_layout(s, s->n_q).total;
+}
+
+DSA_EXPORT size_t dsa_sparse_mla_bwd_min_workspace_size(const dsa_shape* s)
+{
+    if (check_bwd_shape(s) != DSA_OK) return 0;
+    return bwd_layout(s, 1).total;
+}
+
+DSA_EXPORT dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const void* q, const void* kv, const int32_t* idx,
+                                         const int32_t* kv_len, const float* lse, const void* dout,
+                                         float* dq, float* dkv, int32_t accumulate_dkv, void* workspace,
+                                         size_t ws_bytes, hipStream_t stream)
+{
+    DSA_TRY(check_bwd_shape(s));
+    DSA_TRY(ptr_ok(q, 16));
+    DSA_TRY(ptr_ok(kv, 16));
+    DSA_TRY(ptr_ok(idx, 4));
+    DSA_TRY(ptr_ok(kv_len, 4));
+    DSA_TRY(ptr_ok(lse, 4));
+    DSA_TRY(ptr_ok(dout, 16));
+    DSA_TRY(ptr_ok(dq, 16));
+    DSA_TRY(ptr_ok(dkv, 16));
+    if (!workspace) return DSA_ERR_WORKSPACE;
+    if (!aligned(workspace, kAlign)) return DSA_ERR_ALIGN;
+    int tc = s->n_q;
+    while (tc > 0 && bwd_layout(s, tc).total > ws_bytes) tc = next_chunk(tc);
+    if (tc == 0) return DSA_ERR_WORKSPACE;
+    const BwdLayout lay = bwd_layout(s, tc);
+    char* ws = (char*)workspace;
+    if (!accumulate_dkv &&
+        dsa::launch_zero_f32(dkv, (long long)s->batch * s->max_kv * s->qk_dim, stream) != hipSuccess)
+        return DSA_ERR_HIP;
+    for (int t0 = 0; t0 < s->n_q; t0 += tc) {
+        dsa::MlaBwdArgs a;
+        a.B = s->batch;
+        a.T = s->n_q;
+        a.Lmax = s->max_kv;
+        a.H = s->heads;
+        a.Hp = bwd_heads_padded(s);
+        a.K = s->topk;
+        a.Dqk = s->qk_dim;
+        a.Dv = s->v_dim;
+        a.t_begin = t0;
+        a.t_count = (s->n_q - t0) < tc ? (s->n_q - t0) : tc;
+        a.n_split = dsa::mla_split_count(s->batch, a.t_count, s->heads, s->topk);
+        a.sm = s->sm_scale;
+        a.q = (const uint16_t*)q;
+        a.kv = (const uint16_t*)kv;
+        a.idx = idx;
+        a.kv_len = kv_len;
+        a.lse = lse;
+        a.dout = (const uint16_t*)dout;
+        a.dq = dq;
+        a.dkv = dkv;
+        a.Dd = (float*)(ws + lay.Dd);
+        a.qT = (uint16_t*)(ws + lay.qT);
+        a.dT = (uint16_t*)(ws + lay.dT);
+        a.P = (float*)(ws + lay.P);
+        a.DP = (float*)(ws + lay.DP);
+        if (dsa::launch_mla_bwd_chunk(a, stream) != hipSuccess) return DSA_ERR_HIP;
+    }
+    return DSA_OK;
 }
 
 DSA_EXPORT size_t dsa_forward_workspace_size(const dsa_shape* s)

@@ -65,6 +65,31 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 // a preceding kernel on the same stream may clear them instead (pre_zeroed).
 size_t topk_zero_words(const TopkArgs& a);
 
+// Sparse MLA backward for queries [t_begin, t_begin + t_count) of every
+// sequence.  Chunk rows are r = b * t_count + (t - t_begin); Hp = H rounded up
+// to 16 (the padded heads hold zeros).
+struct MlaBwdArgs {
+    int B, T, Lmax, H, Hp, K, Dqk, Dv;
+    int t_begin, t_count, n_split;
+    float sm;
+    const uint16_t* q;      // [B,T,H,Dqk] bf16
+    const uint16_t* kv;     // [B,Lmax,Dqk] bf16
+    const int32_t* idx;     // [B,T,K]
+    const int32_t* kv_len;  // [B]
+    const float* lse;       // [B,T,H] (forward log-sum-exp, natural log)
+    const uint16_t* dout;   // [B,T,H,Dv] bf16
+    float* dq;              // [B,T,H,Dqk] out
+    float* dkv;             // [B,Lmax,Dqk] accumulated into
+    float* Dd;              // [rows, n_split, Hp] workspace: per-split sums of p * dP
+    uint16_t* qT;           // [rows, Dqk, Hp]    workspace
+    uint16_t* dT;           // [rows, Dv, Hp]     workspace
+    float* P;               // [rows, K, Hp]      workspace
+    float* DP;              // [rows, K, Hp]      workspace
+};
+bool mla_bwd_supported(int dtype, int Dqk, int Dv, int H);
+hipError_t launch_mla_bwd_chunk(const MlaBwdArgs& a, hipStream_t s);
+hipError_t launch_zero_f32(float* p, long long n, hipStream_t s);
+
 bool mla_supported(int dtype, int Dqk, int Dv);
 int mla_split_count(int B, int t_count, int H, int K);
 size_t mla_partial_bytes(int dtype, int B, int t_count, int H, int Dv, int n_split);

@@ -165,6 +165,36 @@ def test_mla_kv_quant_rejects_bad_arguments(dsa):
     assert f(4, 576, FAKE, 0, FAKE + 4, None) == -4
 
 
+def test_mla_bwd_rejects_bad_arguments(dsa):
+    L = dsa.lib()
+    f = L.dsa_sparse_mla_bwd
+    args = [FAKE] * 8  # q, kv, idx, kv_len, lse, dout, dq, dkv
+
+    def call(shape, *, ws=FAKE, nbytes=1 << 40, a=args):
+        return f(ctypes.byref(shape.c()), *a, 0, ws, nbytes, None)
+
+    assert call(_shape(dsa, mla_dtype="fp8")) == -3
+    assert call(_shape(dsa, mla_dtype="f32", qk_dim=80, v_dim=64)) == -3
+    assert call(_shape(dsa, heads=129)) == -6
+    assert call(_shape(dsa, qk_dim=320, v_dim=256)) == -6
+    assert call(_shape(dsa), ws=None) == -5
+    assert call(_shape(dsa), ws=FAKE + 16) == -4
+    assert call(_shape(dsa), nbytes=16) == -5
+    bad = list(args)
+    bad[6] = FAKE + 4  # dq
+    assert call(_shape(dsa), a=bad) == -4
+    bad = list(args)
+    bad[4] = None  # lse
+    assert call(_shape(dsa), a=bad) == -1
+    s = _shape(dsa, batch=2, n_q=4, topk=64, heads=20)
+    full, small = dsa.sparse_mla_bwd_workspace_size(s), dsa.sparse_mla_bwd_min_workspace_size(s)
+    # per query: p and dP for K entries x 32 padded heads, the split sums of p dP,
+    # and the transposed q and dout
+    assert small >= 2 * (2 * 64 * 32 * 4 + 32 * 4 + 576 * 32 * 2 + 512 * 32 * 2)
+    assert full >= 4 * small - 4 * 5 * 256
+    assert dsa.sparse_mla_bwd_workspace_size(_shape(dsa, mla_dtype="fp8")) == 0
+
+
 def test_forward_workspace_sizes_and_checks(dsa):
     from workloads import WORKLOADS
     L = dsa.lib()

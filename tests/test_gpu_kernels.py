@@ -393,3 +393,76 @@ def test_sparse_mla_large_logit_jumps(dsa, orc, dt, T):
     err = rel_rowmax(out, ro)
     assert err.max() < TOL["bf16"], err.max()
     assert np.abs(lse - rl).max() < TOL["bf16"] * np.abs(rl).max()
+
+
+# ------------------------------------------------------------ sparse MLA backward
+MLA_BWD_CASES = [
+    # B, T, H, Dqk, Dv, Lmax, lens, K, kind
+    (2, 3, 128, 576, 512, 300, [300, 120], 64, "topk"),          # one split: dq stored
+    (4, 1, 128, 576, 512, 4096, [4096, 3000, 2048, 700], 2048, "topk"),  # split decode: dq atomics
+    (1, 40, 128, 576, 512, 1000, [1000], 256, "messy"),          # duplicates and skipped entries
+    (2, 5, 20, 192, 128, 600, [600, 300], 128, "topk"),          # padded heads, the 192/128 shape
+    (3, 2, 128, 576, 512, 80, [80, 0, 1], 32, "poison"),         # an empty sequence, NaN rows past kv_len
+]
+
+
+def _bwd_run(dsa, case, seed, ws_bytes=None, accumulate=False, dkv=None):
+    B, T, H, Dqk, Dv, Lmax, lens, K, kind = case
+    q, kv, idx, kl = _mla_case(B, T, H, Dqk, Dv, Lmax, lens, K, "bf16", seed=seed, kind=kind)
+    if kind == "poison":
+        _poison_rows(kv, lens, float("nan"))
+    g = torch.Generator().manual_seed(seed + 1)
+    dout = torch.randn(B, T, H, Dv, generator=g).to(torch.bfloat16)
+    sm = Dqk ** -0.5
+    s = shape_of(dsa, batch=B, n_q=T, max_kv=Lmax, heads=H, qk_dim=Dqk, v_dim=Dv, topk=K, sm_scale=sm)
+    dev = [x.to(DEV) for x in (q, kv, idx, kl, dout)]
+    _, lse = dsa.sparse_mla_fwd(s, dev[0], dev[1], dev[2], dev[3])
+    ws = None if ws_bytes is None else torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    dq, dkv = dsa.sparse_mla_bwd(s, dev[0], dev[1], dev[2], dev[3], lse, dev[4], dkv=dkv,
+                                 accumulate_dkv=accumulate, workspace=ws)
+    torch.cuda.synchronize()
+    return (q, kv, idx, kl, dout, sm), dq, dkv, s
+
+
+def _bwd_ref(orc, case, inputs):
+    B, T, H, Dqk, Dv, Lmax, lens, K, kind = case
+    q, kv, idx, kl, dout, sm = inputs
+    ix = idx.clone().reshape(B * T, K)
+    for r in range(B * T):
+        L = lens[r // T]
+        ix[r][(ix[r] >= L) | (ix[r] < 0)] = -1
+    return orc.sparse_mla_bwd(q, kv, dout, ix, sm, v_dim=Dv), ix
+
+
+@pytest.mark.parametrize("case", MLA_BWD_CASES)
+def test_sparse_mla_bwd_against_oracle(dsa, orc, case):
+    """dq and dkv against the fp64 oracle at the bf16 tolerance (per-row max norm:
+    p and dz enter the MFMAs in bf16).  Cache rows nobody selects stay exactly zero."""
+    B, T, H, Dqk, Dv, Lmax, lens, K, kind = case
+    announce(f"sparse_mla_bwd {case}")
+    inputs, dq, dkv, _ = _bwd_run(dsa, case, seed=B * 131 + T + H)
+    (rq, rkv), ix = _bwd_ref(orc, case, inputs)
+    dq = dq.cpu().numpy().reshape(B * T, H, Dqk)
+    dkv = dkv.cpu().numpy()
+    live = np.abs(rq).max(axis=-1) > 0
+    assert np.all(dq[~live] == 0)
+    err = rel_rowmax(dq[live], rq[live])
+    assert err.max() < TOL["bf16"], err.max()
+    touched = np.abs(rkv).max(axis=-1) > 0
+    assert np.all(dkv[~touched] == 0)
+    err = rel_rowmax(dkv[touched], rkv[touched])
+    assert err.max() < TOL["bf16"], err.max()
+
+
+def test_sparse_mla_bwd_chunked_and_accumulated(dsa, orc):
+    """The smallest workspace (one query at a time) gives the one-pass gradients;
+    accumulate_dkv adds to what dkv holds."""
+    case = (1, 40, 128, 576, 512, 1000, [1000], 256, "messy")
+    announce("sparse_mla_bwd chunked")
+    inputs, dq1, dkv1, s = _bwd_run(dsa, case, seed=77)
+    small = dsa.sparse_mla_bwd_min_workspace_size(s)
+    _, dq2, dkv2, _ = _bwd_run(dsa, case, seed=77, ws_bytes=small)
+    assert torch.allclose(dq1, dq2, rtol=1e-4, atol=1e-6 * dq1.abs().max().item())
+    assert torch.allclose(dkv1, dkv2, rtol=1e-4, atol=1e-6 * dkv1.abs().max().item())
+    _, _, dkv3, _ = _bwd_run(dsa, case, seed=77, accumulate=True, dkv=dkv1.clone())
+    assert torch.allclose(dkv3, 2 * dkv1, rtol=1e-4, atol=1e-6 * dkv1.abs().max().item())

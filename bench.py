@@ -13,8 +13,11 @@ stage's fraction of its own roofline in "stages_frac"), with the HBM traffic of
 its kernel taken from a committed rocprofv3 counter summary under profiles/
 while the kernel source still matches it.  FP8 workloads build the index-key
 cache through the cache-append entry point and report that kernel's bandwidth
-("cache_append"), outside the timed step.  The CPU oracle is timed on a bounded
-sample of the same workload on the host cores.
+("cache_append"), outside the timed step.  BF16 workloads also time the sparse
+MLA backward (dq and dkv for the forward's lse and a random output gradient)
+and report it against its own roofline ("mla_bwd"), outside the timed step.
+The CPU oracle is timed on a bounded sample of the same workload on the host
+cores.
 
 Prints one JSON line.
 """
@@ -258,6 +261,74 @@ def time_stages(dsa, torch, cases, reps):
     return res
 
 
+def bwd_algorithmic(wl) -> dict:
+    """Work of one sparse MLA backward: five contractions per selected (query, key)
+    pair and head (logits, dP, dq, dk, dv); HBM bytes for the gathered rows, q, dO,
+    lse and dq once, and one fp32 update of every touched dkv row element (prefill
+    rows: once per cache row, as the forward counts its gather)."""
+    B, T, L, K, H, Dqk, Dv = wl.batch, wl.n_q, wl.kv_len, wl.topk, wl.heads, wl.qk_dim, wl.v_dim
+    sel = B * sum(min(K, L - T + t + 1) for t in range(T))
+    flops = 2.0 * sel * H * (3 * Dqk + 2 * Dv)
+    rows = sel if T == 1 else B * L
+    nbytes = rows * Dqk * 2 + B * T * H * (Dqk * 2 + Dv * 2 + 4 + Dqk * 4) + rows * Dqk * 4
+    return {"flops": flops, "bytes": nbytes, "pairs": sel}
+
+
+BWD_WS_CAP = 8 << 30  # workspace bound for the backward timing: longer query sets run in chunks
+
+
+def time_mla_bwd(dsa, torch, case, reps):
+    """Average duration of dsa_sparse_mla_bwd (every launch of one call) over `reps`
+    back-to-back calls between two HIP events on the launch stream, with the roofline
+    of the whole call; None for shapes the backward does not take.  The calls add
+    into dkv (accumulate_dkv, as gradient accumulation does); one call that clears
+    the dense dkv [B, L_max, D_qk] f32 first is timed on its own ("with_clear_us")."""
+    wl, sh = case.wl, case.shape
+    if wl.mla_dtype != "bf16" or (wl.qk_dim, wl.v_dim) not in ((576, 512), (192, 128)) or wl.heads > 128:
+        return None
+    B, T, H = wl.batch, wl.n_q, wl.heads
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    dout = torch.randn((B, T, H, wl.v_dim), generator=g, device="cuda").to(torch.bfloat16)
+    dq = torch.empty((B, T, H, wl.qk_dim), dtype=torch.float32, device="cuda")
+    dkv = torch.empty((B, wl.max_kv, wl.qk_dim), dtype=torch.float32, device="cuda")
+    ws = torch.empty((min(dsa.sparse_mla_bwd_workspace_size(sh), BWD_WS_CAP),), dtype=torch.uint8, device="cuda")
+    i = case.inp
+
+    def call(acc=True):
+        dsa.sparse_mla_bwd(sh, i["q"], i["kv"], case.idx, i["kv_len"], case.lse, dout, dq=dq, dkv=dkv,
+                           accumulate_dkv=acc, workspace=ws)
+
+    call(False)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    call(False)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    clear_us = e0.elapsed_time(e1) * 1000.0
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    alg = bwd_algorithmic(wl)
+    peak = PEAK_TFLOPS["bf16"]
+    tflops = alg["flops"] / (us * 1e-6) / 1e12
+    gbs = alg["bytes"] / (us * 1e-6) / 1e9
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    mfma = alg["flops"] / alg["bytes"] > ridge
+    return {"kernels": "bwd_prep + bwd_scores + bwd_dq + bwd_dkv per query chunk",
+            "avg_call_us": round(us, 2), "with_clear_us": round(clear_us, 2),
+            "pairs_per_s": round(alg["pairs"] / (us * 1e-6), 1),
+            "bound": "mfma" if mfma else "hbm", "achieved": round(tflops if mfma else gbs, 2 if mfma else 1),
+            "peak": peak if mfma else PEAK_HBM_GBS, "unit": "TFLOP/s" if mfma else "GB/s",
+            "frac": round((tflops / peak) if mfma else (gbs / PEAK_HBM_GBS), 4),
+            "tflops": round(tflops, 2), "gbs": round(gbs, 1), "flops_per_call": alg["flops"],
+            "bytes_per_call": alg["bytes"], "workspace_bytes": ws.numel(), "reps": reps}
+
+
 def recorded_traffic(wl, stage: str):
     """HBM bytes per launch of a stage's kernel from a committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy); None when
@@ -389,6 +460,10 @@ def run(args) -> dict:
                                  "avg_launch_us": round(cases[0].kv_quant_us, 2), "bound": "hbm",
                                  "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": round(gbs / PEAK_HBM_GBS, 4), "work_per_launch": nbytes}
+    if not args.no_bwd:
+        bwd = time_mla_bwd(dsa, torch, cases[0], 20 if wl.n_q == 1 else 3)
+        if bwd is not None:
+            res["mla_bwd"] = bwd
     del cases
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
@@ -404,6 +479,7 @@ def main():
     ap.add_argument("--workload", default="decode_32k")
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the sparse MLA backward timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run plain device copies of BYTES bytes (counter calibration)")
     args = ap.parse_args()

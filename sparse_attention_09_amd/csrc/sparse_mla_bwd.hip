@@ -19,7 +19,8 @@
 //           (list entry, head) in fp32, the split's sum of p dP per head;
 //   dq      D from the split sums, dz formed per entry, then the forward's value
 //           sum run over all key columns with dz in place of p:
-//           dq^T += K^T . dz^T, split lists add with fp32 atomics;
+//           dq += dz . K (head rows, so a lane group writes 32 consecutive
+//           columns of one head), split lists add with fp32 atomics;
 //   dkv     per (query, split): wave w owns 32-column blocks of dk (waves 0-3,
 //           sm dz^T q) or dv (waves 4-7, p^T dO), contracts over the heads on
 //           32x32x16 MFMA per 32-entry tile and adds the block to the cache rows
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a)
 
 // ---------------------------------------------------------------- list set-up
 // Loads the split's index list into LDS as row byte offsets (lrow, row 0 for
-// skipped entries) and cache rows (lsrc, -1 for skipped entries), and the
+// skipped entries) and/or cache rows (lsrc, -1 for skipped entries), and the
 // validity mask of each 32-entry tile.
 template <class C>
 __device__ __forceinline__ void load_list(const int32_t* idxr, int j_begin, int j_end, int n_list, int L,
@@ -135,7 +136,7 @@ __device__ __forceinline__ void load_list(const int32_t* idxr, int j_begin, int 
         const int j = tid + 512 * r;
         const int s = idxr[min(j_begin + j, j_last)];
         const bool ok = j < n_list && j_begin + j < j_end && s >= 0 && s < L;
-        lrow[j] = ok ? (uint32_t)s * C::ROWB : 0u;
+        if (lrow) lrow[j] = ok ? (uint32_t)s * C::ROWB : 0u;
         if (lsrc) lsrc[j] = ok ? s : -1;
         const uint64_t bits = __ballot(ok);
         if (lane == 0) {
@@ -294,9 +295,10 @@ __global__ __launch_bounds__(512) void bwd_scores_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------- dq
-// Wave (pair p, half h): heads 32p.., key columns [HALF * h, + HALF) of dq^T.
-// dz^T is the B operand, formed per lane in the logit register layout from the
-// stored p and dP and D, the sum of the split sums.
+// Wave (pair p, half h): heads 32p.., key columns [HALF * h, + HALF) of dq.
+// dz is the A operand, formed per lane in the logit register layout (lane: head
+// `col`, entries 8*i + 4*kb + jj) from the stored p and dP and D, the sum of the
+// split sums; K comes through transposed LDS reads as the B operand.
 template <int DQK, int DV>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a)
 {
@@ -312,7 +314,6 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a)
     const int pair = w >> 1, half = w & 1;
     const int col = lane & 31, kb = lane >> 5;
     const int head = u.hb * 128 + pair * 32 + col;
-    const bool head_ok = head < a.H;
     const int r = u.b * a.t_count + (u.t - a.t_begin);
 
     load_list<C>(a.idx + u.grow * a.K, u.j_begin, u.j_end, u.n_tiles * kTK, u.L, lrow, nullptr, tmask, tid, lane);
@@ -373,25 +374,26 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a)
                     (__attribute__((address_space(3))) s16x4*)(r1 + 64 * v));
                 const u32x2 y0 = __builtin_bit_cast(u32x2, x0);
                 const u32x2 y1 = __builtin_bit_cast(u32x2, x1);
-                acc[v] = mfma32(u32x4{y0[0], y0[1], y1[0], y1[1]}, pb, acc[v]);
+                acc[v] = mfma32(pb, u32x4{y0[0], y0[1], y1[0], y1[1]}, acc[v]);
             }
         }
     }
-    if (!head_ok) return;
-    // lane holds columns HALF*half + 32*v + 8*i + 4*kb + jj (register 4*i + jj) of head `col`
-    float* dst = a.dq + (u.grow * a.H + head) * DQK + C::HALF * half + 4 * kb;
+    // lane holds column HALF*half + 32*v + col of heads 32*pair + 8*i + 4*kb + jj (register 4*i + jj)
+    const int h0 = u.hb * 128 + pair * 32 + 4 * kb;
+    float* dst = a.dq + (u.grow * a.H + h0) * DQK + C::HALF * half + col;
 #pragma unroll
-    for (int v = 0; v < C::QT; ++v)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float* p = dst + 32 * v + 8 * i;
-            const f32x4 x = {a.sm * acc[v][4 * i], a.sm * acc[v][4 * i + 1], a.sm * acc[v][4 * i + 2],
-                             a.sm * acc[v][4 * i + 3]};
-            if (a.n_split == 1) {
-                *reinterpret_cast<f32x4*>(p) = x;
-            } else {
+        for (int jj = 0; jj < 4; ++jj) {
+            if (h0 + 8 * i + jj >= a.H) continue;
+            float* p = dst + (size_t)(8 * i + jj) * DQK;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) unsafeAtomicAdd(p + k, x[k]);
+            for (int v = 0; v < C::QT; ++v) {
+                const float x = a.sm * acc[v][4 * i + jj];
+                if (a.n_split == 1)
+                    p[32 * v] = x;
+                else
+                    unsafeAtomicAdd(p + 32 * v, x);
             }
         }
 }

@@ -322,7 +322,7 @@ void orc_topk(int B, int T, int Lmax, int K, const int* kv_len,
         long r = row_at(i, rows);
         long b = r / T, t = r % T;
         long p = (long)kv_len[b] - T + t;
-        long n = p + 1;
+        long n = p + 1 > 0 ? p + 1 : 0; /* p < 0: no candidates */
         long keff = n < K ? n : K;
         cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
         for (long s = 0; s < n; ++s) {
@@ -504,11 +504,11 @@ void orc_masked_dense_mla(int B, int T, int Lmax, int H, int Dqk, int Dv, int K,
         long r = row_at(i, rows);
         long b = r / T, t = r % T;
         long p = (long)kv_len[b] - T + t;
-        long n = p + 1;
+        long n = p + 1 > 0 ? p + 1 : 0; /* p < 0: no candidates */
         const int* ir = idx + (size_t)i * K;
         const float* kvb = kv + (size_t)b * Lmax * Dqk;
-        double* mask = (double*)malloc(sizeof(double) * (size_t)n);
-        double* z = (double*)malloc(sizeof(double) * (size_t)n);
+        double* mask = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        double* z = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
         for (long s = 0; s < n; ++s)
             mask[s] = -INFINITY;
         for (int j = 0; j < K; ++j)

@@ -145,6 +145,19 @@ def test_topk_short_rows_keep_everything(orc):
         assert np.all(idx[t][t + 1:] == -1)
 
 
+def test_topk_queries_before_the_cache_have_no_candidates(orc):
+    # kv_len < T: query t sits at p = kv_len - T + t < 0 for the first T - kv_len
+    # queries, which have no candidates at all (all -1), however negative p is
+    T, L, K = 9, 12, 2048
+    kl = np.array([5], np.int32)
+    sc = make_scores(T, L, seed=7).numpy()
+    idx = orc.topk(sc, kl, T, K)
+    for t in range(T):
+        p = 5 - T + t
+        assert sorted(idx[t][idx[t] >= 0].tolist()) == list(range(max(p + 1, 0)))
+        assert np.all(idx[t][max(p + 1, 0):] == -1)
+
+
 def test_topk_invariant_under_positive_weight_scaling(orc):
     rng = np.random.default_rng(6)
     B, T, H, D, L, K = 1, 8, 8, 32, 200, 20

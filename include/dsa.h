@@ -103,6 +103,30 @@ dsa_status dsa_index_scores(const dsa_shape* shape, const void* q_idx, const flo
                             const float* w, const void* k_idx, const float* k_scale,
                             const int32_t* kv_len, float* scores, hipStream_t stream);
 
+/* Indexer scores and per-query top-k in one pass, without the [T, L] score
+ * matrix (page items 1 and 2 fused; the streaming form for long prefill).  Each
+ * query row keeps a list of candidate (score, position) pairs in the workspace:
+ * every causal key joins until the list fills, the list is then cut to the
+ * row's exact top K and later keys join only when they score above the K-th.
+ * The result equals dsa_index_scores followed by dsa_topk on the same inputs,
+ * bit for bit.
+ *   q_idx, q_scale, w, k_idx, k_scale, kv_len as for dsa_index_scores.
+ *   idx [B,T,K] int32 out, as dsa_topk writes it (ascending positions, -1 padded).
+ *   workspace (256-byte aligned): dsa_index_topk_workspace_size(shape) bytes run
+ *   every query in one pass (B * T * cap * 8 bytes, cap = max(4K, K + 64)
+ *   rounded up to 64); any size >= dsa_index_topk_min_workspace_size works, the
+ *   queries then running in chunks of ceil(T / 2^k).  Contents are scratch.
+ * Errors: as dsa_index_scores and dsa_topk check the shape; NULL pointers ->
+ * DSA_ERR_NULL; q_idx or k_idx not 16-byte aligned, w, kv_len, idx or the fp8
+ * scales not 4-byte aligned, workspace not 256-byte aligned -> DSA_ERR_ALIGN;
+ * workspace NULL or below the minimum -> DSA_ERR_WORKSPACE. */
+size_t dsa_index_topk_workspace_size(const dsa_shape* shape);
+size_t dsa_index_topk_min_workspace_size(const dsa_shape* shape);
+dsa_status dsa_index_topk(const dsa_shape* shape, const void* q_idx, const float* q_scale,
+                          const float* w, const void* k_idx, const float* k_scale,
+                          const int32_t* kv_len, int32_t* idx, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
 /* Per-query top-k (page item 2).
  *   scores [B,T,L_max] f32 (only s <= p(t) is read), kv_len [B] int32
  *   idx    [B,T,K] int32 out: the k_eff = min(K, p(t)+1) positions with the

@@ -25,7 +25,8 @@ STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_DTY
 EXPORTS = ["dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_workspace_size",
            "dsa_sparse_mla_fwd", "dsa_rotate_quant_fp8", "dsa_index_cache_append_fp8", "dsa_forward_workspace_size",
            "dsa_mla_kv_quant_fp8", "dsa_forward_min_workspace_size", "dsa_forward", "dsa_status_string",
-           "dsa_sparse_mla_bwd_workspace_size", "dsa_sparse_mla_bwd_min_workspace_size", "dsa_sparse_mla_bwd"]
+           "dsa_sparse_mla_bwd_workspace_size", "dsa_sparse_mla_bwd_min_workspace_size", "dsa_sparse_mla_bwd",
+           "dsa_index_topk_workspace_size", "dsa_index_topk_min_workspace_size", "dsa_index_topk"]
 
 
 class DsaError(RuntimeError):
@@ -80,6 +81,9 @@ def lib() -> ctypes.CDLL:
         SP = ctypes.POINTER(CShape)
         sig = {
             "dsa_index_scores": ([SP, P, P, P, P, P, P, P, P], I32),
+            "dsa_index_topk_workspace_size": ([SP], SZ),
+            "dsa_index_topk_min_workspace_size": ([SP], SZ),
+            "dsa_index_topk": ([SP, P, P, P, P, P, P, P, P, SZ, P], I32),
             "dsa_topk_workspace_size": ([SP], SZ),
             "dsa_topk": ([SP, P, P, P, P, SZ, P], I32),
             "dsa_sparse_mla_workspace_size": ([SP], SZ),
@@ -150,6 +154,31 @@ def index_scores(shape: DsaShape, q_idx, w, k_idx, kv_len, q_scale=None, k_scale
                                                        _ptr(k_idx), _ptr(k_scale), _ptr(kv_len), _ptr(scores),
                                                        _stream(stream)))
     return scores
+
+
+def index_topk_workspace_size(shape: DsaShape) -> int:
+    return int(lib().dsa_index_topk_workspace_size(ctypes.byref(shape.c())))
+
+
+def index_topk_min_workspace_size(shape: DsaShape) -> int:
+    return int(lib().dsa_index_topk_min_workspace_size(ctypes.byref(shape.c())))
+
+
+def index_topk(shape: DsaShape, q_idx, w, k_idx, kv_len, q_scale=None, k_scale=None, idx=None, workspace=None,
+               stream=None):
+    """Indexer scores and top-k in one pass (no score matrix) -> idx [B,T,K] int32."""
+    if shape.idx_dtype == "fp8":
+        q_idx, k_idx = _view_u8(q_idx), _view_u8(k_idx)
+    dev = q_idx.device
+    if idx is None:
+        idx = _empty((shape.batch, shape.n_q, shape.topk), torch.int32, dev)
+    if workspace is None:
+        workspace = _empty((max(1, index_topk_workspace_size(shape)),), torch.uint8, dev)
+    cs = shape.c()
+    _check("dsa_index_topk", lib().dsa_index_topk(ctypes.byref(cs), _ptr(q_idx), _ptr(q_scale), _ptr(w),
+                                                   _ptr(k_idx), _ptr(k_scale), _ptr(kv_len), _ptr(idx),
+                                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+    return idx
 
 
 def topk_workspace_size(shape: DsaShape) -> int:

@@ -97,7 +97,17 @@ dsa::IndexerArgs indexer_args(const dsa_shape* s, const void* q, const float* qs
     a.fill = fill;
     a.zero = nullptr;
     a.zero_words = 0;
+    a.sel_cand = nullptr;
+    a.sel_cap = 0;
+    a.sel_k = 0;
+    a.sel_idx = nullptr;
     return a;
+}
+
+// Candidate-list bytes of dsa_index_topk for a query chunk of tc rows.
+size_t index_topk_bytes(const dsa_shape* s, int tc)
+{
+    return align_up((size_t)s->batch * tc * dsa::index_topk_cap(s->topk) * sizeof(uint64_t));
 }
 
 dsa::TopkArgs topk_args(const dsa_shape* s, const float* scores, const int32_t* kv_len, int32_t* idx, void* ws,
@@ -314,6 +324,51 @@ DSA_EXPORT dsa_status dsa_index_scores(const dsa_shape* s, const void* q_idx, co
     const dsa::IndexerArgs a =
         indexer_args(s, q_idx, q_scale, w, k_idx, k_scale, kv_len, scores, 0, s->n_q, /*fill=*/1);
     return hip_status(dsa::launch_indexer(s->idx_dtype, a, stream));
+}
+
+DSA_EXPORT size_t dsa_index_topk_workspace_size(const dsa_shape* s)
+{
+    if (check_common(s) != DSA_OK || check_indexer_shape(s) != DSA_OK || check_topk_shape(s) != DSA_OK) return 0;
+    return index_topk_bytes(s, s->n_q);
+}
+
+DSA_EXPORT size_t dsa_index_topk_min_workspace_size(const dsa_shape* s)
+{
+    if (check_common(s) != DSA_OK || check_indexer_shape(s) != DSA_OK || check_topk_shape(s) != DSA_OK) return 0;
+    return index_topk_bytes(s, 1);
+}
+
+DSA_EXPORT dsa_status dsa_index_topk(const dsa_shape* s, const void* q_idx, const float* q_scale, const float* w,
+                                     const void* k_idx, const float* k_scale, const int32_t* kv_len, int32_t* idx,
+                                     void* workspace, size_t ws_bytes, hipStream_t stream)
+{
+    DSA_TRY(check_common(s));
+    DSA_TRY(check_indexer_shape(s));
+    DSA_TRY(check_topk_shape(s));
+    DSA_TRY(ptr_ok(q_idx, 16));
+    DSA_TRY(ptr_ok(k_idx, 16));
+    DSA_TRY(ptr_ok(w, 4));
+    DSA_TRY(ptr_ok(kv_len, 4));
+    DSA_TRY(ptr_ok(idx, 4));
+    if (s->idx_dtype == DSA_FP8_E4M3) {
+        DSA_TRY(ptr_ok(q_scale, 4));
+        DSA_TRY(ptr_ok(k_scale, 4));
+    }
+    if (!workspace) return DSA_ERR_WORKSPACE;
+    if (!aligned(workspace, kAlign)) return DSA_ERR_ALIGN;
+    int tc = s->n_q;
+    while (tc > 0 && index_topk_bytes(s, tc) > ws_bytes) tc = next_chunk(tc);
+    if (tc == 0) return DSA_ERR_WORKSPACE;
+    for (int t0 = 0; t0 < s->n_q; t0 += tc) {
+        const int cnt = (s->n_q - t0) < tc ? (s->n_q - t0) : tc;
+        dsa::IndexerArgs a = indexer_args(s, q_idx, q_scale, w, k_idx, k_scale, kv_len, nullptr, t0, cnt, 0);
+        a.sel_cand = (uint32_t*)workspace;
+        a.sel_cap = dsa::index_topk_cap(s->topk);
+        a.sel_k = s->topk;
+        a.sel_idx = idx;
+        if (dsa::launch_index_topk(s->idx_dtype, a, stream) != hipSuccess) return DSA_ERR_HIP;
+    }
+    return DSA_OK;
 }
 
 DSA_EXPORT size_t dsa_topk_workspace_size(const dsa_shape* s)

@@ -24,6 +24,12 @@ struct IndexerArgs {
     int fill;               // write -inf for every s > p(t)
     uint32_t* zero;         // optional: words [0, zero_words) are cleared by the launch
     long long zero_words;   //   (a following top-k's counters, see topk_zero_words)
+    // streaming top-k (launch_index_topk): per chunk row a list of sel_cap
+    // (key, position) pairs in place of the score row; the top sel_k positions of
+    // row (b, t) go to sel_idx[(b * T + t) * sel_k ..]
+    uint32_t* sel_cand;     // [B * t_count, sel_cap, 2]
+    int sel_cap, sel_k;
+    int32_t* sel_idx;
 };
 
 // Top-k over score rows laid out as in IndexerArgs; writes idx rows of the full
@@ -57,6 +63,9 @@ struct MlaArgs {
 
 bool indexer_supported(int dtype, int D, int H);
 hipError_t launch_indexer(int dtype, const IndexerArgs& a, hipStream_t s);
+// Indexer scores and top-k in one pass, without the score matrix (IndexerArgs sel_*).
+hipError_t launch_index_topk(int dtype, const IndexerArgs& a, hipStream_t s);
+int index_topk_cap(int K);
 
 // Workspace of one top-k launch over B * t_count rows (0 when none is needed).
 size_t topk_workspace_bytes(int B, int t_count, int Lmax, int K);

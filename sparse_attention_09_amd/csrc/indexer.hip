@@ -19,6 +19,10 @@
 //   prefill (many queries): 4 waves x 2 queries share 64-key tiles staged in
 //           LDS (double buffered through registers), so each key row leaves L2
 //           once per 8 queries; blocks are issued longest-row first.
+// The prefill tiling also runs fused with the top-k of item 2 (launch_index_topk):
+// a wave owns its two query rows over the whole key range, so it keeps each
+// row's candidates in a list of its own instead of writing the score row, and
+// the [T, L] score matrix is never formed.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -255,12 +259,93 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a)
     }
 }
 
+// --------------------------------------------------------------- streaming top-k
+// A row's candidate list holds (position << 32 | key) words in position order,
+// key = float_key(score).  Until the list first fills, every causal key is
+// appended; then the list is cut to the row's exact top K (score descending,
+// position ascending) and only keys above the K-th key tau join later: a later
+// key equal to tau ranks behind K listed keys at least as large with smaller
+// positions, a smaller one behind K larger ones, so neither can be selected.
+// One wave owns a row.  The list lives in global memory (it stays in L2) and
+// is read back with device-coherent loads after the wave's stores have landed.
+
+__device__ __forceinline__ uint64_t cand_load(uint64_t* c, int i)
+{
+    return __hip_atomic_load(c + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Number of set bits of a wave mask in the lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Cuts list c[0, n), n >= K, to its top K in place (order kept) and returns the
+// K-th largest key.  Radix select over 8-bit digits with a 256-bin histogram in
+// the wave's own LDS words, then one ordered compaction (ballot prefixes).
+__device__ uint32_t cut_to_topk(uint64_t* c, int n, int K, uint32_t* hist, int lane)
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the wave's appends have reached L2
+    uint32_t prefix = 0, pmask = 0;
+    int want = K;  // rank of the K-th key among keys that match the prefix
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+        for (int i = lane; i < n; i += 64) {
+            const uint32_t k = (uint32_t)cand_load(c, i);
+            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        }
+        uint32_t hb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hb[j] = hist[4 * lane + j];
+        const uint32_t s = hb[0] + hb[1] + hb[2] + hb[3];
+        uint32_t suf = s;  // keys in the bins of this and higher lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t t = __shfl_down(suf, o, 64);
+            if (lane + o < 64) suf += t;
+        }
+        uint32_t cum = suf - s;  // keys in higher digits than this lane's bins
+        int d = -1;
+        uint32_t above = 0;
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+            if (d < 0 && cum < (uint32_t)want && cum + hb[j] >= (uint32_t)want) {
+                d = 4 * lane + j;
+                above = cum;
+            }
+            cum += hb[j];
+        }
+        const uint64_t m = __ballot(d >= 0);
+        const int src = __ffsll((unsigned long long)m) - 1;
+        d = __shfl(d, src, 64);
+        above = __shfl(above, src, 64);
+        prefix |= (uint32_t)d << shift;
+        pmask |= 0xFFu << shift;
+        want -= (int)above;
+    }
+    // keep every key above the K-th and the first `want` keys equal to it
+    int out = 0, eq_seen = 0;
+    for (int base = 0; base < n; base += 64) {
+        const int i = base + lane;
+        const uint64_t e = i < n ? cand_load(c, i) : 0ull;
+        const uint32_t k = (uint32_t)e;
+        const bool gt = i < n && k > prefix, eq = i < n && k == prefix;
+        const uint64_t be = __ballot(eq);
+        const bool keep = gt || (eq && eq_seen + lanes_below(be) < want);
+        const uint64_t bk = __ballot(keep);
+        if (keep) c[out + lanes_below(bk)] = e;
+        out += __popcll(bk);
+        eq_seen += __popcll(be);
+    }
+    return __builtin_amdgcn_readfirstlane(prefix);
+}
+
 // --------------------------------------------------------------- prefill tiling
 constexpr int kPrefillQPW = 2;
 constexpr int kPrefillTK = 64;  // keys per LDS tile
 
-template <int DT, int D, int HT>
-__global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs a)
+template <int DT, int D, int HT, bool SEL>
+__global__ __launch_bounds__(256, (SEL && DT != kF32) ? 2 : 1) void indexer_prefill_kernel(IndexerArgs a)
 {
     constexpr int QPW = kPrefillQPW;
     constexpr int QPB = 4 * QPW;
@@ -273,6 +358,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs a)
     constexpr int NLD = TK * CPR / 256;   // chunks each thread stages per tile
     static_assert(NLD >= 1 && (TK * CPR) % 256 == 0, "tile must split evenly over 256 threads");
     __shared__ __attribute__((aligned(16))) char smem[2][TK * PITCH];
+    __shared__ uint32_t shist[SEL ? 4 : 1][256];
 
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const int wave = threadIdx.x >> 6;
@@ -299,6 +385,21 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs a)
     float wv[QPW][HT][4];
 #pragma unroll
     for (int q = 0; q < QPW; ++q) load_query<DT, D, HT>(a, b, vq[q] ? tq[q] : a.t_begin, vq[q], qa[q], wv[q]);
+    // streaming top-k state of the wave's rows (wave-uniform)
+    uint64_t* cand[QPW];
+    int cnt[QPW];
+    uint32_t tau[QPW];
+    bool cut[QPW];
+    if constexpr (SEL) {
+#pragma unroll
+        for (int q = 0; q < QPW; ++q) {
+            const int r = b * a.t_count + (vq[q] ? tq[q] - a.t_begin : 0);
+            cand[q] = reinterpret_cast<uint64_t*>(a.sel_cand) + (size_t)r * a.sel_cap;
+            cnt[q] = 0;
+            tau[q] = 0u;
+            cut[q] = false;
+        }
+    }
 
     const char* kbase = (const char*)a.k + (size_t)b * a.Lmax * ROWB;
     const int ntile = (kend_blk + TK - 1) / TK;
@@ -347,8 +448,21 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs a)
 #pragma unroll
                         for (int m = 0; m < HT; ++m) acc[m] = dot_share<DT, NCH>(qa[q][m], kb, f32x4{0, 0, 0, 0});
                         const float v = head_sum<HT>(acc, wv[q]);
-                        if (g == 0 && key <= pq[q])
-                            a.scores[b * a.ld_b + (long long)(tq[q] - a.t_begin) * a.ld_t + key] = v * ks;
+                        if constexpr (SEL) {
+                            if (cnt[q] + 16 > a.sel_cap) {
+                                tau[q] = cut_to_topk(cand[q], cnt[q], a.sel_k, shist[wave], lane);
+                                cnt[q] = a.sel_k;
+                                cut[q] = true;
+                            }
+                            const uint32_t kk = float_key(v * ks);
+                            const bool app = g == 0 && key <= pq[q] && (!cut[q] || kk > tau[q]);
+                            const uint64_t m = __ballot(app);
+                            if (app) cand[q][cnt[q] + lanes_below(m)] = ((uint64_t)(uint32_t)key << 32) | kk;
+                            cnt[q] += __popcll(m);
+                        } else {
+                            if (g == 0 && key <= pq[q])
+                                a.scores[b * a.ld_b + (long long)(tq[q] - a.t_begin) * a.ld_t + key] = v * ks;
+                        }
                     }
                 }
             }
@@ -357,7 +471,20 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs a)
         __syncthreads();
     }
 
-    if (a.fill) {
+    if constexpr (SEL) {
+#pragma unroll
+        for (int q = 0; q < QPW; ++q) {
+            if (!vq[q]) continue;
+            if (cnt[q] > a.sel_k) {
+                cut_to_topk(cand[q], cnt[q], a.sel_k, shist[wave], lane);
+                cnt[q] = a.sel_k;
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            int32_t* dst = a.sel_idx + ((size_t)b * a.T + tq[q]) * a.sel_k;
+            for (int j = lane; j < a.sel_k; j += 64)
+                dst[j] = j < cnt[q] ? (int32_t)(cand_load(cand[q], j) >> 32) : -1;
+        }
+    } else if (a.fill) {
 #pragma unroll
         for (int q = 0; q < QPW; ++q) {
             if (!vq[q]) continue;
@@ -390,9 +517,25 @@ hipError_t launch_dt(const IndexerArgs& a, hipStream_t s)
     } else {
         constexpr int QPB = 4 * kPrefillQPW;
         dim3 grid((a.t_count + QPB - 1) / QPB, a.B);
-        indexer_prefill_kernel<DT, D, HT><<<grid, 256, 0, s>>>(a);
+        indexer_prefill_kernel<DT, D, HT, false><<<grid, 256, 0, s>>>(a);
     }
     return hipGetLastError();
+}
+
+template <int DT, int D, int HT>
+hipError_t launch_sel_dt(const IndexerArgs& a, hipStream_t s)
+{
+    if (a.t_count <= 0 || a.B <= 0) return hipSuccess;
+    constexpr int QPB = 4 * kPrefillQPW;
+    dim3 grid((a.t_count + QPB - 1) / QPB, a.B);
+    indexer_prefill_kernel<DT, D, HT, true><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_sel_heads(const IndexerArgs& a, hipStream_t s)
+{
+    return a.H <= 16 ? launch_sel_dt<DT, D, 1>(a, s) : launch_sel_dt<DT, D, 4>(a, s);
 }
 
 template <int DT, int D>
@@ -409,6 +552,22 @@ bool indexer_supported(int dtype, int D, int H)
     if (dtype == kF32) return D == 32 || D == 64 || D == 128;
     if (dtype == kBF16 || dtype == kFP8) return D == 128;
     return false;
+}
+
+int index_topk_cap(int K)
+{
+    const int c = std::max(4 * K, K + 64);
+    return (c + 63) / 64 * 64;
+}
+
+hipError_t launch_index_topk(int dtype, const IndexerArgs& a, hipStream_t s)
+{
+    if (a.sel_k < 1 || a.sel_cap < a.sel_k + 16) return hipErrorInvalidValue;
+    if (dtype == kBF16) return launch_sel_heads<kBF16, 128>(a, s);
+    if (dtype == kFP8) return launch_sel_heads<kFP8, 128>(a, s);
+    if (a.D == 32) return launch_sel_heads<kF32, 32>(a, s);
+    if (a.D == 64) return launch_sel_heads<kF32, 64>(a, s);
+    return launch_sel_heads<kF32, 128>(a, s);
 }
 
 hipError_t launch_indexer(int dtype, const IndexerArgs& a, hipStream_t s)

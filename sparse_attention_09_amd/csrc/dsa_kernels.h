@@ -65,7 +65,7 @@ bool indexer_supported(int dtype, int D, int H);
 hipError_t launch_indexer(int dtype, const IndexerArgs& a, hipStream_t s);
 // Indexer scores and top-k in one pass, without the score matrix (IndexerArgs sel_*).
 hipError_t launch_index_topk(int dtype, const IndexerArgs& a, hipStream_t s);
-int index_topk_cap(int K);
+int index_topk_cap(int K);  // list entries per row
 
 // Workspace of one top-k launch over B * t_count rows (0 when none is needed).
 size_t topk_workspace_bytes(int B, int t_count, int Lmax, int K);

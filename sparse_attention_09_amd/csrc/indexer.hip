@@ -266,13 +266,9 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a)
 // position ascending) and only keys above the K-th key tau join later: a later
 // key equal to tau ranks behind K listed keys at least as large with smaller
 // positions, a smaller one behind K larger ones, so neither can be selected.
-// One wave owns a row.  The list lives in global memory (it stays in L2) and
-// is read back with device-coherent loads after the wave's stores have landed.
-
-__device__ __forceinline__ uint64_t cand_load(uint64_t* c, int i)
-{
-    return __hip_atomic_load(c + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// One wave owns a row.  The list lives in global memory (it stays in L2); before
+// reading it back the wave waits for its own stores and invalidates its vector
+// L1 (an agent-scope acquire-release fence), so plain loads see the list.
 
 // Number of set bits of a wave mask in the lanes below this one.
 __device__ __forceinline__ int lanes_below(uint64_t m)
@@ -280,19 +276,29 @@ __device__ __forceinline__ int lanes_below(uint64_t m)
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+
 // Cuts list c[0, n), n >= K, to its top K in place (order kept) and returns the
 // K-th largest key.  Radix select over 8-bit digits with a 256-bin histogram in
 // the wave's own LDS words, then one ordered compaction (ballot prefixes).
-__device__ uint32_t cut_to_topk(uint64_t* c, int n, int K, uint32_t* hist, int lane)
+template <int kCutBatch>  // list entries per lane in flight
+__device__ __forceinline__ uint32_t cut_to_topk(uint64_t* c, int n, int K, uint32_t* hist, int lane)
 {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the wave's appends have reached L2
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+    const uint32_t* keys = reinterpret_cast<const uint32_t*>(c);  // low word of each entry
     uint32_t prefix = 0, pmask = 0;
     int want = K;  // rank of the K-th key among keys that match the prefix
     for (int shift = 24; shift >= 0; shift -= 8) {
         for (int i = lane; i < 256; i += 64) hist[i] = 0u;
-        for (int i = lane; i < n; i += 64) {
-            const uint32_t k = (uint32_t)cand_load(c, i);
-            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        for (int base = 0; base < n; base += 64 * kCutBatch) {
+            uint32_t k[kCutBatch];
+#pragma unroll
+            for (int u = 0; u < kCutBatch; ++u) {
+                const int i = min(base + 64 * u + lane, n - 1);
+                k[u] = keys[2 * i];
+            }
+#pragma unroll
+            for (int u = 0; u < kCutBatch; ++u)
+                if (base + 64 * u + lane < n && (k[u] & pmask) == prefix) atomicAdd(&hist[(k[u] >> shift) & 255u], 1u);
         }
         uint32_t hb[4];
 #pragma unroll
@@ -323,19 +329,26 @@ __device__ uint32_t cut_to_topk(uint64_t* c, int n, int K, uint32_t* hist, int l
         pmask |= 0xFFu << shift;
         want -= (int)above;
     }
-    // keep every key above the K-th and the first `want` keys equal to it
+    // keep every key above the K-th and the first `want` keys equal to it; a
+    // batch is read whole before any of it is written, and writes never pass
+    // the entries read
     int out = 0, eq_seen = 0;
-    for (int base = 0; base < n; base += 64) {
-        const int i = base + lane;
-        const uint64_t e = i < n ? cand_load(c, i) : 0ull;
-        const uint32_t k = (uint32_t)e;
-        const bool gt = i < n && k > prefix, eq = i < n && k == prefix;
-        const uint64_t be = __ballot(eq);
-        const bool keep = gt || (eq && eq_seen + lanes_below(be) < want);
-        const uint64_t bk = __ballot(keep);
-        if (keep) c[out + lanes_below(bk)] = e;
-        out += __popcll(bk);
-        eq_seen += __popcll(be);
+    for (int base = 0; base < n; base += 64 * kCutBatch) {
+        uint64_t e[kCutBatch];
+#pragma unroll
+        for (int u = 0; u < kCutBatch; ++u) e[u] = c[min(base + 64 * u + lane, n - 1)];
+#pragma unroll
+        for (int u = 0; u < kCutBatch; ++u) {
+            const bool in = base + 64 * u + lane < n;
+            const uint32_t k = (uint32_t)e[u];
+            const bool gt = in && k > prefix, eq = in && k == prefix;
+            const uint64_t be = __ballot(eq);
+            const bool keep = gt || (eq && eq_seen + lanes_below(be) < want);
+            const uint64_t bk = __ballot(keep);
+            if (keep) c[out + lanes_below(bk)] = e[u];
+            out += __popcll(bk);
+            eq_seen += __popcll(be);
+        }
     }
     return __builtin_amdgcn_readfirstlane(prefix);
 }
@@ -429,6 +442,27 @@ __global__ __launch_bounds__(256, (SEL && DT != kF32) ? 2 : 1) void indexer_pref
         const int buf = it & 1;
         if (it + 1 < ntile) fetch(it + 1);
         const int tile0 = it * TK;
+        if constexpr (SEL) {
+            // room for a whole tile of appends (TK per row) before it is scored;
+            // one inlined cut serves both rows (operands picked, not indexed)
+            static_assert(QPW == 2, "the cut below picks between two rows");
+            for (;;) {
+                const bool c0 = tile0 <= pq[0] && cnt[0] + TK > a.sel_cap;
+                const bool c1 = tile0 <= pq[1] && cnt[1] + TK > a.sel_cap;
+                if (!c0 && !c1) break;
+                const uint32_t t =
+                    cut_to_topk<4>(c0 ? cand[0] : cand[1], c0 ? cnt[0] : cnt[1], a.sel_k, shist[wave], lane);
+                if (c0) {
+                    tau[0] = t;
+                    cnt[0] = a.sel_k;
+                    cut[0] = true;
+                } else {
+                    tau[1] = t;
+                    cnt[1] = a.sel_k;
+                    cut[1] = true;
+                }
+            }
+        }
         if (tile0 < kend_w) {
 #pragma unroll
             for (int sub = 0; sub < TK / 16; ++sub) {
@@ -449,11 +483,6 @@ __global__ __launch_bounds__(256, (SEL && DT != kF32) ? 2 : 1) void indexer_pref
                         for (int m = 0; m < HT; ++m) acc[m] = dot_share<DT, NCH>(qa[q][m], kb, f32x4{0, 0, 0, 0});
                         const float v = head_sum<HT>(acc, wv[q]);
                         if constexpr (SEL) {
-                            if (cnt[q] + 16 > a.sel_cap) {
-                                tau[q] = cut_to_topk(cand[q], cnt[q], a.sel_k, shist[wave], lane);
-                                cnt[q] = a.sel_k;
-                                cut[q] = true;
-                            }
                             const uint32_t kk = float_key(v * ks);
                             const bool app = g == 0 && key <= pq[q] && (!cut[q] || kk > tau[q]);
                             const uint64_t m = __ballot(app);
@@ -472,17 +501,22 @@ __global__ __launch_bounds__(256, (SEL && DT != kF32) ? 2 : 1) void indexer_pref
     }
 
     if constexpr (SEL) {
+        for (;;) {  // the final cuts, one inlined copy for both rows
+            const bool c0 = vq[0] && cnt[0] > a.sel_k, c1 = vq[1] && cnt[1] > a.sel_k;
+            if (!c0 && !c1) break;
+            cut_to_topk<16>(c0 ? cand[0] : cand[1], c0 ? cnt[0] : cnt[1], a.sel_k, shist[wave], lane);
+            if (c0)
+                cnt[0] = a.sel_k;
+            else
+                cnt[1] = a.sel_k;
+        }
 #pragma unroll
         for (int q = 0; q < QPW; ++q) {
             if (!vq[q]) continue;
-            if (cnt[q] > a.sel_k) {
-                cut_to_topk(cand[q], cnt[q], a.sel_k, shist[wave], lane);
-                cnt[q] = a.sel_k;
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
             int32_t* dst = a.sel_idx + ((size_t)b * a.T + tq[q]) * a.sel_k;
             for (int j = lane; j < a.sel_k; j += 64)
-                dst[j] = j < cnt[q] ? (int32_t)(cand_load(cand[q], j) >> 32) : -1;
+                dst[j] = j < cnt[q] ? (int32_t)(cand[q][j] >> 32) : -1;
         }
     } else if (a.fill) {
 #pragma unroll
@@ -562,7 +596,7 @@ int index_topk_cap(int K)
 
 hipError_t launch_index_topk(int dtype, const IndexerArgs& a, hipStream_t s)
 {
-    if (a.sel_k < 1 || a.sel_cap < a.sel_k + 16) return hipErrorInvalidValue;
+    if (a.sel_k < 1 || a.sel_cap < a.sel_k + kPrefillTK) return hipErrorInvalidValue;
     if (dtype == kBF16) return launch_sel_heads<kBF16, 128>(a, s);
     if (dtype == kFP8) return launch_sel_heads<kFP8, 128>(a, s);
     if (a.D == 32) return launch_sel_heads<kF32, 32>(a, s);

@@ -16,6 +16,8 @@ cache through the cache-append entry point and report that kernel's bandwidth
 ("cache_append"), outside the timed step.  BF16 workloads also time the sparse
 MLA backward (dq and dkv for the forward's lse and a random output gradient)
 and report it against its own roofline ("mla_bwd"), outside the timed step.
+Prefill workloads also time the streaming indexer -> top-k entry point, which
+keeps per-row candidate lists instead of the score matrix ("index_topk_stream").
 The CPU oracle is timed on a bounded sample of the same workload on the host
 cores.
 
@@ -329,6 +331,39 @@ def time_mla_bwd(dsa, torch, case, reps):
             "bytes_per_call": alg["bytes"], "workspace_bytes": ws.numel(), "reps": reps}
 
 
+def time_index_topk(dsa, torch, case, reps):
+    """Average duration of dsa_index_topk (indexer scores and top-k in one pass, no
+    score matrix) on the case's inputs, and whether it selects what the forward did."""
+    wl, sh, i = case.wl, case.shape, case.inp
+    qi = case.q_codes if wl.idx_dtype == "fp8" else i["q_idx"]
+    qs = getattr(case, "q_scale", None)
+    ws = torch.empty((dsa.index_topk_workspace_size(sh),), dtype=torch.uint8, device="cuda")
+    idx = torch.empty_like(case.idx)
+
+    def call():
+        dsa.index_topk(sh, qi, i["w"], case.k_idx, i["kv_len"], q_scale=qs, k_scale=case.k_scale, idx=idx,
+                       workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(idx, case.idx))
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    flops = algorithmic(wl)["indexer"]["flops"]
+    tf = flops / (us * 1e-6) / 1e12
+    peak = mfma_peak(wl, "indexer")
+    return {"kernel": "indexer_prefill_kernel (streaming top-k)", "avg_call_us": round(us, 2),
+            "bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+            "workspace_bytes": ws.numel(), "score_matrix_bytes": wl.batch * wl.n_q * wl.max_kv * 4,
+            "same_selection_as_forward": same, "reps": reps}
+
+
 def recorded_traffic(wl, stage: str):
     """HBM bytes per launch of a stage's kernel from a committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy); None when
@@ -460,6 +495,8 @@ def run(args) -> dict:
                                  "avg_launch_us": round(cases[0].kv_quant_us, 2), "bound": "hbm",
                                  "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": round(gbs / PEAK_HBM_GBS, 4), "work_per_launch": nbytes}
+    if wl.n_q > 2 and not args.no_stages:
+        res["index_topk_stream"] = time_index_topk(dsa, torch, cases[0], max(3, min(steps, 20)))
     if not args.no_bwd:
         bwd = time_mla_bwd(dsa, torch, cases[0], 20 if wl.n_q == 1 else 3)
         if bwd is not None:

@@ -214,3 +214,36 @@ def test_forward_workspace_sizes_and_checks(dsa):
     bad = dsa.DsaShape.of(WORKLOADS["decode_32k"])
     bad.heads = 0
     assert dsa.forward_workspace_size(bad) == 0
+
+
+def test_index_topk_rejects_bad_arguments(dsa):
+    L = dsa.lib()
+    f = L.dsa_index_topk
+    args = [FAKE] * 7  # q_idx, q_scale, w, k_idx, k_scale, kv_len, idx
+
+    def call(shape, *, ws=FAKE, nbytes=1 << 40, a=args):
+        return f(ctypes.byref(shape.c()), *a, ws, nbytes, None)
+
+    assert call(_shape(dsa, topk=0)) == -2
+    assert call(_shape(dsa, topk=4097)) == -6
+    assert call(_shape(dsa, idx_heads=65)) == -6
+    assert call(_shape(dsa, n_q=300, max_kv=256)) == -2
+    assert call(_shape(dsa), ws=None) == -5
+    assert call(_shape(dsa), ws=FAKE + 16) == -4
+    assert call(_shape(dsa), nbytes=16) == -5
+    for i, name in ((0, "q_idx"), (2, "w"), (3, "k_idx"), (5, "kv_len"), (6, "idx")):
+        bad = list(args)
+        bad[i] = None
+        assert call(_shape(dsa), a=bad) == -1, name
+    bad = list(args)
+    bad[6] = FAKE + 2  # idx
+    assert call(_shape(dsa), a=bad) == -4
+    bad = list(args)
+    bad[1] = None  # fp8 needs the query scales
+    assert call(_shape(dsa, idx_dtype="fp8"), a=bad) == -1
+    # sizes: one pass for every query, or one query at a time; 8-byte list words per row
+    s = _shape(dsa, batch=2, n_q=4, topk=64)
+    full, small = dsa.index_topk_workspace_size(s), dsa.index_topk_min_workspace_size(s)
+    cap = max(4 * 64, 64 + 64)
+    assert full >= 2 * 4 * cap * 8 and small >= 2 * cap * 8 and small < full
+    assert dsa.index_topk_workspace_size(_shape(dsa, topk=0)) == 0

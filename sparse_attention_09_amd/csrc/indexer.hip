@@ -261,11 +261,14 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a)
 
 // --------------------------------------------------------------- streaming top-k
 // A row's candidate list holds (position << 32 | key) words in position order,
-// key = float_key(score).  Until the list first fills, every causal key is
-// appended; then the list is cut to the row's exact top K (score descending,
-// position ascending) and only keys above the K-th key tau join later: a later
-// key equal to tau ranks behind K listed keys at least as large with smaller
-// positions, a smaller one behind K larger ones, so neither can be selected.
+// key = float_key(score); keys below the row's bound lo never join it.  Until the
+// list first fills, lo = 0 and every causal key joins.  A full list is cut: every
+// key whose top 16 bits reach those of the K-th key is kept and lo becomes that
+// 16-bit floor (a dropped or later key below it ranks behind K kept keys larger
+// than it); if that leaves no room, the list is cut to the row's exact top K
+// (score descending, position ascending) and lo becomes the K-th key + 1 (a later
+// key equal to it ranks behind K listed keys at least as large with smaller
+// positions).  The end of the row takes the exact cut.
 // One wave owns a row.  The list lives in global memory (it stays in L2); before
 // reading it back the wave waits for its own stores and invalidates its vector
 // L1 (an agent-scope acquire-release fence), so plain loads see the list.
@@ -277,17 +280,21 @@ __device__ __forceinline__ int lanes_below(uint64_t m)
 }
 
 
-// Cuts list c[0, n), n >= K, to its top K in place (order kept) and returns the
-// K-th largest key.  Radix select over 8-bit digits with a 256-bin histogram in
-// the wave's own LDS words, then one ordered compaction (ballot prefixes).
-template <int kCutBatch>  // list entries per lane in flight
-__device__ __forceinline__ uint32_t cut_to_topk(uint64_t* c, int n, int K, uint32_t* hist, int lane)
+// Cuts list c[0, n), n >= K, in place (order kept).  Radix select over 8-bit
+// digits with a 256-bin histogram in the wave's own LDS words, then one ordered
+// compaction (ballot prefixes).  With EXACT the list keeps exactly the top K and
+// the K-th largest key tau is returned; otherwise only the top 16 bits of tau are
+// resolved and every key at or above lo = (those bits << 16) is kept (at least K
+// keys), lo being returned: each dropped key is then below K kept ones.  *kept
+// receives the new length.
+template <int kCutBatch, bool EXACT>  // list entries per lane in flight
+__device__ __forceinline__ uint32_t cut_to_topk(uint64_t* c, int n, int K, uint32_t* hist, int lane, int* kept)
 {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
     const uint32_t* keys = reinterpret_cast<const uint32_t*>(c);  // low word of each entry
     uint32_t prefix = 0, pmask = 0;
     int want = K;  // rank of the K-th key among keys that match the prefix
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int shift = 24; shift >= (EXACT ? 0 : 16); shift -= 8) {
         for (int i = lane; i < 256; i += 64) hist[i] = 0u;
         for (int base = 0; base < n; base += 64 * kCutBatch) {
             uint32_t k[kCutBatch];
@@ -329,9 +336,9 @@ __device__ __forceinline__ uint32_t cut_to_topk(uint64_t* c, int n, int K, uint3
         pmask |= 0xFFu << shift;
         want -= (int)above;
     }
-    // keep every key above the K-th and the first `want` keys equal to it; a
-    // batch is read whole before any of it is written, and writes never pass
-    // the entries read
+    // EXACT: keep every key above the K-th and the first `want` keys equal to it;
+    // else every key whose top 16 bits are at least the prefix.  A batch is read
+    // whole before any of it is written, and writes never pass the entries read.
     int out = 0, eq_seen = 0;
     for (int base = 0; base < n; base += 64 * kCutBatch) {
         uint64_t e[kCutBatch];
@@ -341,7 +348,7 @@ __device__ __forceinline__ uint32_t cut_to_topk(uint64_t* c, int n, int K, uint3
         for (int u = 0; u < kCutBatch; ++u) {
             const bool in = base + 64 * u + lane < n;
             const uint32_t k = (uint32_t)e[u];
-            const bool gt = in && k > prefix, eq = in && k == prefix;
+            const bool gt = in && (EXACT ? k > prefix : k >= prefix), eq = EXACT && in && k == prefix;
             const uint64_t be = __ballot(eq);
             const bool keep = gt || (eq && eq_seen + lanes_below(be) < want);
             const uint64_t bk = __ballot(keep);
@@ -350,6 +357,7 @@ __device__ __forceinline__ uint32_t cut_to_topk(uint64_t* c, int n, int K, uint3
             eq_seen += __popcll(be);
         }
     }
+    *kept = out;
     return __builtin_amdgcn_readfirstlane(prefix);
 }
 
@@ -401,16 +409,14 @@ __global__ __launch_bounds__(256, (SEL && DT != kF32) ? 2 : 1) void indexer_pref
     // streaming top-k state of the wave's rows (wave-uniform)
     uint64_t* cand[QPW];
     int cnt[QPW];
-    uint32_t tau[QPW];
-    bool cut[QPW];
+    uint32_t lo[QPW];  // smallest key that still joins the list
     if constexpr (SEL) {
 #pragma unroll
         for (int q = 0; q < QPW; ++q) {
             const int r = b * a.t_count + (vq[q] ? tq[q] - a.t_begin : 0);
             cand[q] = reinterpret_cast<uint64_t*>(a.sel_cand) + (size_t)r * a.sel_cap;
             cnt[q] = 0;
-            tau[q] = 0u;
-            cut[q] = false;
+            lo[q] = 0u;
         }
     }
 
@@ -446,20 +452,25 @@ __global__ __launch_bounds__(256, (SEL && DT != kF32) ? 2 : 1) void indexer_pref
             // room for a whole tile of appends (TK per row) before it is scored;
             // one inlined cut serves both rows (operands picked, not indexed)
             static_assert(QPW == 2, "the cut below picks between two rows");
+            // The cut first resolves 16 bits of the K-th key only; when the keys
+            // sharing them leave no room, the exact cut follows.
             for (;;) {
                 const bool c0 = tile0 <= pq[0] && cnt[0] + TK > a.sel_cap;
                 const bool c1 = tile0 <= pq[1] && cnt[1] + TK > a.sel_cap;
                 if (!c0 && !c1) break;
-                const uint32_t t =
-                    cut_to_topk<4>(c0 ? cand[0] : cand[1], c0 ? cnt[0] : cnt[1], a.sel_k, shist[wave], lane);
+                uint64_t* c = c0 ? cand[0] : cand[1];
+                int n = c0 ? cnt[0] : cnt[1];
+                uint32_t l = cut_to_topk<4, false>(c, n, a.sel_k, shist[wave], lane, &n);
+                if (n + TK > a.sel_cap) {
+                    const uint32_t t = cut_to_topk<4, true>(c, n, a.sel_k, shist[wave], lane, &n);
+                    l = t == 0xFFFFFFFFu ? t : t + 1u;  // strictly above the K-th key
+                }
                 if (c0) {
-                    tau[0] = t;
-                    cnt[0] = a.sel_k;
-                    cut[0] = true;
+                    lo[0] = l;
+                    cnt[0] = n;
                 } else {
-                    tau[1] = t;
-                    cnt[1] = a.sel_k;
-                    cut[1] = true;
+                    lo[1] = l;
+                    cnt[1] = n;
                 }
             }
         }
@@ -484,7 +495,7 @@ __global__ __launch_bounds__(256, (SEL && DT != kF32) ? 2 : 1) void indexer_pref
                         const float v = head_sum<HT>(acc, wv[q]);
                         if constexpr (SEL) {
                             const uint32_t kk = float_key(v * ks);
-                            const bool app = g == 0 && key <= pq[q] && (!cut[q] || kk > tau[q]);
+                            const bool app = g == 0 && key <= pq[q] && kk >= lo[q];
                             const uint64_t m = __ballot(app);
                             if (app) cand[q][cnt[q] + lanes_below(m)] = ((uint64_t)(uint32_t)key << 32) | kk;
                             cnt[q] += __popcll(m);
@@ -504,11 +515,12 @@ __global__ __launch_bounds__(256, (SEL && DT != kF32) ? 2 : 1) void indexer_pref
         for (;;) {  // the final cuts, one inlined copy for both rows
             const bool c0 = vq[0] && cnt[0] > a.sel_k, c1 = vq[1] && cnt[1] > a.sel_k;
             if (!c0 && !c1) break;
-            cut_to_topk<16>(c0 ? cand[0] : cand[1], c0 ? cnt[0] : cnt[1], a.sel_k, shist[wave], lane);
+            int n = 0;
+            cut_to_topk<16, true>(c0 ? cand[0] : cand[1], c0 ? cnt[0] : cnt[1], a.sel_k, shist[wave], lane, &n);
             if (c0)
-                cnt[0] = a.sel_k;
+                cnt[0] = n;
             else
-                cnt[1] = a.sel_k;
+                cnt[1] = n;
         }
 #pragma unroll
         for (int q = 0; q < QPW; ++q) {

@@ -214,7 +214,7 @@ def _mla_case(B, T, H, Dqk, Dv, Lmax, lens, K, dt, seed, kind="topk"):
             p = lens[b] - T + t
             n = max(0, min(K, p + 1))
             perm = torch.randperm(max(p + 1, 1), generator=g)[:n]
-            idx[b, t, :n] = perm.int()
+            idx[b, t, :n] = (perm.sort().values if kind == "sorted" else perm).int()
             if kind in ("messy", "poison") and K >= 8:
                 idx[b, t, 0] = idx[b, t, 1]          # a duplicate
                 idx[b, t, 2] = lens[b] + 5           # out of range -> skipped
@@ -405,6 +405,9 @@ MLA_BWD_CASES = [
     (3, 2, 128, 576, 512, 80, [80, 0, 1], 32, "poison"),         # an empty sequence, NaN rows past kv_len
     (2, 3, 128, 576, 512, 500, [500, 2], 100, "messy"),          # K not a multiple of 32; a query before the cache
     (1, 70, 96, 576, 512, 4096, [4096], 1000, "topk"),           # two list splits of a long list, 96 heads
+    # one query per sequence, ascending lists (top-k's layout)
+    (4, 1, 128, 576, 512, 4096, [4096, 3000, 2048, 700], 2048, "sorted"),
+    (3, 1, 20, 192, 128, 600, [600, 1, 0], 128, "sorted"),
 ]
 
 
@@ -474,4 +477,9 @@ def test_sparse_mla_bwd_chunked_and_accumulated(dsa, orc):
     assert torch.allclose(dq1, dq2, rtol=1e-4, atol=1e-6 * dq1.abs().max().item())
     assert torch.allclose(dkv1, dkv2, rtol=1e-4, atol=1e-6 * dkv1.abs().max().item())
     _, _, dkv3, _ = _bwd_run(dsa, case, seed=77, accumulate=True, dkv=dkv1.clone())
+    assert torch.allclose(dkv3, 2 * dkv1, rtol=1e-4, atol=1e-6 * dkv1.abs().max().item())
+    # the same with one query per sequence and ascending lists
+    case = (4, 1, 128, 576, 512, 3000, [3000, 2500, 900, 64], 512, "sorted")
+    _, _, dkv1, _ = _bwd_run(dsa, case, seed=78)
+    _, _, dkv3, _ = _bwd_run(dsa, case, seed=78, accumulate=True, dkv=dkv1.clone())
     assert torch.allclose(dkv3, 2 * dkv1, rtol=1e-4, atol=1e-6 * dkv1.abs().max().item())

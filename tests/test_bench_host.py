@@ -61,3 +61,16 @@ def test_recorded_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     assert bench.recorded_traffic(wl, "indexer") == 1024
     src.write_text("kernel v2\n")  # other source: the same
     assert bench.recorded_traffic(wl, "indexer") is None
+
+
+def test_backward_algorithmic_work():
+    """Five contractions per selected (query, key) pair and head; decode pairs are
+    B * K, prefill pairs follow the causal ramp (short rows keep every key)."""
+    import bench
+    from workloads import get
+    d = bench.bwd_algorithmic(get("decode_32k"))
+    assert d["pairs"] == 64 * 2048
+    assert d["flops"] == 2.0 * 64 * 2048 * 128 * (3 * 576 + 2 * 512)
+    p = bench.bwd_algorithmic(get("prefill_4k"))
+    assert p["pairs"] == sum(min(2048, t + 1) for t in range(4096))
+    assert p["flops"] / p["pairs"] == d["flops"] / d["pairs"]

@@ -180,17 +180,39 @@ class Case:
                     idx_out=self.idx, out=self.out, lse=self.lse, workspace=self.ws)
 
 
-def time_forward(dsa, torch, cases, steps, warmup):
+def capture_graphs(dsa, torch, cases):
+    """One HIP graph per input set holding that set's whole dsa_forward call (the
+    library's launches go to the capturing stream); None if capture fails."""
+    try:
+        graphs = []
+        for c in cases:
+            c.forward(dsa)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                c.forward(dsa)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
+    except Exception as e:  # noqa: BLE001 -- fall back to eager launches, say so in the output
+        print(f"graph capture failed, timing eager launches: {e}", file=sys.stderr)
+        return None
+
+
+def time_forward(dsa, torch, cases, steps, warmup, graphs=None):
+    """Average step time over `steps` steps (rotating the input sets) between two HIP
+    events on the launch stream; with graphs, each step replays its set's graph."""
     stream = torch.cuda.current_stream()
+    step = (lambda s: graphs[s % len(graphs)].replay()) if graphs else (lambda s: cases[s % len(cases)].forward(dsa))
     for s in range(warmup):
-        cases[s % len(cases)].forward(dsa)
+        step(s)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     t0 = time.perf_counter()
     for s in range(steps):
-        cases[s % len(cases)].forward(dsa)
+        step(s)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -458,7 +480,8 @@ def run(args) -> dict:
     n_sets = 3 if wl.n_q == 1 else 1
     cases = [Case(dsa, wl, seed, torch) for seed in range(n_sets)]
     torch.cuda.synchronize()
-    ms, wall = time_forward(dsa, torch, cases, steps, warmup)
+    graphs = capture_graphs(dsa, torch, cases) if args.graph else None
+    ms, wall = time_forward(dsa, torch, cases, steps, warmup, graphs)
     queries = wl.batch * wl.n_q
     res = {
         "metric": METRIC, "value": round(queries / (ms * 1e-3), 1), "unit": "queries/s", "n_gpus": 1,
@@ -471,6 +494,7 @@ def run(args) -> dict:
                    "qk_dim": wl.qk_dim, "v_dim": wl.v_dim, "idx_dtype": wl.idx_dtype, "mla_dtype": wl.mla_dtype,
                    "input_sets": n_sets},
         "wall_s": round(wall, 4),
+        "launch": "hip_graph" if graphs else "eager",
     }
     if not args.no_stages:
         st = time_stages(dsa, torch, cases, max(5, min(steps, 50)))
@@ -517,6 +541,7 @@ def main():
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the sparse MLA backward timing")
+    ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run plain device copies of BYTES bytes (counter calibration)")
     args = ap.parse_args()

@@ -21,10 +21,10 @@
 //           sum run over all key columns with dz in place of p:
 //           dq += dz . K (head rows, so a lane group writes 32 consecutive
 //           columns of one head), split lists add with fp32 atomics;
-//   dkv     per (query, split): wave w owns 32-column blocks of dk (waves 0-3,
-//           sm dz^T q) or dv (waves 4-7, p^T dO), contracts over the heads on
-//           32x32x16 MFMA per 32-entry tile and adds the block to the cache rows
-//           with fp32 atomics.
+//   dkv     per (query, split): for each 32-column block the key part
+//           (sm dz^T q) and, below Dv, the value part (p^T dO) contract over the
+//           heads into one accumulator on 32x32x16 MFMA per 32-entry tile, and
+//           the block is added to the cache rows with fp32 atomics.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -59,7 +59,6 @@ struct BwdCfg {
     static constexpr int VHALF = DV / 2, VSHARE = DV / 4, VS = VSHARE / 8;  // dO.v contraction split
     static constexpr int QT = HALF / 32;                                     // dq tiles of a wave half
     static constexpr int NBK = DQK / 32, NBV = DV / 32;                      // dkv column blocks
-    static constexpr int MAXB = (NBK > NBV ? NBK : NBV) / 4 + (((NBK > NBV ? NBK : NBV) % 4) ? 1 : 0);
     static_assert(DQK % 64 == 0 && DV % 64 == 0 && DV <= DQK && SHARE % 8 == 0 && VSHARE % 8 == 0, "shape");
 };
 
@@ -399,18 +398,23 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------- dkv
-// Per (query, split): wave w < 4 owns dk column blocks w, w + 4, ... (32 columns
-// each) and contracts sm dz^T [32 entries x heads] with q [heads x 32 columns];
-// wave w >= 4 owns dv blocks w - 4, w, ... with p^T and dO.  The block's q / dO
-// operands (head-minor rows from prep) stay in registers; per tile the A
-// operand is formed from the stored p (and dP and D for dz), and each lane adds
-// its 16 results (entries 8*i + 4*kb + jj, column `col`) to the cache rows with
-// atomics.
+// Per (query, split).  A value column c < DV of a cache row gets sm dz q (key part)
+// and p dO (value part); both contractions over the heads share one accumulator,
+// so each (entry, column) takes one atomic.  Main pass: wave w owns the 32-column
+// blocks w and w + 8 below DV with their q and dO operands (head-minor rows from
+// prep) in registers; per tile it forms its A operands, bf16 p and sm dz =
+// sm p (dP - D), for entry row `col` of the tile, runs both contractions on
+// 32x32x16 MFMA and adds each lane's 16 results (entries 8*i + 4*kb + jj, column
+// `col`) to the cache rows with fp32 atomics.  Second pass: the key-only blocks
+// (the rope columns at and past DV), tiles dealt round-robin over the waves.
 template <int DQK, int DV>
 __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdArgs a)
 {
     using C = BwdCfg<DQK, DV>;
     constexpr int HS = 8;  // 16-head steps: up to 128 heads
+    constexpr int NB = C::NBK, NV = C::NBV;
+    constexpr int NR = NB - NV;  // key-only blocks
+    static_assert(NV <= 16 && NR >= 1 && NR <= 2, "block split of the dkv kernel");
     __shared__ int32_t lsrc[kMaxList];
     __shared__ uint32_t lrow[kMaxList];
     __shared__ uint32_t tmask[kMaxList / kTK];
@@ -429,73 +433,104 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdArgs a)
     }
     __syncthreads();
 
-    const bool isk = w < 4;
-    const int wb = w & 3;
-    const int nb = isk ? C::NBK : C::NBV;
-    const uint16_t* opT = isk ? a.qT + (size_t)r * DQK * a.Hp : a.dT + (size_t)r * DV * a.Hp;
+    const uint16_t* qT = a.qT + (size_t)r * DQK * a.Hp;
+    const uint16_t* dT = a.dT + (size_t)r * DV * a.Hp;
     const float* srcp = a.P + (size_t)r * a.K * a.Hp;
     const float* srcd = a.DP + (size_t)r * a.K * a.Hp;
-    const float scale = isk ? a.sm : 1.f;
     const int hs = a.Hp / 16;
-    // B operands: block bi = wb + 4 * i, lane (column col, k-block kb) holds heads 16 s + 8 kb .. + 8
-    u32x4 bop[C::MAXB][HS];
-#pragma unroll
-    for (int i = 0; i < C::MAXB; ++i) {
-        const int blk = min(wb + 4 * i, nb - 1);
-#pragma unroll
-        for (int s = 0; s < HS; ++s)
-            bop[i][s] = s < hs ? ld16(opT + (size_t)(32 * blk + col) * a.Hp + 16 * s + 8 * kb) : u32x4{0u, 0u, 0u, 0u};
-    }
     float* dkvb = a.dkv + (size_t)u.b * a.Lmax * DQK;
-#pragma unroll 1
-    for (int it = 0; it < u.n_tiles; ++it) {
-        const int j0 = u.j_begin + it * kTK;
-        const uint32_t vm = tmask[it];
-        // A operand: entry row `col` of the tile, heads 16 s + 8 kb .. + 8: p for
-        // dv, dz = p (dP - D) for dk
-        const size_t ao = (size_t)min(j0 + col, a.K - 1) * a.Hp + 8 * kb;
-        u32x4 aop[HS];
+
+    // A operands of tile `it`: entry row `col`, heads 16 s + 8 kb .. + 8
+    auto load_a = [&](int it, u32x4 (&ap)[HS], u32x4 (&az)[HS], bool want_p) {
+        const size_t ao = (size_t)min(u.j_begin + it * kTK + col, a.K - 1) * a.Hp + 8 * kb;
 #pragma unroll
         for (int s = 0; s < HS; ++s) {
             if (s < hs) {
                 const u32x4 lo = ld16(srcp + ao + 16 * s), hi = ld16(srcp + ao + 16 * s + 4);
-                float x[8] = {__uint_as_float(lo[0]), __uint_as_float(lo[1]), __uint_as_float(lo[2]),
-                              __uint_as_float(lo[3]), __uint_as_float(hi[0]), __uint_as_float(hi[1]),
-                              __uint_as_float(hi[2]), __uint_as_float(hi[3])};
-                if (isk) {
-                    const u32x4 dlo = ld16(srcd + ao + 16 * s), dhi = ld16(srcd + ao + 16 * s + 4);
-                    const f32x4 D0 = *reinterpret_cast<const f32x4*>(&Ds[16 * s + 8 * kb]);
-                    const f32x4 D1 = *reinterpret_cast<const f32x4*>(&Ds[16 * s + 8 * kb + 4]);
+                const u32x4 dlo = ld16(srcd + ao + 16 * s), dhi = ld16(srcd + ao + 16 * s + 4);
+                const f32x4 D0 = *reinterpret_cast<const f32x4*>(&Ds[16 * s + 8 * kb]);
+                const f32x4 D1 = *reinterpret_cast<const f32x4*>(&Ds[16 * s + 8 * kb + 4]);
+                float pv[8], z[8];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        x[k] *= __uint_as_float(dlo[k]) - D0[k];
-                        x[4 + k] *= __uint_as_float(dhi[k]) - D1[k];
-                    }
+                for (int k = 0; k < 4; ++k) {
+                    pv[k] = __uint_as_float(lo[k]);
+                    pv[4 + k] = __uint_as_float(hi[k]);
+                    z[k] = a.sm * pv[k] * (__uint_as_float(dlo[k]) - D0[k]);
+                    z[4 + k] = a.sm * pv[4 + k] * (__uint_as_float(dhi[k]) - D1[k]);
                 }
-                aop[s] = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                               pack_bf16x2(x[6], x[7])};
+                if (want_p)
+                    ap[s] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                                  pack_bf16x2(pv[6], pv[7])};
+                az[s] = u32x4{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]), pack_bf16x2(z[4], z[5]),
+                              pack_bf16x2(z[6], z[7])};
             } else {
-                aop[s] = u32x4{0u, 0u, 0u, 0u};
+                ap[s] = u32x4{0u, 0u, 0u, 0u};
+                az[s] = u32x4{0u, 0u, 0u, 0u};
             }
         }
-        int rows[16];
+    };
+    // B operand of column block blk: lane (column col, k-block kb) holds heads 16 s + 8 kb .. + 8
+    auto load_b = [&](const uint16_t* opT, int blk, u32x4 (&bo)[HS]) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) rows[e] = lsrc[it * kTK + 8 * (e >> 2) + 4 * kb + (e & 3)];
+        for (int s = 0; s < HS; ++s)
+            bo[s] = s < hs ? ld16(opT + (size_t)(32 * blk + col) * a.Hp + 16 * s + 8 * kb) : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto add_rows = [&](int it, int blk, const f32x16& acc) {
+        const uint32_t vm = tmask[it];
 #pragma unroll
-        for (int i = 0; i < C::MAXB; ++i) {
-            const int blk = wb + 4 * i;
-            if (blk >= nb) break;
-            f32x16 acc;
+        for (int e = 0; e < 16; ++e) {
+            const int key = 8 * (e >> 2) + 4 * kb + (e & 3);
+            const int row = lsrc[it * kTK + key];
+            if (((vm >> key) & 1u) && row >= 0) unsafeAtomicAdd(dkvb + (size_t)row * DQK + 32 * blk + col, acc[e]);
+        }
+    };
+
+    {  // main pass: blocks w and w + 8 below DV, key and value parts together
+        u32x4 bq[2][HS], bv[2][HS];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+        for (int i = 0; i < 2; ++i) {
+            const int blk = min(w + 8 * i, NV - 1);
+            load_b(qT, blk, bq[i]);
+            load_b(dT, blk, bv[i]);
+        }
+#pragma unroll 1
+        for (int it = 0; it < u.n_tiles && w < NV; ++it) {
+            u32x4 ap[HS], az[HS];
+            load_a(it, ap, az, true);
 #pragma unroll
-            for (int s = 0; s < HS; ++s)
-                if (s < hs) acc = mfma32(aop[s], bop[i][s], acc);
+            for (int i = 0; i < 2; ++i) {
+                const int blk = w + 8 * i;
+                if (blk >= NV) break;
+                f32x16 acc;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int key = 8 * (e >> 2) + 4 * kb + (e & 3);
-                if (((vm >> key) & 1u) && rows[e] >= 0)
-                    unsafeAtomicAdd(dkvb + (size_t)rows[e] * DQK + 32 * blk + col, scale * acc[e]);
+                for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+                for (int s = 0; s < HS; ++s)
+                    if (s < hs) {
+                        acc = mfma32(az[s], bq[i][s], acc);
+                        acc = mfma32(ap[s], bv[i][s], acc);
+                    }
+                add_rows(it, blk, acc);
+            }
+        }
+    }
+    {  // second pass: key-only blocks, tiles dealt over the waves
+        u32x4 br[NR][HS];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) load_b(qT, NV + i, br[i]);
+#pragma unroll 1
+        for (int it = w; it < u.n_tiles; it += 8) {
+            u32x4 ap[HS], az[HS];
+            load_a(it, ap, az, false);
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                f32x16 acc;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+                for (int s = 0; s < HS; ++s)
+                    if (s < hs) acc = mfma32(az[s], br[i][s], acc);
+                add_rows(it, NV + i, acc);
             }
         }
     }

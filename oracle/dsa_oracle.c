@@ -23,8 +23,8 @@
  * hold the exact values the device receives (bf16 and fp32 values are exact
  * in float32; fp8 inputs arrive as codes plus float scales).
  *
- * Query t of sequence b sits at position p = kv_len[b] - T + t and may see
- * keys s = 0..p (itself included).
+ * Query t of sequence b sits at position p = L - T + t, L = min(kv_len[b], Lmax),
+ * and may see keys s = 0..p (itself included).
  *
  * Parity pins live in tests/test_oracle_*.py.
  */
@@ -211,6 +211,11 @@ void orc_quant(long rows, int D, const float* x, uint8_t* codes, float* scales)
 
 static long row_at(long i, const long* rows) { return rows ? rows[i] : i; }
 
+/* A sequence's length as the path reads it: kv_len[b] clamped to the cache
+ * capacity Lmax (a length past the cache cannot have cached keys), so a query
+ * never sees a position outside its sequence's cache rows. */
+static long seq_len(int kv_len, int Lmax) { return kv_len < Lmax ? (long)kv_len : (long)Lmax; }
+
 /* Lightning-indexer scores for the listed rows.
  *   q  [B, T, H, D]   w [B, T, H]   k [B, Lmax, D]   kv_len [B]
  *   out [n_rows, Lmax]: I[s] = sum_h w[h] * max(0, q[h] . k[s]) for s <= p,
@@ -224,7 +229,7 @@ void orc_index_scores(int B, int T, int Lmax, int H, int D,
     for (long i = 0; i < n_rows; ++i) {
         long r = row_at(i, rows);
         long b = r / T, t = r % T;
-        long p = (long)kv_len[b] - T + t;
+        long p = seq_len(kv_len[b], Lmax) - T + t;
         long qi = compact ? i : r;
         const float* qr = q + (size_t)qi * H * D;
         const float* wr = w + (size_t)qi * H;
@@ -264,7 +269,7 @@ void orc_index_scores_fp8(int B, int T, int Lmax, int H, int D,
     for (long i = 0; i < n_rows; ++i) {
         long r = row_at(i, rows);
         long b = r / T, t = r % T;
-        long p = (long)kv_len[b] - T + t;
+        long p = seq_len(kv_len[b], Lmax) - T + t;
         long qi = compact ? i : r;
         double* qd = (double*)malloc(sizeof(double) * (size_t)H * D);
         for (int h = 0; h < H; ++h)
@@ -321,7 +326,7 @@ void orc_topk(int B, int T, int Lmax, int K, const int* kv_len,
     for (long i = 0; i < n_rows; ++i) {
         long r = row_at(i, rows);
         long b = r / T, t = r % T;
-        long p = (long)kv_len[b] - T + t;
+        long p = seq_len(kv_len[b], Lmax) - T + t;
         long n = p + 1 > 0 ? p + 1 : 0; /* p < 0: no candidates */
         long keff = n < K ? n : K;
         cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
@@ -503,7 +508,7 @@ void orc_masked_dense_mla(int B, int T, int Lmax, int H, int Dqk, int Dv, int K,
     for (long i = 0; i < n_rows; ++i) {
         long r = row_at(i, rows);
         long b = r / T, t = r % T;
-        long p = (long)kv_len[b] - T + t;
+        long p = seq_len(kv_len[b], Lmax) - T + t;
         long n = p + 1 > 0 ? p + 1 : 0; /* p < 0: no candidates */
         const int* ir = idx + (size_t)i * K;
         const float* kvb = kv + (size_t)b * Lmax * Dqk;

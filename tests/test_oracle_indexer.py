@@ -174,3 +174,25 @@ def test_topk_invariant_under_positive_weight_scaling(orc):
     wi = rng.integers(-3, 4, (B, T, H)).astype(np.float32)
     b2 = orc.topk(orc.index_scores(qi, wi, ki, kl), kl, T, K)
     assert np.array_equal(orc.topk(orc.index_scores(qi, wi * 3, ki, kl), kl, T, K), b2)
+
+
+def test_lengths_past_the_cache_are_clamped_to_it(orc):
+    """A kv_len larger than the cache capacity reads as the capacity (reading R19: a
+    sequence cannot have keys past its cache rows): scores, top-k and the masked-dense
+    attention equal those of kv_len = Lmax, and no query sees a position >= Lmax."""
+    rng = np.random.default_rng(11)
+    B, T, H, D, L, K = 2, 3, 4, 16, 10, 6
+    q = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    k = rng.standard_normal((B, L, D)).astype(np.float32)
+    w = rng.standard_normal((B, T, H)).astype(np.float32)
+    long_ = np.array([L + 7, L], np.int32)
+    exact = np.array([L, L], np.int32)
+    s1, s2 = orc.index_scores(q, w, k, long_), orc.index_scores(q, w, k, exact)
+    assert np.array_equal(s1, s2)
+    i1, i2 = orc.topk(s1, long_, T, K), orc.topk(s2, exact, T, K)
+    assert np.array_equal(i1, i2) and i1.max() < L
+    qm = rng.standard_normal((B, T, 2, 24)).astype(np.float32)
+    kv = rng.standard_normal((B, L, 24)).astype(np.float32)
+    o1, l1 = orc.masked_dense_mla(qm, kv, long_, i1, 0.3, v_dim=16)
+    o2, l2 = orc.masked_dense_mla(qm, kv, exact, i2, 0.3, v_dim=16)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

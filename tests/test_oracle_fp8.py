@@ -182,3 +182,132 @@ def test_cache_append_touches_only_the_new_rows(orc):
                 assert np.array_equal(codes[b, p], nc[b, t]) and scales[b, p] == ns[b, t]
             else:
                 assert np.array_equal(codes[b, p], codes0[b, p]) and scales[b, p] == scales0[b, p]
+
+
+# ------------------------------------------------- exact rounding of the rotation
+# The rotated value of element i is (S x)_i / sqrt(D) with S the +-1 Sylvester
+# matrix.  The pins below compute it with exact integer / rational arithmetic and
+# round it to fp32 themselves (nearest, ties to even), so they fix the rounding of
+# every rotated element, not only its closeness.  S is built here by the Kronecker
+# recursion S_2D = [[S, S], [S, -S]] (the oracle uses the popcount formula).
+from fractions import Fraction
+import math
+
+
+def _sylvester_int(D):
+    S = np.array([[1]], dtype=object)
+    while S.shape[0] < D:
+        S = np.block([[S, S], [S, -S]])
+    return S
+
+
+def _exact_ints(row):
+    """row (fp32) -> (python ints n_j, e) with row[j] == n_j * 2**e exactly."""
+    parts = [math.frexp(float(v)) for v in row]
+    exps = [e - 24 for m, e in parts if m != 0.0]
+    e0 = min(exps) if exps else 0
+    return [int(m * (1 << 24)) << (e - 24 - e0) if m != 0.0 else 0 for m, e in parts], e0
+
+
+def _nearest_f32(cmp, approx):
+    """The fp32 value nearest to an exact value v known only through cmp(m) = sign(v - m)
+    for rational m; ties go to the even significand."""
+    c = np.float32(approx)
+    for _ in range(64):
+        up = np.nextafter(c, np.float32(np.inf))
+        dn = np.nextafter(c, np.float32(-np.inf))
+        hi = (Fraction(float(c)) + Fraction(float(up))) / 2
+        lo = (Fraction(float(dn)) + Fraction(float(c))) / 2
+        ch, cl = cmp(hi), cmp(lo)
+        if ch > 0:
+            c = up
+        elif cl < 0:
+            c = dn
+        elif ch == 0:
+            return c if int(c.view(np.uint32)) % 2 == 0 else up
+        elif cl == 0:
+            return c if int(c.view(np.uint32)) % 2 == 0 else dn
+        else:
+            return c
+    raise AssertionError("no convergence")
+
+
+def _sign(x):
+    return (x > 0) - (x < 0)
+
+
+def _exact_rotation(x):
+    """Correctly rounded fp32(S x / sqrt(D)) for every row of x, by exact arithmetic:
+    rationals when sqrt(D) is an integer, else v = A sqrt(2) with A rational, compared
+    with a rational m through the signs and squares of both sides."""
+    D = x.shape[-1]
+    S = _sylvester_int(D)
+    r = math.isqrt(D)
+    rational = r * r == D
+    c2 = math.isqrt(D // 2)  # D = 2 c2^2 otherwise: 1/sqrt(D) = sqrt(2) / (2 c2)
+    out = np.empty(x.shape, dtype=np.float32)
+    for i, row in enumerate(x):
+        n, e = _exact_ints(row)
+        sn = S.dot(np.array(n, dtype=object))
+        scale = Fraction(2) ** e
+        for k in range(D):
+            if rational:
+                v = Fraction(int(sn[k])) * scale / r
+                out[i, k] = _nearest_f32(lambda m, v=v: _sign(v - m), float(v))
+            else:
+                A = Fraction(int(sn[k])) * scale / (2 * c2)  # v = A sqrt(2)
+
+                def cmp(m, A=A):
+                    if A >= 0 and m <= 0:
+                        return 0 if (A == 0 and m == 0) else 1
+                    if A <= 0 and m >= 0:
+                        return -1
+                    d = 2 * A * A - m * m  # |v|^2 - |m|^2, same signs
+                    return _sign(d) if A > 0 else -_sign(d)
+
+                out[i, k] = _nearest_f32(cmp, float(A) * math.sqrt(2.0))
+    return out
+
+
+@pytest.mark.parametrize("D,rows", [(16, 100), (32, 100), (64, 64), (128, 48), (256, 24)])
+def test_rotation_is_correctly_rounded_fp32_of_the_exact_product(orc, D, rows):
+    """Every rotated element equals the correctly rounded fp32 of the exact H x (about
+    20K elements over the five widths): Gaussian rows, rows under lognormal scales, and
+    rows whose exact products land on fp32 midpoints (ties to even) where sqrt(D) is an
+    integer."""
+    rng = np.random.default_rng(40 + D)
+    x = rng.standard_normal((rows, D)) * np.exp(rng.normal(0.0, 2.0, (rows, 1)))
+    x = x.astype(np.float32)
+    if D in (16, 64, 256):
+        # 2^24 + small odd integers: (S x)_i / sqrt(D) falls halfway between fp32 values
+        x[0] = 0.0
+        x[0, 0], x[0, 1] = 2.0 ** 24, 1.0
+        x[1] = 0.0
+        x[1, 0], x[1, 1], x[1, 2] = 2.0 ** 24, 3.0, -2.0
+        x[2] = 0.0
+        x[2, 0], x[2, 3] = -(2.0 ** 25), 3.0
+    ref = _exact_rotation(x)
+    got = orc.rotate(x)
+    bad = np.nonzero(got.view(np.uint32) != ref.view(np.uint32))
+    assert bad[0].size == 0, f"{bad[0].size} elements differ, first at {bad[0][0]}, {bad[1][0]}"
+
+
+def test_rotate_quant_scale_and_codes_from_exact_arithmetic(orc):
+    """The quantiser's arithmetic (reading of the FP8 indexer): amax of the rotated row,
+    r = fp32(448 / amax), y = fp32(x' r), code = e4m3 round-to-nearest-even of y
+    (saturating), scale = fp32(amax / 448).  Recomputed here with exact rationals for
+    every rounding and torch's float8_e4m3fn cast (a library routine) for the codes."""
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((64, 128)) * np.exp(rng.normal(0.0, 1.5, (64, 1)))).astype(np.float32)
+    codes, scales = orc.rotate_quant(x)
+    xr = orc.rotate(x)  # pinned exactly above
+    for i in range(x.shape[0]):
+        amax = Fraction(float(np.abs(xr[i]).max()))
+        sc = _nearest_f32(lambda m: _sign(amax / 448 - m), float(amax) / 448.0)
+        assert scales[i] == sc, i
+        r = _nearest_f32(lambda m: _sign(448 / amax - m), 448.0 / float(amax))
+        y = np.array([_nearest_f32(lambda m, v=Fraction(float(v)) * Fraction(float(r)): _sign(v - m),
+                                   float(v) * float(r)) for v in xr[i]], dtype=np.float32)
+        y = np.clip(y, -448.0, 448.0)
+        ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(codes[i], ref), i

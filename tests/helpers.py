@@ -26,12 +26,20 @@ def announce(msg: str):
 
 
 def rel_rowmax(got, ref, axis=-1):
+    """Per-row max |got - ref| / max |ref| over the finite reference entries.  Every
+    reference entry must be finite or -inf; got must be finite exactly where ref is
+    and -inf exactly where ref is -inf (NaN or +inf in got fails)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     fin = np.isfinite(ref)
+    masked = ref == -np.inf
+    assert np.all(fin | masked), "reference holds NaN or +inf"
     assert np.array_equal(fin, np.isfinite(got)), "masked (-inf) pattern differs"
-    d = np.where(fin, np.abs(got - ref), 0.0).max(axis=axis)
-    m = np.where(fin, np.abs(ref), 0.0).max(axis=axis)
+    assert np.all(got[masked] == -np.inf), "masked entries are not -inf"
+    g = np.where(fin, got, 0.0)
+    r = np.where(fin, ref, 0.0)
+    d = np.abs(g - r).max(axis=axis)
+    m = np.abs(r).max(axis=axis)
     return np.where(m > 0, d / np.where(m > 0, m, 1.0), d)
 
 

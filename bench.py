@@ -1,6 +1,7 @@
 """DSA forward throughput on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode_32k|prefill_32k|decode_128k_fp8|...]
+    python bench.py [--steps K] [--warmup W] [--workload decode_32k|prefill_32k|decode_128k_fp8|...] [--single]
+    python bench.py --sweep-context     (stage times of bf16 decode, batch 16, context 4K..128K)
 
 A step is one dsa_forward call (fp8 workloads: q rotation + quantisation,
 index scores, top-k, sparse MLA) over one batch of synthetic inputs already
@@ -19,7 +20,11 @@ and report it against its own roofline ("mla_bwd"), outside the timed step.
 Prefill workloads also time the streaming indexer -> top-k entry point, which
 keeps per-row candidate lists instead of the score matrix ("index_topk_stream").
 The CPU oracle is timed on a bounded sample of the same workload on the host
-cores.
+cores, and on one thread over a smaller sample (CPU model named).
+
+The default run measures the three points of the metric in one process:
+decode_32k (the line's value), prefill_32k and decode_128k_fp8, each with its
+own roofline, stage fractions and oracle timing under "points".
 
 Prints one JSON line.
 """
@@ -412,34 +417,45 @@ def recorded_traffic(wl, stage: str):
 
 
 CPU_BUDGET_S = 10.0  # oracle work to time, at least (one pass is always completed)
+CPU_BUDGET_1T_S = 3.0  # single-thread oracle work to time, at least
 
 
-def cpu_baseline(wl) -> dict:
-    """The oracle, as it stands, on a bounded sample of the workload (host cores)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, budget_s: float = CPU_BUDGET_S) -> dict:
+    """The oracle, as it stands, on a bounded sample of the workload: on all host
+    threads (the reported value), then on one thread over a smaller sample."""
     import numpy as np
 
     import oracle
     from workloads import make_inputs
     oracle.build()
     threads = oracle.num_threads()
-    if wl.n_q == 1:
-        # every sequence of the batch, in repeated passes until the budget is spent
-        inp = make_inputs(wl)
-        rows = list(range(wl.batch))
+    inp = make_inputs(wl)
+
+    def decode_sample(n_seq, budget):
+        # the first n_seq sequences only (the oracle quantises the key caches it is given)
+        sub = {k: v[:n_seq] for k, v in inp.items()}
+        wsub = wl.replace(batch=n_seq)
+        rows = list(range(n_seq))
         passes, dt = 0, 0.0
-        while dt < CPU_BUDGET_S and dt < 30.0:
+        while dt < budget and dt < 3 * budget:
             t0 = time.perf_counter()
-            oracle.forward(inp, wl, rows=rows)
+            oracle.forward(sub, wsub, rows=rows)
             dt += time.perf_counter() - t0
             passes += 1
-        n = passes * wl.batch
-        sample = f"all {wl.batch} sequences (one decode query each, {wl.kv_len}-token context), {passes} passes"
-        used = min(threads, wl.batch)
-    else:
-        # uniformly drawn query rows, the count doubled until one run fills the budget
+        return passes * n_seq, dt, passes
+
+    def prefill_sample(n, budget, grow):
         rng = np.random.default_rng(0)
-        inp = make_inputs(wl)
-        n = min(wl.rows, max(2, threads))
         while True:
             rows = sorted(rng.choice(wl.rows, size=n, replace=False).tolist())
             flat = lambda t: t.reshape(wl.rows, *t.shape[2:])[rows]
@@ -447,13 +463,38 @@ def cpu_baseline(wl) -> dict:
             t0 = time.perf_counter()
             oracle.forward(cin, wl, rows=rows, compact=True)
             dt = time.perf_counter() - t0
-            if dt >= CPU_BUDGET_S or n >= wl.rows or dt * 2 > 30.0:
-                break
-            n = min(wl.rows, int(n * max(2.0, min(8.0, CPU_BUDGET_S / max(dt, 1e-3)))))
+            if not grow or dt >= budget or n >= wl.rows or dt * 2 > 3 * budget:
+                return n, dt
+            n = min(wl.rows, int(n * max(2.0, min(8.0, budget / max(dt, 1e-3)))))
+
+    if wl.n_q == 1:
+        # every sequence of the batch, in repeated passes until the budget is spent
+        n, dt, passes = decode_sample(wl.batch, budget_s)
+        sample = f"all {wl.batch} sequences (one decode query each, {wl.kv_len}-token context), {passes} passes"
+        if wl.idx_dtype == "fp8":
+            sample += "; the oracle rotates and quantises the whole index-key cache in every pass"
+        used = min(threads, wl.batch)
+    else:
+        # uniformly drawn query rows, the count raised until one run fills the budget
+        n, dt = prefill_sample(min(wl.rows, max(2, threads)), budget_s, True)
         sample = f"{n} uniformly drawn query rows of {wl.rows}"
         used = min(threads, n)
-    return {"value": round(n / dt, 3), "unit": "queries/s", "cores": used, "kind": "oracle", "sample": sample,
-            "seconds": round(dt, 2)}
+    res = {"value": round(n / dt, 3), "unit": "queries/s", "cores": used, "kind": "oracle", "sample": sample,
+           "seconds": round(dt, 2), "cpu_model": cpu_model(), "host_threads": threads}
+    # one thread: two sequences (decode) or a handful of rows (prefill)
+    oracle.set_num_threads(1)
+    try:
+        if wl.n_q == 1:
+            n1, dt1, _ = decode_sample(min(2, wl.batch), CPU_BUDGET_1T_S)
+            s1 = f"first {min(2, wl.batch)} sequences, repeated passes"
+        else:
+            n1, dt1 = prefill_sample(2, CPU_BUDGET_1T_S, False)
+            s1 = "2 uniformly drawn query rows"
+    finally:
+        oracle.set_num_threads(threads)
+    res["single_thread"] = {"value": round(n1 / dt1, 4), "unit": "queries/s", "seconds": round(dt1, 2),
+                            "sample": s1}
+    return res
 
 
 def copy_calibration(nbytes: int, reps: int) -> dict:
@@ -468,15 +509,54 @@ def copy_calibration(nbytes: int, reps: int) -> dict:
     return {"copy_bytes": nbytes, "reps": reps}
 
 
-def run(args) -> dict:
+SWEEP_BATCH = 16
+SWEEP_CONTEXTS = (4096, 8192, 16384, 32768, 65536, 131072)
+
+
+def sweep_context(args) -> dict:
+    """Per-query cost against context length (the O(L) -> O(index_topk) claim of the
+    DSA section, item 2): bf16 decode at a fixed batch of 16 sequences, stage times
+    of the indexer (linear in L), top-k and sparse MLA (flat once L >= index_topk)
+    for L = 4K .. 128K.  Three input sets per length, as in the decode benchmark."""
     import torch
 
     import sparse_attention_09_amd as dsa
     from workloads import get
 
-    wl = get(args.workload)
+    reps = args.steps or 50
+    rows = []
+    for L in SWEEP_CONTEXTS:
+        wl = get("decode_32k").replace(name=f"decode_b{SWEEP_BATCH}_{L // 1024}k", batch=SWEEP_BATCH, max_kv=L,
+                                       kv_len=L)
+        cases = [Case(dsa, wl, seed, torch) for seed in range(3)]
+        torch.cuda.synchronize()
+        ms, _ = time_forward(dsa, torch, cases, reps, args.warmup)
+        st = time_stages(dsa, torch, cases, reps)
+        rows.append({"context": L, "ms_per_step": round(ms, 4), "stages_us": {k: round(v, 2) for k, v in st.items()},
+                     "stages_frac": stage_fractions(wl, st)})
+        del cases
+        torch.cuda.empty_cache()
+    return {"sweep": "decode bf16, fixed batch, context length", "batch": SWEEP_BATCH, "topk": 2048,
+            "reps": reps, "rows": rows}
+
+
+# Metric points reported by one default run: L = 32K decode (the headline value),
+# L = 32K prefill and L = 128K decode with the fp8 indexer.
+POINTS = ("decode_32k", "prefill_32k", "decode_128k_fp8")
+
+
+def run_point(args, name: str, with_bwd: bool, cpu_budget: float) -> dict:
+    """Time one workload: the forward step, the stages and the extras."""
+    import torch
+
+    import sparse_attention_09_amd as dsa
+    from workloads import get
+
+    wl = get(name)
     steps = args.steps if args.steps is not None else DEFAULT_STEPS.get(wl.name, 20)
-    warmup = args.warmup
+    if wl.n_q > 1:
+        steps = min(steps, DEFAULT_STEPS.get(wl.name, steps))
+    warmup = args.warmup if wl.n_q == 1 else min(args.warmup, 3)
     n_sets = 3 if wl.n_q == 1 else 1
     cases = [Case(dsa, wl, seed, torch) for seed in range(n_sets)]
     torch.cuda.synchronize()
@@ -484,11 +564,8 @@ def run(args) -> dict:
     ms, wall = time_forward(dsa, torch, cases, steps, warmup, graphs)
     queries = wl.batch * wl.n_q
     res = {
-        "metric": METRIC, "value": round(queries / (ms * 1e-3), 1), "unit": "queries/s", "n_gpus": 1,
-        "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None,
+        "value": round(queries / (ms * 1e-3), 1), "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
         "dtype": wl.mla_dtype if "fp8" not in (wl.idx_dtype, wl.mla_dtype) else "fp8+bf16",
-        "data": "synthetic (seeded Gaussian, DeepSeek-V3.2 shapes)",
         "config": {"workload": wl.name, "batch": wl.batch, "queries_per_seq": wl.n_q, "context": wl.kv_len,
                    "index_heads": wl.idx_heads, "index_dim": wl.idx_dim, "topk": wl.topk, "heads": wl.heads,
                    "qk_dim": wl.qk_dim, "v_dim": wl.v_dim, "idx_dtype": wl.idx_dtype, "mla_dtype": wl.mla_dtype,
@@ -521,14 +598,37 @@ def run(args) -> dict:
                                  "frac": round(gbs / PEAK_HBM_GBS, 4), "work_per_launch": nbytes}
     if wl.n_q > 2 and not args.no_stages:
         res["index_topk_stream"] = time_index_topk(dsa, torch, cases[0], max(3, min(steps, 20)))
-    if not args.no_bwd:
+    if with_bwd and not args.no_bwd:
         bwd = time_mla_bwd(dsa, torch, cases[0], 20 if wl.n_q == 1 else 3)
         if bwd is not None:
             res["mla_bwd"] = bwd
-    del cases
+    del cases, graphs
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl)
+        res["cpu_baseline"] = cpu_baseline(wl, cpu_budget)
+    return res
+
+
+def run(args) -> dict:
+    head = run_point(args, args.workload, True, CPU_BUDGET_S)
+    res = {"metric": METRIC, "value": head["value"], "unit": "queries/s", "n_gpus": 1, "steps": head["steps"],
+           "warmup": head["warmup"], "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"],
+           "data": "synthetic (seeded Gaussian, DeepSeek-V3.2 shapes)"}
+    res.update({k: v for k, v in head.items() if k not in res and k not in ("value", "steps", "warmup")})
+    if args.points and not args.single:
+        # the other L = 32K / 128K points of the metric, each with its own roofline
+        pts = {args.workload: {k: head[k] for k in ("value", "ms_per_step", "stages_us", "stages_frac", "roofline")
+                               if k in head}}
+        for name in POINTS:
+            if name == args.workload:
+                continue
+            p = run_point(args, name, False, CPU_BUDGET_S / 2)
+            keep = ("value", "ms_per_step", "steps", "dtype", "config", "stages_us", "stages_frac", "roofline",
+                    "cache_append", "index_topk_stream", "cpu_baseline")
+            pts[name] = {k: p[k] for k in keep if k in p}
+            pts[name]["unit"] = "queries/s"
+        res["points"] = pts
     return res
 
 
@@ -542,6 +642,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the sparse MLA backward timing")
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
+    ap.add_argument("--single", action="store_true", help="time only --workload, not the other metric points")
+    ap.add_argument("--sweep-context", action="store_true",
+                    help="only time the stages of bf16 decode at a fixed batch over context lengths 4K..128K")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run plain device copies of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -549,6 +652,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    args.points = args.workload in POINTS
+    if args.sweep_context:
+        print(json.dumps(sweep_context(args)), flush=True)
+        return
     if args.copy_calibration:
         print(json.dumps(copy_calibration(args.copy_calibration, args.steps or 3)), flush=True)
         return

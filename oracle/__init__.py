@@ -49,6 +49,8 @@ def _load():
             L = ctypes.c_long
             D = ctypes.c_double
             lib.orc_num_threads.restype = I
+            lib.orc_set_num_threads.argtypes = [I]
+            lib.orc_set_num_threads.restype = None
             lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
             lib.orc_e4m3_decode.restype = D
             lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
@@ -107,6 +109,11 @@ def _p(a: np.ndarray):
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the oracle's following calls (for timing it)."""
+    _load().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- fp8 codec

@@ -36,6 +36,9 @@
 
 int orc_num_threads(void) { return omp_get_max_threads(); }
 
+/* Threads of the following parallel loops (timing of the oracle only). */
+void orc_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* ------------------------------------------------------------------ */
 /* OCP FP8 E4M3FN codec (sign, 4 exponent bits with bias 7, 3 mantissa */
 /* bits; no infinities; 0x7F / 0xFF are NaN; largest finite 448).       */

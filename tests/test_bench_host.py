@@ -74,3 +74,12 @@ def test_backward_algorithmic_work():
     p = bench.bwd_algorithmic(get("prefill_4k"))
     assert p["pairs"] == sum(min(2048, t + 1) for t in range(4096))
     assert p["flops"] / p["pairs"] == d["flops"] / d["pairs"]
+
+
+def test_default_run_covers_the_metric_points():
+    import bench
+    from workloads import get
+    assert set(bench.POINTS) == {"decode_32k", "prefill_32k", "decode_128k_fp8"}
+    ctx = {get(n).kv_len for n in bench.POINTS}
+    assert ctx == {32768, 131072}
+    assert bench.SWEEP_CONTEXTS[0] <= 4096 and bench.SWEEP_CONTEXTS[-1] >= 131072

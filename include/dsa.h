@@ -62,7 +62,8 @@ typedef enum {
     DSA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                    */
     DSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required             */
     DSA_ERR_UNSUPPORTED = -6, /* valid but not built (a head width, a head count)    */
-    DSA_ERR_HIP = -7          /* the HIP runtime reported an error on launch         */
+    DSA_ERR_HIP = -7,         /* the HIP runtime reported an error on launch         */
+    DSA_ERR_SCRATCH = -8      /* dsa_forward_noalloc: needs more than its scratch    */
 } dsa_status;
 
 /* Problem description.  Dtype fields hold dsa_dtype values. */
@@ -258,6 +259,32 @@ dsa_status dsa_forward(const dsa_shape* shape, const void* q_idx, const float* w
                        const void* k_idx, const float* k_scale, const void* q, const void* kv,
                        const int32_t* kv_len, int32_t* idx_out, void* out, float* lse,
                        void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* dsa_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  It computes exactly what dsa_forward computes, with
+ * the same kernels and the same query chunking, on a workspace that the library
+ * holds: one static device array of DSA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU,
+ * kept from the library's first use on that GPU until the process ends.  The
+ * call itself allocates nothing (no hipMalloc, no allocating library routine);
+ * the caller still owns every input and output.
+ *   Arguments as for dsa_forward, without workspace / ws_bytes; stream must
+ *   belong to the current device (whose scratch is used).
+ *   Shapes whose smallest dsa_forward workspace (dsa_forward_min_workspace_size,
+ *   or its idx_out == NULL variant) exceeds the scratch are rejected on the host
+ *   with DSA_ERR_SCRATCH before anything is enqueued; the DeepSeek-V3.2 decode
+ *   shapes (64 x 32K bf16, 16 x 128K fp8) run in one pass, larger prefill in
+ *   query chunks.
+ *   Every call on one GPU uses that GPU's one scratch array: calls that overlap
+ *   on a GPU (concurrent streams, or threads enqueueing at once) race on it and
+ *   must be ordered by the caller.  Everything that must start at zero is
+ *   cleared by the call's own kernels; the array keeps the last call's contents.
+ *   Other errors as for dsa_forward. */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dsa_status dsa_forward_noalloc(const dsa_shape* shape, const void* q_idx, const float* w,
+                               const void* k_idx, const float* k_scale, const void* q, const void* kv,
+                               const int32_t* kv_len, int32_t* idx_out, void* out, float* lse,
+                               hipStream_t stream);
 
 /* Static text for a status value. */
 const char* dsa_status_string(dsa_status status);

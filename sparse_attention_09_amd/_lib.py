@@ -20,13 +20,15 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 _DT = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
 
 STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_DTYPE", -4: "DSA_ERR_ALIGN",
-          -5: "DSA_ERR_WORKSPACE", -6: "DSA_ERR_UNSUPPORTED", -7: "DSA_ERR_HIP"}
+          -5: "DSA_ERR_WORKSPACE", -6: "DSA_ERR_UNSUPPORTED", -7: "DSA_ERR_HIP",
+          -8: "DSA_ERR_SCRATCH"}
 
 EXPORTS = ["dsa_index_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_workspace_size",
            "dsa_sparse_mla_fwd", "dsa_rotate_quant_fp8", "dsa_index_cache_append_fp8", "dsa_forward_workspace_size",
            "dsa_mla_kv_quant_fp8", "dsa_forward_min_workspace_size", "dsa_forward", "dsa_status_string",
            "dsa_sparse_mla_bwd_workspace_size", "dsa_sparse_mla_bwd_min_workspace_size", "dsa_sparse_mla_bwd",
-           "dsa_index_topk_workspace_size", "dsa_index_topk_min_workspace_size", "dsa_index_topk"]
+           "dsa_index_topk_workspace_size", "dsa_index_topk_min_workspace_size", "dsa_index_topk",
+           "dsa_forward_noalloc"]
 
 
 class DsaError(RuntimeError):
@@ -97,6 +99,7 @@ def lib() -> ctypes.CDLL:
             "dsa_forward_workspace_size": ([SP], SZ),
             "dsa_forward_min_workspace_size": ([SP], SZ),
             "dsa_forward": ([SP, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+            "dsa_forward_noalloc": ([SP, P, P, P, P, P, P, P, P, P, P, P], I32),
             "dsa_status_string": ([I32], ctypes.c_char_p),
         }
         for name, (args, res) in sig.items():
@@ -319,4 +322,22 @@ def forward(shape: DsaShape, q_idx, w, k_idx, q, kv, kv_len, k_scale=None, idx_o
     _check("dsa_forward", lib().dsa_forward(ctypes.byref(cs), _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale),
                                             _ptr(q), _ptr(kv), _ptr(kv_len), _ptr(idx_out), _ptr(out), _ptr(lse),
                                             _ptr(workspace), workspace.numel(), _stream(stream)))
+    return idx_out, out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # DSA_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(shape: DsaShape, q_idx, w, k_idx, q, kv, kv_len, idx_out, out, lse=None, k_scale=None,
+                    stream=None):
+    """dsa_forward_noalloc: the whole path on the library's static scratch; the caller
+    passes every output (this wrapper allocates nothing either)."""
+    if shape.idx_dtype == "fp8":
+        k_idx = _view_u8(k_idx)
+    if shape.mla_dtype == "fp8":
+        kv = _view_u8(kv)
+    cs = shape.c()
+    _check("dsa_forward_noalloc",
+           lib().dsa_forward_noalloc(ctypes.byref(cs), _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q),
+                                     _ptr(kv), _ptr(kv_len), _ptr(idx_out), _ptr(out), _ptr(lse), _stream(stream)))
     return idx_out, out, lse

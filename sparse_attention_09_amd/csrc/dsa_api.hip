@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dsa.h"
 #include "dsa_kernels.h"
 
@@ -302,6 +304,7 @@ DSA_EXPORT const char* dsa_status_string(dsa_status st)
         case DSA_ERR_WORKSPACE: return "workspace missing or too small";
         case DSA_ERR_UNSUPPORTED: return "sizes valid but not supported by the built kernels";
         case DSA_ERR_HIP: return "HIP runtime error on launch";
+        case DSA_ERR_SCRATCH: return "shape needs more than the library's static scratch (dsa_forward_noalloc)";
     }
     return "unknown status";
 }
@@ -550,10 +553,12 @@ DSA_EXPORT size_t dsa_forward_min_workspace_size(const dsa_shape* s)
     return min_forward_ws(s, true);
 }
 
-DSA_EXPORT dsa_status dsa_forward(const dsa_shape* s, const void* q_idx, const float* w, const void* k_idx,
-                                  const float* k_scale, const void* q, const void* kv, const int32_t* kv_len,
-                                  int32_t* idx_out, void* out, float* lse, void* workspace, size_t ws_bytes,
-                                  hipStream_t stream)
+namespace {
+
+// Argument checks of dsa_forward other than the workspace.
+dsa_status check_forward_args(const dsa_shape* s, const void* q_idx, const float* w, const void* k_idx,
+                              const float* k_scale, const void* q, const void* kv, const int32_t* kv_len,
+                              const int32_t* idx_out, const void* out, const float* lse)
 {
     DSA_TRY(check_forward_shape(s));
     DSA_TRY(ptr_ok(q_idx, 16));
@@ -566,9 +571,15 @@ DSA_EXPORT dsa_status dsa_forward(const dsa_shape* s, const void* q_idx, const f
     if (s->idx_dtype == DSA_FP8_E4M3) DSA_TRY(ptr_ok(k_scale, 4));
     if (idx_out && !aligned(idx_out, 4)) return DSA_ERR_ALIGN;
     if (lse && !aligned(lse, 4)) return DSA_ERR_ALIGN;
-    if (!workspace) return DSA_ERR_WORKSPACE;
-    if (!aligned(workspace, kAlign)) return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
 
+// The launch sequence of dsa_forward on a checked, 256-byte aligned workspace.
+dsa_status forward_run(const dsa_shape* s, const void* q_idx, const float* w, const void* k_idx,
+                       const float* k_scale, const void* q, const void* kv, const int32_t* kv_len,
+                       int32_t* idx_out, void* out, float* lse, void* workspace, size_t ws_bytes,
+                       hipStream_t stream)
+{
     const bool own_idx = idx_out == nullptr;
     // largest query chunk whose workspace fits
     int tc = s->n_q;
@@ -618,4 +629,60 @@ DSA_EXPORT dsa_status dsa_forward(const dsa_shape* s, const void* q_idx, const f
         if (dsa::launch_mla(s->mla_dtype, ma, stream) != hipSuccess) return DSA_ERR_HIP;
     }
     return DSA_OK;
+}
+
+// ------------------------------------------------------------ static scratch
+// The workspace of dsa_forward_noalloc: one file-scope device array, of which
+// every GPU that runs the library holds its own copy until the process ends.
+// Host code never uses the array's name as an address (on the host it is only a
+// stand-in for the symbol): the device address of the current GPU's copy comes
+// from hipGetSymbolAddress, looked up once per device and kept here.
+constexpr size_t kScratchBytes = DSA_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % kAlign == 0, "scratch size");
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (the symbol lookup runs once per
+// device, under the lock, with that device current).
+dsa_status device_scratch(void** ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DSA_ERR_HIP;
+        if (!aligned(p, kAlign)) return DSA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return DSA_OK;
+}
+
+}  // namespace
+
+DSA_EXPORT dsa_status dsa_forward(const dsa_shape* s, const void* q_idx, const float* w, const void* k_idx,
+                                  const float* k_scale, const void* q, const void* kv, const int32_t* kv_len,
+                                  int32_t* idx_out, void* out, float* lse, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream)
+{
+    DSA_TRY(check_forward_args(s, q_idx, w, k_idx, k_scale, q, kv, kv_len, idx_out, out, lse));
+    if (!workspace) return DSA_ERR_WORKSPACE;
+    if (!aligned(workspace, kAlign)) return DSA_ERR_ALIGN;
+    return forward_run(s, q_idx, w, k_idx, k_scale, q, kv, kv_len, idx_out, out, lse, workspace, ws_bytes, stream);
+}
+
+DSA_EXPORT dsa_status dsa_forward_noalloc(const dsa_shape* s, const void* q_idx, const float* w, const void* k_idx,
+                                          const float* k_scale, const void* q, const void* kv,
+                                          const int32_t* kv_len, int32_t* idx_out, void* out, float* lse,
+                                          hipStream_t stream)
+{
+    DSA_TRY(check_forward_args(s, q_idx, w, k_idx, k_scale, q, kv, kv_len, idx_out, out, lse));
+    if (min_forward_ws(s, idx_out == nullptr) > kScratchBytes) return DSA_ERR_SCRATCH;
+    void* ws = nullptr;
+    DSA_TRY(device_scratch(&ws));
+    return forward_run(s, q_idx, w, k_idx, k_scale, q, kv, kv_len, idx_out, out, lse, ws, kScratchBytes, stream);
 }

@@ -60,7 +60,7 @@ def _call_scores(dsa, shape, q=FAKE, w=FAKE, k=FAKE, kl=FAKE, out=FAKE, qs=None,
 
 def test_status_strings(dsa):
     L = dsa.lib()
-    for st in range(0, -8, -1):
+    for st in range(0, -9, -1):
         assert L.dsa_status_string(st)
     assert L.dsa_status_string(-99) == b"unknown status"
 
@@ -247,3 +247,43 @@ def test_index_topk_rejects_bad_arguments(dsa):
     cap = max(4 * 64, 64 + 64)
     assert full >= 2 * 4 * cap * 8 and small >= 2 * cap * 8 and small < full
     assert dsa.index_topk_workspace_size(_shape(dsa, topk=0)) == 0
+
+
+def test_forward_noalloc_rejects_on_the_host(dsa):
+    """dsa_forward_noalloc checks its arguments as dsa_forward does and rejects a shape
+    whose smallest workspace exceeds the static scratch with DSA_ERR_SCRATCH, all
+    before any GPU call (these run without a GPU)."""
+    from workloads import WORKLOADS
+    L = dsa.lib()
+    f = L.dsa_forward_noalloc
+    assert L.dsa_status_string(-8)
+    args = [FAKE] * 7  # q_idx, w, k_idx, k_scale, q, kv, kv_len
+
+    def call(shape, a=args, idx=FAKE, out=FAKE, lse=FAKE):
+        return f(ctypes.byref(shape.c()), *a, idx, out, lse, None)
+
+    assert f(None, *args, FAKE, FAKE, FAKE, None) == -1
+    s = dsa.DsaShape.of(WORKLOADS["decode_32k"])
+    bad = list(args)
+    bad[0] = None
+    assert call(s, a=bad) == -1
+    assert call(s, out=None) == -1
+    bad = list(args)
+    bad[4] = FAKE + 8  # q
+    assert call(s, a=bad) == -4
+    z = dsa.DsaShape.of(WORKLOADS["decode_32k"])
+    z.heads = 0
+    assert call(z) == -2
+    # one decode query per sequence cannot be chunked: 64 rows of 2^20 scores need 256 MiB
+    big = dsa.DsaShape.of(WORKLOADS["decode_32k"])
+    big.max_kv = 1 << 20
+    assert dsa.forward_min_workspace_size(big) > dsa.NOALLOC_SCRATCH_BYTES
+    assert call(big) == -8
+    # the fp8 MLA quantises every query before the chunk loop: 2.4 GB of codes at prefill_32k
+    p = dsa.DsaShape.of(WORKLOADS["prefill_32k"])
+    p.mla_dtype = "fp8"
+    assert call(p) == -8
+    # the decode workloads fit the scratch in one pass (the checks above stop before it)
+    for name in ("decode_32k", "decode_128k_fp8", "decode_128k_fp8_mla"):
+        s = dsa.DsaShape.of(WORKLOADS[name])
+        assert dsa.forward_workspace_size(s) <= dsa.NOALLOC_SCRATCH_BYTES, name

@@ -220,7 +220,10 @@ dsa_status dsa_mla_kv_quant_fp8(int64_t rows, int32_t dim, const void* x, int32_
  *   dq  [B,T,H,D_qk] f32 out (every row written).
  *   dkv [B,L_max,D_qk] f32: cleared first unless accumulate_dkv != 0, in which
  *       case the gradients are added to what it holds (fp32 atomics: the order of
- *       the additions, and so the last bits, vary from run to run).
+ *       the additions, and so the last bits, vary from run to run).  When the call
+ *       clears dkv, T == 1 and every query's valid entries are strictly increasing
+ *       with skipped entries only after them (top-k's layout), each touched word
+ *       receives one update and is stored directly: dkv is then bit-reproducible.
  *   workspace (256-byte aligned): dsa_sparse_mla_bwd_workspace_size(shape) bytes
  *   run every query in one pass; any size >= dsa_sparse_mla_bwd_min_workspace_size
  *   works, the queries then being processed in the largest chunk of ceil(T / 2^k)

@@ -522,6 +522,7 @@ DSA_EXPORT dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const void* q, cons
         a.t_begin = t0;
         a.t_count = (s->n_q - t0) < tc ? (s->n_q - t0) : tc;
         a.n_split = dsa::mla_split_count(s->batch, a.t_count, s->heads, s->topk);
+        a.accumulate = accumulate_dkv ? 1 : 0;
         a.sm = s->sm_scale;
         a.q = (const uint16_t*)q;
         a.kv = (const uint16_t*)kv;

@@ -80,6 +80,7 @@ size_t topk_zero_words(const TopkArgs& a);
 struct MlaBwdArgs {
     int B, T, Lmax, H, Hp, K, Dqk, Dv;
     int t_begin, t_count, n_split;
+    int accumulate;         // dkv holds earlier gradients (else the call cleared it)
     float sm;
     const uint16_t* q;      // [B,T,H,Dqk] bf16
     const uint16_t* kv;     // [B,Lmax,Dqk] bf16

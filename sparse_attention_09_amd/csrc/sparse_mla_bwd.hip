@@ -24,7 +24,9 @@
 //   dkv     per (query, split): for each 32-column block the key part
 //           (sm dz^T q) and, below Dv, the value part (p^T dO) contract over the
 //           heads into one accumulator on 32x32x16 MFMA per 32-entry tile, and
-//           the block is added to the cache rows with fp32 atomics.
+//           the block is added to the cache rows with fp32 atomics, or stored when
+//           the call cleared dkv and no two (query, entry) pairs share a row (one
+//           query per sequence, strictly increasing list).
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -431,7 +433,27 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdArgs a)
         for (int s = 0; s < a.n_split; ++s) d += a.Dd[((size_t)r * a.n_split + s) * a.Hp + tid];
         Ds[tid] = d;
     }
-    __syncthreads();
+    // Exclusive rows: with one query per sequence, and the query's whole list made
+    // of strictly increasing valid entries followed only by skipped ones (top-k's
+    // layout), every cache row gets one update from one lane in the whole call.  When
+    // dkv was cleared by this call, the blocks are then stored instead of added with
+    // atomics (with accumulation the atomics stay: a load before each store would
+    // make the wave wait on memory, which the no-return atomics do not).  Every
+    // workgroup of the query reads the same list and so takes the same path.
+    bool viol = a.T != 1 || a.accumulate;
+    if (!viol) {
+        const int32_t* full = a.idx + u.grow * a.K;
+        for (int i = tid; i < a.K; i += 512) {
+            const int s1 = full[i];
+            const bool v1 = s1 >= 0 && s1 < u.L;
+            if (i > 0 && v1) {
+                const int s0 = full[i - 1];
+                const bool v0 = s0 >= 0 && s0 < u.L;
+                if (!v0 || s0 >= s1) viol = true;
+            }
+        }
+    }
+    const bool excl = !__syncthreads_or(viol);
 
     const uint16_t* qT = a.qT + (size_t)r * DQK * a.Hp;
     const uint16_t* dT = a.dT + (size_t)r * DV * a.Hp;
@@ -477,6 +499,15 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdArgs a)
     };
     auto add_rows = [&](int it, int blk, const f32x16& acc) {
         const uint32_t vm = tmask[it];
+        if (excl) {  // every word of these rows is this lane's alone, and dkv was cleared: store
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int key = 8 * (e >> 2) + 4 * kb + (e & 3);
+                const int row = lsrc[it * kTK + key];
+                if (((vm >> key) & 1u) && row >= 0) dkvb[(size_t)row * DQK + 32 * blk + col] = acc[e];
+            }
+            return;
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int key = 8 * (e >> 2) + 4 * kb + (e & 3);

@@ -214,7 +214,11 @@ def _mla_case(B, T, H, Dqk, Dv, Lmax, lens, K, dt, seed, kind="topk"):
             p = lens[b] - T + t
             n = max(0, min(K, p + 1))
             perm = torch.randperm(max(p + 1, 1), generator=g)[:n]
-            idx[b, t, :n] = (perm.sort().values if kind == "sorted" else perm).int()
+            idx[b, t, :n] = (perm.sort().values if kind.startswith("sorted") else perm).int()
+            if kind == "sorted_dup" and n >= 4:
+                idx[b, t, 2] = idx[b, t, 1]          # adjacent duplicate in an ascending list
+            if kind == "sorted_gap" and n >= 4:
+                idx[b, t, 2] = -1                    # a skipped entry before valid ones
             if kind in ("messy", "poison") and K >= 8:
                 idx[b, t, 0] = idx[b, t, 1]          # a duplicate
                 idx[b, t, 2] = lens[b] + 5           # out of range -> skipped
@@ -405,9 +409,13 @@ MLA_BWD_CASES = [
     (3, 2, 128, 576, 512, 80, [80, 0, 1], 32, "poison"),         # an empty sequence, NaN rows past kv_len
     (2, 3, 128, 576, 512, 500, [500, 2], 100, "messy"),          # K not a multiple of 32; a query before the cache
     (1, 70, 96, 576, 512, 4096, [4096], 1000, "topk"),           # two list splits of a long list, 96 heads
-    # one query per sequence, ascending lists (top-k's layout)
+    # one query per sequence, ascending lists (top-k's layout): rows updated with plain stores
     (4, 1, 128, 576, 512, 4096, [4096, 3000, 2048, 700], 2048, "sorted"),
     (3, 1, 20, 192, 128, 600, [600, 1, 0], 128, "sorted"),
+    # one query per sequence whose list repeats or skips rows mid-list: atomics again
+    (3, 1, 128, 576, 512, 2000, [2000, 1500, 40], 512, "messy"),
+    (2, 1, 128, 576, 512, 3000, [3000, 2000], 1024, "sorted_dup"),
+    (2, 1, 128, 576, 512, 3000, [3000, 2000], 1024, "sorted_gap"),
 ]
 
 

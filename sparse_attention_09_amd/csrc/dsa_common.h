@@ -53,6 +53,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Raw buffer accesses (no stride) through a descriptor whose record count bounds
+// them: a load at or past the end returns zero, a store there is dropped, with no
+// branch.  Offsets are bytes; kDropOffset lies past every record count used.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+constexpr int kDropOffset = 0x7FFFFFF0;
+
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(buf_rsrc r, int off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_ld4(buf_rsrc r, int off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+__device__ __forceinline__ void buf_st4(buf_rsrc r, int off, uint32_t v) { __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0); }
+__device__ __forceinline__ void buf_st8(buf_rsrc r, int off, uint32_t lo, uint32_t hi)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, r, off, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),

@@ -2,6 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload decode_32k|prefill_32k|decode_128k_fp8|...] [--single]
     python bench.py --sweep-context     (stage times of bf16 decode, batch 16, context 4K..128K)
+    python bench.py --mfma-ceiling      (sustained bf16 MFMA rate, constant and random operands)
 
 A step is one dsa_forward call (fp8 workloads: q rotation + quantisation,
 index scores, top-k, sparse MLA) over one batch of synthetic inputs already
@@ -497,6 +498,27 @@ def cpu_baseline(wl, budget_s: float = CPU_BUDGET_S) -> dict:
     return res
 
 
+def mfma_ceiling() -> dict:
+    """Sustained bf16 MFMA rate of this GPU on constant and on random operands
+    (mfma_ceiling.hip beside this file, built with hipcc and run as a child
+    process), the context for the MFMA fractions of the published peak."""
+    import subprocess
+    here = os.path.dirname(os.path.abspath(__file__))
+    out_dir = os.path.join(here, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    exe = os.path.join(out_dir, "mfma_ceiling")
+    cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", exe,
+           os.path.join(here, "mfma_ceiling.hip")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for mfma_ceiling.hip:\n" + r.stderr)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        raise RuntimeError("mfma_ceiling failed:\n" + r.stderr)
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def copy_calibration(nbytes: int, reps: int) -> dict:
     """Plain device-to-device copies of a known size, for calibrating HBM counters."""
     import torch
@@ -645,6 +667,8 @@ def main():
     ap.add_argument("--single", action="store_true", help="time only --workload, not the other metric points")
     ap.add_argument("--sweep-context", action="store_true",
                     help="only time the stages of bf16 decode at a fixed batch over context lengths 4K..128K")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only measure the sustained bf16 MFMA rate (constant and random operands)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run plain device copies of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -655,6 +679,9 @@ def main():
     args.points = args.workload in POINTS
     if args.sweep_context:
         print(json.dumps(sweep_context(args)), flush=True)
+        return
+    if args.mfma_ceiling:
+        print(json.dumps(mfma_ceiling()), flush=True)
         return
     if args.copy_calibration:
         print(json.dumps(copy_calibration(args.copy_calibration, args.steps or 3)), flush=True)

@@ -5,8 +5,10 @@
 // v_mfma_f32_16x16x32_bf16) for a fixed number of iterations, at two waves per
 // SIMD, with operands that are either the same bits every time or drawn at
 // random (uniform in [-1, 1]) and rotated so that every MFMA sees new bits, as
-// real data does.  The matrix units draw more power on changing operands, so the
-// clock, and with it the sustained rate, is lower for the second kind.  Only each
+// real data does; the sustained rate depends on the operand values, not only on
+// the instruction count.  The "vmix" cases follow every MFMA with n independent
+// fma instructions (on small structured operands, in a fixed MFMA / VALU issue
+// order) to measure how many other vector instructions an MFMA hides.  Only each
 // thread's final sum is stored.  Prints one JSON line.
 //
 // Build and run (bench.py --mfma-ceiling does both):
@@ -85,6 +87,84 @@ __global__ __launch_bounds__(256, 2) void mfma16_kernel(const bf16x8* ops, float
     out[blockIdx.x * 256 + threadIdx.x] = r;
 }
 
+// n fma instructions after every MFMA, in the order MFMA, n VALU, MFMA, ...
+template <int NV>
+__global__ __launch_bounds__(256, 2) void vmix16_kernel(const bf16x8* ops, float* out, int iters)
+{
+    (void)ops;
+    bf16x8 a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(threadIdx.x * 0.001f + i);
+        b[i] = (__bf16)(1.f + i);
+    }
+    f32x4 acc[8];
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        x[j] = threadIdx.x * 0.5f + j;
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < NV; ++u) x[(j * NV + u) & 7] = fmaf(x[(j * NV + u) & 7], 0.999f, 1.f);
+        }
+        if constexpr (NV > 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+            }
+        }
+    }
+    float r = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3] + x[j];
+    out[blockIdx.x * 256 + threadIdx.x] = r;
+}
+
+template <int NV>
+__global__ __launch_bounds__(256, 2) void vmix32_kernel(const bf16x8* ops, float* out, int iters)
+{
+    (void)ops;
+    bf16x8 a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(threadIdx.x * 0.001f + i);
+        b[i] = (__bf16)(1.f + i);
+    }
+    f32x16 acc[4];
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = threadIdx.x * 0.5f + j;
+    for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < NV; ++u) x[(j * NV + u) & 7] = fmaf(x[(j * NV + u) & 7], 0.999f, 1.f);
+        }
+        if constexpr (NV > 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+            }
+        }
+    }
+    float r = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        for (int e = 0; e < 16; ++e) r += acc[j][e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r += x[j];
+    out[blockIdx.x * 256 + threadIdx.x] = r;
+}
+
 #define CHECK(x)                                                                          \
     do {                                                                                  \
         hipError_t e_ = (x);                                                              \
@@ -124,10 +204,20 @@ int main()
         {"32x32x16_random", mfma32_kernel<true>, 4.0 * 32 * 32 * 16 * 2},
         {"16x16x32_const", mfma16_kernel<false>, 8.0 * 16 * 16 * 32 * 2},
         {"16x16x32_random", mfma16_kernel<true>, 8.0 * 16 * 16 * 32 * 2},
+        {"vmix_16x16x32_n0", vmix16_kernel<0>, 8.0 * 16 * 16 * 32 * 2},
+        {"vmix_16x16x32_n2", vmix16_kernel<2>, 8.0 * 16 * 16 * 32 * 2},
+        {"vmix_16x16x32_n3", vmix16_kernel<3>, 8.0 * 16 * 16 * 32 * 2},
+        {"vmix_16x16x32_n4", vmix16_kernel<4>, 8.0 * 16 * 16 * 32 * 2},
+        {"vmix_16x16x32_n6", vmix16_kernel<6>, 8.0 * 16 * 16 * 32 * 2},
+        {"vmix_32x32x16_n0", vmix32_kernel<0>, 2.0 * 32 * 32 * 16 * 2},
+        {"vmix_32x32x16_n3", vmix32_kernel<3>, 2.0 * 32 * 32 * 16 * 2},
+        {"vmix_32x32x16_n6", vmix32_kernel<6>, 2.0 * 32 * 32 * 16 * 2},
+        {"vmix_32x32x16_n9", vmix32_kernel<9>, 2.0 * 32 * 32 * 16 * 2},
     };
     printf("{\"probe\": \"sustained bf16 MFMA\", \"blocks\": %d, \"waves_per_simd\": 2, \"iters\": %d, \"results\": {",
            blocks, iters);
-    for (int c = 0; c < 4; ++c) {
+    const int ncase = (int)(sizeof(cases) / sizeof(cases[0]));
+    for (int c = 0; c < ncase; ++c) {
         cases[c].k<<<blocks, 256>>>(ops, out, iters);  // warm-up launch
         CHECK(hipDeviceSynchronize());
         CHECK(hipEventRecord(e0));

@@ -125,6 +125,37 @@ def test_indexer_fp8_exact_codes(dsa, orc, T):
     assert np.array_equal(got.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+@pytest.mark.parametrize("H", [20, 40, 64])
+def test_indexer_prefill_edge_lengths_bit_exact(dsa, orc, dt, H):
+    """Prefill score rows (T = 37: ragged against the 8-row blocks) with a sequence
+    shorter than T, an empty one and one whose length passes the cache (clamped to
+    it), at head counts that fill one 32-head tile, part of a second, and two.
+    Small-integer operands (and power-of-two fp8 scales) make every sum exact, so
+    the rows must equal the oracle's bit for bit, -inf past each query's position."""
+    B, T, D, Lmax = 4, 37, 128, 300
+    lens = [300, 20, 0, 350]
+    g = torch.Generator().manual_seed(H * 7 + (dt == "fp8"))
+    qv = torch.randint(-3, 4, (B, T, H, D), generator=g).float()
+    kv = torch.randint(-3, 4, (B, Lmax, D), generator=g).float()
+    w = torch.randint(-4, 5, (B, T, H), generator=g).float()
+    kl = torch.tensor(lens, dtype=torch.int32)
+    s = shape_of(dsa, batch=B, n_q=T, max_kv=Lmax, idx_heads=H, idx_dim=D, idx_dtype=dt)
+    announce(f"indexer prefill edge lengths {dt} H={H}")
+    if dt == "bf16":
+        got = dsa.index_scores(s, qv.to(torch.bfloat16).to(DEV), w.to(DEV), kv.to(torch.bfloat16).to(DEV), kl.to(DEV))
+        ref = orc.index_scores(qv, w, kv, kl).reshape(B, T, Lmax)
+    else:
+        qs = 2.0 ** torch.randint(-2, 3, (B, T, H), generator=g).float()
+        ks = 2.0 ** torch.randint(-2, 3, (B, Lmax), generator=g).float()
+        qc = torch.from_numpy(orc.e4m3_encode(qv.numpy()))
+        kc = torch.from_numpy(orc.e4m3_encode(kv.numpy()))
+        got = dsa.index_scores(s, qc.to(DEV), w.to(DEV), kc.to(DEV), kl.to(DEV), q_scale=qs.to(DEV),
+                               k_scale=ks.to(DEV))
+        ref = orc.index_scores_fp8(qc, qs, w, kc, ks, kl).reshape(B, T, Lmax)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("name,seqs,rows", [("tiny_f32", None, None), ("prefill_4k", None, [0, 1, 7, 8, 2047, 2048,
                                                                                              3001, 4095]),
                                             ("decode_32k", [0, 33, 63], None)])

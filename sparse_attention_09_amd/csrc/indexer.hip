@@ -829,9 +829,12 @@ hipError_t launch_dt(const IndexerArgs& a, hipStream_t s)
     if (a.t_count <= 0 || a.B <= 0) return hipSuccess;
     if (a.t_count <= 2) {
         constexpr int NCH = Share<DT, D>::nch;
-        // about 2048 resident waves over the whole grid; 8 KB strips keep the
-        // window of rows in flight small (measured best among 4, 8 and 16 KB)
-        const int per_seq = (2048 + 4 * a.B - 1) / (4 * a.B);
+        // about 2048 persistent waves over the grid for bf16 keys, 4096 for fp8
+        // (measured: 1024-8192 waves; fp8 64-key strips carry twice the products
+        // per byte); 8 KB strips keep the window of rows in flight small (measured
+        // best among 4, 8 and 16 KB)
+        const int waves = DT == kFP8 ? 4096 : 2048;
+        const int per_seq = (waves + 4 * a.B - 1) / (4 * a.B);
         if (a.t_count == 1) {
             constexpr int TPW = NCH >= 8 ? 1 : 8 / NCH;
             const int strips = (a.Lmax + TPW * 16 - 1) / (TPW * 16);

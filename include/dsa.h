@@ -255,7 +255,11 @@ dsa_status dsa_sparse_mla_bwd(const dsa_shape* shape, const void* q, const void*
  *   workspace (256-byte aligned): dsa_forward_workspace_size(shape) bytes run
  *   every query in one pass; any size >= dsa_forward_min_workspace_size(shape)
  *   works, the queries then being processed in the largest chunk of
- *   ceil(T / 2^k) queries whose buffers fit. */
+ *   ceil(T / 2^k) queries whose buffers fit.  When not even one query's score
+ *   rows fit, each chunk's scores and top-k run fused as in dsa_index_topk
+ *   (8 * cap bytes per query row instead of 4 * L_max, cap as there); the
+ *   selection is the same (scores equal to the last bit give the same set;
+ *   otherwise the top-k tie band applies). */
 size_t dsa_forward_workspace_size(const dsa_shape* shape);
 size_t dsa_forward_min_workspace_size(const dsa_shape* shape);
 dsa_status dsa_forward(const dsa_shape* shape, const void* q_idx, const float* w,

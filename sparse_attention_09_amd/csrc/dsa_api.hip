@@ -196,12 +196,16 @@ hipError_t quant_mla_queries(const dsa_shape* s, const void* q, uint8_t* codes, 
 
 // Workspace layout of dsa_forward for a query chunk of tc rows.  The top-k
 // scratch and the MLA split partials share one region: on one stream the top-k
-// of a chunk has finished before its MLA starts.
+// of a chunk has finished before its MLA starts.  With `stream` the chunk's
+// index scores and top-k run fused (launch_index_topk): per row a candidate
+// list of index_topk_cap(K) 8-byte words takes the place of the L_max-float
+// score row, and the top-k needs no scratch of its own.
 struct FwdLayout {
-    size_t qcodes = 0, qscale = 0, mqcodes = 0, mqscale = 0, idx = 0, scores = 0, part = 0, total = 0;
+    size_t qcodes = 0, qscale = 0, mqcodes = 0, mqscale = 0, idx = 0, scores = 0, cand = 0, part = 0, total = 0;
+    bool stream = false;
 };
 
-FwdLayout fwd_layout(const dsa_shape* s, int tc, bool own_idx)
+FwdLayout fwd_layout(const dsa_shape* s, int tc, bool own_idx, bool stream = false)
 {
     FwdLayout l;
     size_t off = 0;
@@ -222,10 +226,16 @@ FwdLayout fwd_layout(const dsa_shape* s, int tc, bool own_idx)
         l.idx = off;
         off += align_up(BT * s->topk * sizeof(int32_t));
     }
-    l.scores = off;
-    off += align_up((size_t)s->batch * tc * s->max_kv * sizeof(float));
+    l.stream = stream;
+    if (stream) {
+        l.cand = off;
+        off += align_up((size_t)s->batch * tc * dsa::index_topk_cap(s->topk) * sizeof(uint64_t));
+    } else {
+        l.scores = off;
+        off += align_up((size_t)s->batch * tc * s->max_kv * sizeof(float));
+    }
     l.part = off;
-    const size_t tk = dsa::topk_workspace_bytes(s->batch, tc, s->max_kv, s->topk);
+    const size_t tk = stream ? 0 : dsa::topk_workspace_bytes(s->batch, tc, s->max_kv, s->topk);
     const size_t pw = mla_ws(s, tc);
     off += align_up(tk > pw ? tk : pw);
     l.total = off;
@@ -249,11 +259,35 @@ int next_chunk(int tc) { return tc <= 1 ? 0 : (tc + 1) / 2; }
 size_t min_forward_ws(const dsa_shape* s, bool own_idx)
 {
     size_t best = (size_t)-1;
-    for (int tc = s->n_q; tc > 0; tc = next_chunk(tc)) {
-        const size_t w = fwd_layout(s, tc, own_idx).total;
-        if (w < best) best = w;
-    }
+    for (int tc = s->n_q; tc > 0; tc = next_chunk(tc))
+        for (int st = 0; st < 2; ++st) {
+            const size_t w = fwd_layout(s, tc, own_idx, st == 1).total;
+            if (w < best) best = w;
+        }
     return best;
+}
+
+// The layout dsa_forward runs with in ws_bytes, and its query rows per chunk
+// (*tc, 0 when nothing fits): the largest chunk of the score-row path, or, when
+// not even one query's score rows fit, the largest chunk of the fused streaming
+// path (8·cap bytes per row against 4·L_max: long contexts).  Chunking the score
+// rows costs next to nothing (prefill_32k in 256 MiB: 27.4 ms against 28.1 ms in
+// one pass), while streaming chunks cost more (29.4 ms there), so streaming is
+// only the fallback.
+FwdLayout choose_forward_layout(const dsa_shape* s, bool own_idx, size_t ws_bytes, int* tc)
+{
+    int ts = s->n_q;
+    while (ts > 0 && fwd_layout(s, ts, own_idx).total > ws_bytes) ts = next_chunk(ts);
+    if (ts == 0) {
+        int tx = s->n_q;
+        while (tx > 0 && fwd_layout(s, tx, own_idx, true).total > ws_bytes) tx = next_chunk(tx);
+        if (tx > 0) {
+            *tc = tx;
+            return fwd_layout(s, tx, own_idx, true);
+        }
+    }
+    *tc = ts;
+    return ts > 0 ? fwd_layout(s, ts, own_idx) : FwdLayout{};
 }
 
 // Workspace of dsa_sparse_mla_bwd for a query chunk of tc rows.
@@ -575,6 +609,24 @@ dsa_status check_forward_args(const dsa_shape* s, const void* q_idx, const float
     return DSA_OK;
 }
 
+// One chunk's index scores and top-k through the score rows.
+hipError_t forward_scores_topk(const dsa_shape* s, const void* qi, const float* qsc, const float* w, const void* k_idx,
+                               const float* k_scale, const int32_t* kv_len, float* scores, int32_t* idx, void* part,
+                               int t0, int cnt, hipStream_t stream)
+{
+    dsa::IndexerArgs ia = indexer_args(s, qi, qsc, w, k_idx, k_scale, kv_len, scores, t0, cnt, 0);
+    dsa::TopkArgs ta = topk_args(s, scores, kv_len, idx, part, t0, cnt);
+    // the indexer clears the top-k's counters, which saves the top-k a launch
+    const size_t zw = dsa::topk_zero_words(ta);
+    if (zw > 0) {
+        ia.zero = (uint32_t*)part;
+        ia.zero_words = (long long)zw;
+        ta.pre_zeroed = 1;
+    }
+    const hipError_t e = dsa::launch_indexer(s->idx_dtype, ia, stream);
+    return e != hipSuccess ? e : dsa::launch_topk(ta, stream);
+}
+
 // The launch sequence of dsa_forward on a checked, 256-byte aligned workspace.
 dsa_status forward_run(const dsa_shape* s, const void* q_idx, const float* w, const void* k_idx,
                        const float* k_scale, const void* q, const void* kv, const int32_t* kv_len,
@@ -582,11 +634,9 @@ dsa_status forward_run(const dsa_shape* s, const void* q_idx, const float* w, co
                        hipStream_t stream)
 {
     const bool own_idx = idx_out == nullptr;
-    // largest query chunk whose workspace fits
-    int tc = s->n_q;
-    while (tc > 0 && fwd_layout(s, tc, own_idx).total > ws_bytes) tc = next_chunk(tc);
+    int tc = 0;
+    const FwdLayout lay = choose_forward_layout(s, own_idx, ws_bytes, &tc);
     if (tc == 0) return DSA_ERR_WORKSPACE;
-    const FwdLayout lay = fwd_layout(s, tc, own_idx);
 
     char* ws = (char*)workspace;
     int32_t* idx = own_idx ? (int32_t*)(ws + lay.idx) : idx_out;
@@ -614,17 +664,18 @@ dsa_status forward_run(const dsa_shape* s, const void* q_idx, const float* w, co
     }
     for (int t0 = 0; t0 < s->n_q; t0 += tc) {
         const int cnt = (s->n_q - t0) < tc ? (s->n_q - t0) : tc;
-        dsa::IndexerArgs ia = indexer_args(s, qi, qsc, w, k_idx, k_scale, kv_len, scores, t0, cnt, 0);
-        dsa::TopkArgs ta = topk_args(s, scores, kv_len, idx, part, t0, cnt);
-        // the indexer clears the top-k's counters, which saves the top-k a launch
-        const size_t zw = dsa::topk_zero_words(ta);
-        if (zw > 0) {
-            ia.zero = (uint32_t*)part;
-            ia.zero_words = (long long)zw;
-            ta.pre_zeroed = 1;
+        if (lay.stream) {
+            dsa::IndexerArgs ia = indexer_args(s, qi, qsc, w, k_idx, k_scale, kv_len, nullptr, t0, cnt, 0);
+            ia.sel_cand = (uint32_t*)(ws + lay.cand);
+            ia.sel_cap = dsa::index_topk_cap(s->topk);
+            ia.sel_k = s->topk;
+            ia.sel_idx = idx;
+            if (dsa::launch_index_topk(s->idx_dtype, ia, stream) != hipSuccess) return DSA_ERR_HIP;
+        } else {
+            if (forward_scores_topk(s, qi, qsc, w, k_idx, k_scale, kv_len, scores, idx, part, t0, cnt, stream) !=
+                hipSuccess)
+                return DSA_ERR_HIP;
         }
-        if (dsa::launch_indexer(s->idx_dtype, ia, stream) != hipSuccess) return DSA_ERR_HIP;
-        if (dsa::launch_topk(ta, stream) != hipSuccess) return DSA_ERR_HIP;
         const int ns = dsa::mla_split_count(s->batch, cnt, s->heads, s->topk);
         const dsa::MlaArgs ma = mla_args(s, qm, qms, kv, idx, kv_len, out, lse, part, t0, cnt, ns);
         if (dsa::launch_mla(s->mla_dtype, ma, stream) != hipSuccess) return DSA_ERR_HIP;

@@ -274,9 +274,14 @@ def test_forward_noalloc_rejects_on_the_host(dsa):
     z = dsa.DsaShape.of(WORKLOADS["decode_32k"])
     z.heads = 0
     assert call(z) == -2
-    # one decode query per sequence cannot be chunked: 64 rows of 2^20 scores need 256 MiB
+    # one decode query per sequence cannot be chunked: 64 rows of 2^20 scores need 256 MiB,
+    # but the fused scores + top-k needs 64 KiB of candidate list per row, which fits
     big = dsa.DsaShape.of(WORKLOADS["decode_32k"])
     big.max_kv = 1 << 20
+    assert dsa.forward_workspace_size(big) > dsa.NOALLOC_SCRATCH_BYTES
+    assert dsa.forward_min_workspace_size(big) <= dsa.NOALLOC_SCRATCH_BYTES
+    # 4096 such rows need 256 MiB of candidate lists and 16 GiB of score rows: rejected
+    big.batch = 4096
     assert dsa.forward_min_workspace_size(big) > dsa.NOALLOC_SCRATCH_BYTES
     assert call(big) == -8
     # the fp8 MLA quantises every query before the chunk loop: 2.4 GB of codes at prefill_32k

@@ -55,7 +55,9 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 
 // Raw buffer accesses (no stride) through a descriptor whose record count bounds
 // them: a load at or past the end returns zero, a store there is dropped, with no
-// branch.  Offsets are bytes; kDropOffset lies past every record count used.
+// branch.  Offsets are bytes (32-bit: the library's supported sizes, L_max <= 2^20
+// rows of at most 512 bytes, keep every offset below 2^31); kDropOffset lies past
+// every record count used.
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
 constexpr int kDropOffset = 0x7FFFFFF0;
 

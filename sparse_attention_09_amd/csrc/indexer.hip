@@ -365,6 +365,120 @@ __device__ __forceinline__ uint32_t cut_to_topk(uint64_t* c, int n, int K, uint3
     return __builtin_amdgcn_readfirstlane(prefix);
 }
 
+// ------------------------------------------------- final select of a candidate list
+// The end of a fused row: its list (n > K entries in position order) is cut to the
+// row's exact top K by the whole block.  The keys are staged in LDS with one load
+// per entry (all of a thread's loads in flight at once; word j at j + j/32, so the
+// per-thread segments below read without bank conflicts), three radix passes (11,
+// 11 and 10 bits) find the K-th largest key tau and how many keys equal to it to
+// take (the first ones in list order: the smallest positions), and an ordered
+// compaction over contiguous per-thread segments writes the positions.
+constexpr int kSelStage = 8192;                       // longest list staged in LDS
+constexpr int kSelPad = kSelStage + kSelStage / 32;   // with one pad word per 32
+
+__device__ __forceinline__ int sel_slot(int j) { return j + (j >> 5); }
+
+// Exclusive prefix sum over the 256 threads of a block (tmp: 4 words of LDS).
+__device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t* tmp)
+{
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) tmp[wave] = x;
+    __syncthreads();
+    uint32_t base = 0;
+    for (int w = 0; w < wave; ++w) base += tmp[w];
+    __syncthreads();
+    return base + x - v;
+}
+
+// Top K (score descending, position ascending) of list[0, n), K < n <= kSelStage,
+// by all 256 threads; positions to dst[0, K) in ascending order.
+__device__ __forceinline__ void block_select_list(const uint64_t* list, int n, int K, int32_t* dst, uint32_t* keys,
+                                                  uint32_t* hist, uint32_t* tmp)
+{
+    const int tid = threadIdx.x;
+    constexpr int PER = kSelStage / 256;
+    {
+        uint64_t e[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) e[i] = list[min(tid + 256 * i, n - 1)];
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (tid + 256 * i < n) keys[sel_slot(tid + 256 * i)] = (uint32_t)e[i];
+    }
+    __syncthreads();
+    uint32_t prefix = 0, pmask = 0;
+    int want = K;  // rank of the K-th key among the keys that match the prefix
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nb = pass == 2 ? 1024 : 2048;
+        for (int i = tid; i < 2048; i += 256) hist[i] = 0u;
+        __syncthreads();
+        for (int j = tid; j < n; j += 256) {
+            const uint32_t k = keys[sel_slot(j)];
+            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        // thread t owns bins [hi - per, hi), hi = nb - per * t: the highest bins first
+        const int per = nb / 256;
+        const int hi = nb - per * tid;
+        uint32_t sum = 0;
+        for (int i = 0; i < per; ++i) sum += hist[hi - 1 - i];
+        const uint32_t above = block_excl_scan256(sum, tmp);
+        if (above < (uint32_t)want && above + sum >= (uint32_t)want) {
+            uint32_t acc = above;
+            int d = hi - 1;
+            for (int i = 0; i < per; ++i) {
+                const uint32_t h = hist[hi - 1 - i];
+                if (acc + h >= (uint32_t)want) {
+                    d = hi - 1 - i;
+                    break;
+                }
+                acc += h;
+            }
+            tmp[4] = (uint32_t)d;
+            tmp[5] = acc;
+        }
+        __syncthreads();
+        want -= (int)tmp[5];
+        prefix |= tmp[4] << shift;
+        pmask |= (uint32_t)(nb - 1) << shift;
+        __syncthreads();
+    }
+    const uint32_t tau = prefix;
+    // ordered compaction: thread t takes entries [t*S, (t+1)*S)
+    const int S = (n + 255) / 256;
+    const int j0 = min(n, tid * S), j1 = min(n, j0 + S);
+    int32_t pos[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) pos[i] = (int32_t)(list[min(j0 + i, n - 1)] >> 32);
+    uint32_t gt = 0, eq = 0;
+    for (int j = j0; j < j1; ++j) {
+        const uint32_t k = keys[sel_slot(j)];
+        gt += k > tau;
+        eq += k == tau;
+    }
+    const uint32_t before = block_excl_scan256((gt << 16) | eq, tmp);
+    const int eq_before = (int)(before & 0xFFFFu);
+    int out = (int)(before >> 16) + min(eq_before, want);
+    int eq_seen = eq_before;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (j0 + i < j1) {
+            const uint32_t k = keys[sel_slot(j0 + i)];
+            bool take = k > tau;
+            if (k == tau) take = eq_seen++ < want;
+            if (take) dst[out++] = pos[i];
+        }
+    }
+}
+
 // ---------------------------------------------------- prefill tiling, 16x16 products
 constexpr int kPrefillQPW = 2;
 constexpr int kPrefillTK = 64;  // keys per LDS tile
@@ -384,6 +498,10 @@ __global__ __launch_bounds__(256, (SEL && DT != kF32) ? 2 : 1) void indexer_pref
     static_assert(NLD >= 1 && (TK * CPR) % 256 == 0, "tile must split evenly over 256 threads");
     __shared__ __attribute__((aligned(16))) char smem[2][TK * PITCH];
     __shared__ uint32_t shist[SEL ? 4 : 1][256];
+    __shared__ uint32_t sel_keys[SEL ? kSelPad : 1];
+    __shared__ uint32_t sel_hist[SEL ? 2048 : 1];
+    __shared__ uint32_t sel_tmp[8];
+    __shared__ int sel_cnt[SEL ? QPB : 1];
 
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -583,23 +701,32 @@ __global__ __launch_bounds__(256, (SEL && DT != kF32) ? 2 : 1) void indexer_pref
     }
 
     if constexpr (SEL) {
-        for (;;) {  // the final cuts, one inlined copy for both rows
-            const bool c0 = vq[0] && cnt[0] > a.sel_k, c1 = vq[1] && cnt[1] > a.sel_k;
-            if (!c0 && !c1) break;
-            int n = 0;
-            cut_to_topk<16, true>(c0 ? cand[0] : cand[1], c0 ? cnt[0] : cnt[1], a.sel_k, shist[wave], lane, &n);
-            if (c0)
-                cnt[0] = n;
-            else
-                cnt[1] = n;
-        }
+        // The rows' lists are cut to their top K by the whole block, one row at a
+        // time (lists past the LDS stage: by their own wave, the mid-row cut's way).
+        if (lane == 0) {
 #pragma unroll
-        for (int q = 0; q < QPW; ++q) {
-            if (!vq[q]) continue;
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
-            int32_t* dst = a.sel_idx + ((size_t)b * a.T + tq[q]) * a.sel_k;
-            for (int j = lane; j < a.sel_k; j += 64)
-                dst[j] = j < cnt[q] ? (int32_t)(cand[q][j] >> 32) : -1;
+            for (int q = 0; q < QPW; ++q) sel_cnt[wave * QPW + q] = vq[q] ? cnt[q] : -1;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        for (int r = 0; r < QPB; ++r) {
+            const int nr = sel_cnt[r];
+            if (nr < 0) continue;
+            const int tr = t0 + r;
+            uint64_t* list = reinterpret_cast<uint64_t*>(a.sel_cand) + (size_t)(b * a.t_count + tr - a.t_begin) * a.sel_cap;
+            int32_t* dst = a.sel_idx + ((size_t)b * a.T + tr) * a.sel_k;
+            if (nr <= a.sel_k) {
+                for (int j = threadIdx.x; j < a.sel_k; j += 256) dst[j] = j < nr ? (int32_t)(list[j] >> 32) : -1;
+            } else if (nr <= kSelStage) {
+                block_select_list(list, nr, a.sel_k, dst, sel_keys, sel_hist, sel_tmp);
+            } else if (r / QPW == wave) {
+                int m = 0;
+                cut_to_topk<16, true>(list, nr, a.sel_k, shist[wave], lane, &m);
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+                for (int j = lane; j < a.sel_k; j += 64) dst[j] = (int32_t)(list[j] >> 32);
+            }
+            __syncthreads();
         }
     } else if (a.fill) {
 #pragma unroll

@@ -43,6 +43,9 @@ INT_CASES = [
     ("f32", 64, 64, 2, 20, 5000, [5000, 4000], 1000, 8),    # one cut late in the row
     ("bf16", 128, 64, 1, 3, 600, [600], 1, 3),              # K = 1
     ("bf16", 128, 64, 4, 1, 3000, [3000, 2000, 1, 0], 256, 3),  # one query per sequence; an empty one
+    # lists longer than the final select's LDS stage: rows of the 10000-key sequence never fill
+    # their 12032-entry lists, so they end with 9993..10000 entries
+    ("bf16", 128, 16, 2, 8, 20000, [20000, 10000], 3000, 3),
 ]
 
 

@@ -210,6 +210,8 @@ TOPK_CASES = [
     (2, 1, 9000, [9000, 8500], 1000),     # K not a power of two
     (1, 1, 131072, [131072], 2048),
     (2, 1, 70000, [70000, 5000], 4096),   # the largest K
+    (5, 4, 9000, [9000, 8200, 4000, 100, 8999], 512),  # 20 rows: three ticket groups, ragged
+    (1, 1, 140000, [140000], 2048),       # over 32 chunks: the three-launch split path
 ]
 
 

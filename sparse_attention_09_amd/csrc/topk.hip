@@ -423,7 +423,7 @@ constexpr int kCoarse = 64;  // coarse bins: the top 6 key bits (64 fine bins ea
 struct SplitWs {
     uint32_t* hist;  // [rows][4096]
     uint32_t* coarse;  // [rows][64]
-    uint32_t* cnt;   // [rows][4]: selected count, candidate count
+    uint32_t* cnt;   // [rows][4]: selected count, candidate count (one 64-bit word, 8-byte aligned)
     int32_t* sel;    // [rows][K]
     uint2* cand;     // [rows][kCandCap] (key, position)
 };
@@ -566,11 +566,15 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a)
         wtot[1][wave] = ic;
     }
     __syncthreads();
-    if (tid == 0) {  // one reservation per workgroup and list
+    if (tid == 0) {  // one reservation per workgroup for both lists: (candidates << 32) + selected
         const uint32_t ts = wtot[0][0] + wtot[0][1] + wtot[0][2] + wtot[0][3];
         const uint32_t tc = wtot[1][0] + wtot[1][1] + wtot[1][2] + wtot[1][3];
-        gbase[0] = ts ? atomicAdd(&w.cnt[row * 4 + 0], ts) : 0u;
-        gbase[1] = tc ? atomicAdd(&w.cnt[row * 4 + 1], tc) : 0u;
+        uint64_t old = 0;
+        if (ts | tc)
+            old = atomicAdd(reinterpret_cast<unsigned long long*>(&w.cnt[row * 4]),
+                            ((unsigned long long)tc << 32) | ts);
+        gbase[0] = (uint32_t)old;
+        gbase[1] = (uint32_t)(old >> 32);
     }
     __syncthreads();
     uint32_t ps = gbase[0] + is - ns, pc = gbase[1] + ic - nc;

@@ -85,7 +85,7 @@ typedef struct {
 /*
  * Supported sizes (anything else returns DSA_ERR_UNSUPPORTED):
  *   indexer  idx_dtype F32: idx_dim in {32, 64, 128};  BF16 / FP8: idx_dim = 128;
- *            idx_heads 1..64 (padded internally to 16, 32 or 64).
+ *            idx_heads 1..64 (padded internally to 16 or 64).
  *   MLA      (mla_dtype, qk_dim, v_dim) in {(F32, 80, 64), (BF16, 576, 512),
  *            (BF16, 192, 128), (FP8_E4M3, 576, 512)}; any heads >= 1.
  *   top-k    topk <= 4096, max_kv <= 1 << 20.

@@ -12,21 +12,18 @@
 // run in-lane, followed by a sum across lane groups.  Scores stay fp32 from the
 // accumulator on.
 //
-// Three tilings of the same arithmetic:
-//   decode   (few queries, long cache): 16x16 tiles; each wave owns a strip of
-//            16-key tiles and streams them straight from HBM into registers,
-//            all loads of a strip issued before any MFMA (HBM-bound, no LDS, no
-//            barriers);
-//   prefill, 32x32 (bf16 and fp8 scores): 32 heads x 32 keys tiles, one query
-//            row per wave and 8 waves sharing 64-key tiles staged in LDS, so each
-//            key row leaves L2 once per 8 queries;
-//   prefill, 16x16 (fp32 operands, and the fused top-k below): 4 waves x 2
-//            query rows share 64-key LDS tiles.
-// Prefill blocks are issued longest-row first.  The 16x16 prefill tiling also
-// runs fused with the top-k of item 2 (launch_index_topk): a wave owns its two
-// query rows over the whole key range, so it keeps each row's candidates in a
-// list of its own instead of writing the score row, and the [T, L] score matrix
-// is never formed.
+// Two tilings of the same arithmetic, both on 16x16 MFMA tiles with the same
+// contraction order, so that every path yields the same scores to the last bit:
+//   decode   (few queries, long cache): each wave owns a strip of 16-key tiles
+//            and streams them straight from HBM into registers, all loads of a
+//            strip issued before any MFMA (HBM-bound, no LDS, no barriers);
+//   prefill: 4 waves x 2 query rows share 64-key LDS tiles.
+// Prefill blocks are issued longest-row first.  The prefill tiling also runs
+// fused with the top-k of item 2 (launch_index_topk): a wave owns its two query
+// rows over the whole key range, so it keeps each row's candidates in a list of
+// its own instead of writing the score row, and the [T, L] score matrix is never
+// formed.  The fused form and the score rows agreeing bit for bit is what makes
+// dsa_index_topk select exactly what dsa_index_scores + dsa_topk select.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -738,218 +735,6 @@ __global__ __launch_bounds__(256, (SEL && DT != kF32) ? 2 : 1) void indexer_pref
     }
 }
 
-// ---------------------------------------------------- prefill tiling, 32x32 products
-// Score rows from bf16 or fp8 operands (index_head_dim 128).  A 16x16x32 MFMA
-// hides about two other vector instructions issued beside it, a 32x32x16 one
-// about six (measured), while the epilogue needs two per score element (relu,
-// weighted add) whatever the tile shape; so these rows run on 32 heads x 32 keys
-// tiles:
-//   v_mfma_f32_32x32x16: A (32 x 16): lane l holds row l%32, k-block l/32
-//   (8 elements); B (16 x 32): column l%32, the same k-block; C (32 x 32): lane
-//   l holds column l%32 and rows 8*(e/4) + 4*(l/32) + e%4, e = 0..15.
-// Heads are on M and keys on N, so a lane holds one key and 16 heads of each
-// 32-head tile: relu and the weighted head sum run in-lane, then one exchange
-// between the lane halves.  Contraction chunks: for k-step pair j a lane half h
-// takes the 16-byte chunk 2j + h of a row (bf16: one step of 8 elements; fp8:
-// two steps, its low and high 8 bytes).
-// One query row per wave, eight waves share each LDS key tile (a key row leaves
-// L2 once per 8 queries).  Each wave scores every 32-key sub-tile of every tile
-// the block loads (keys past its row are dropped at the store), and runs the
-// products of sub-tile j beside the epilogue of sub-tile j - 1.  (The fused
-// top-k keeps the 16x16 tiling, which measured faster there.)
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-template <int DT>
-__device__ __forceinline__ f32x16 mfma32_chunk(u32x4 a, u32x4 b, f32x16 c)
-{
-    if constexpr (DT == kBF16) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                       c, 0, 0, 0);
-    } else {
-        c = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(__builtin_bit_cast(long, u32x2{a[0], a[1]}),
-                                                       __builtin_bit_cast(long, u32x2{b[0], b[1]}), c, 0, 0, 0);
-        return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(__builtin_bit_cast(long, u32x2{a[2], a[3]}),
-                                                          __builtin_bit_cast(long, u32x2{b[2], b[3]}), c, 0, 0, 0);
-    }
-}
-
-constexpr int kP32Rows = 8;   // query rows (waves) per block
-constexpr int kP32TK = 64;    // keys per LDS tile: two 32-key sub-tiles
-
-template <int DT, int MT>
-__global__ __launch_bounds__(512) void indexer_prefill32_kernel(IndexerArgs a)
-{
-    static_assert(DT == kBF16 || DT == kFP8, "bf16 or fp8 operands");
-    constexpr int D = 128;
-    constexpr int ROWB = D * ElemBytes<DT>::v;  // bytes of a key row
-    constexpr int NC = ROWB / 32;               // 16-byte chunks per lane half
-    constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
-    constexpr int PITCH = ROWB + 16;            // padded LDS pitch (conflict-free 16-lane reads)
-    constexpr int TK = kP32TK;
-    constexpr int NT = 64 * kP32Rows;
-    constexpr int NLD = TK * CPR / NT;          // chunks each thread stages per tile
-    constexpr int NMFMA = MT * NC * (DT == kFP8 ? 2 : 1);
-    static_assert(NLD >= 1 && (TK * CPR) % NT == 0, "tile must split evenly over the block");
-    __shared__ __attribute__((aligned(16))) char smem[2][TK * PITCH];
-
-    const int lane = lane_id(), n = lane & 31, hf = lane >> 5;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int b = blockIdx.y;
-    const int qb = gridDim.x - 1 - blockIdx.x;  // longest rows first
-    clear_words(a);
-    const int L = seq_len(a, b);
-    const int t_end = a.t_begin + a.t_count;
-    const int t0 = a.t_begin + qb * kP32Rows;
-    const int t_last = min(t0 + kP32Rows, t_end) - 1;
-    const int kend_blk = max(0, min(a.Lmax, L - a.T + t_last + 1));
-    const int tq = t0 + wave;
-    const bool vq = tq < t_end;
-    const int pq = vq ? L - a.T + tq : -1;
-
-    // query operand (heads on M) and the weights of the heads this lane holds in C
-    u32x4 qa[MT][NC];
-    float wv[MT][16];
-    {
-        const size_t qrow = ((size_t)b * a.T + (vq ? tq : a.t_begin)) * a.H;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int h = 32 * mt + n;
-            const bool ok = vq && h < a.H;
-            const char* src = (const char*)a.q + (qrow + (ok ? h : 0)) * ROWB;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) qa[mt][c] = ok ? ld16(src + 16 * (2 * c + hf)) : u32x4{0, 0, 0, 0};
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int hh = 32 * mt + 8 * (e >> 2) + 4 * hf + (e & 3);
-                float wt = 0.f;
-                if (vq && hh < a.H) {
-                    wt = a.w[qrow + hh];
-                    if constexpr (DT == kFP8) wt *= a.q_scale[qrow + hh];
-                }
-                wv[mt][e] = wt;
-            }
-        }
-    }
-
-    const char* kbase = (const char*)a.k + (size_t)b * a.Lmax * ROWB;
-    const int ntile = (kend_blk + TK - 1) / TK;
-    // bounded buffer accesses: rows at or past kend_blk load as zero; a store past
-    // the row's end (keys after the query, the upper lane half) is dropped
-    const buf_rsrc krs = make_rsrc(kbase, kend_blk * ROWB);
-    const buf_rsrc ksr = make_rsrc(a.k_scale + (DT == kFP8 ? (size_t)b * a.Lmax : 0), DT == kFP8 ? kend_blk * 4 : 0);
-    const buf_rsrc orow = make_rsrc(a.scores + b * a.ld_b + (long long)((vq ? tq : a.t_begin) - a.t_begin) * a.ld_t,
-                                    vq ? max(pq + 1, 0) * 4 : 0);
-
-    u32x4 st[NLD];
-    auto fetch = [&](int tile) {
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int c = threadIdx.x + NT * i;
-            st[i] = buf_ld16(krs, (tile * TK + c / CPR) * ROWB + (c % CPR) * 16);
-        }
-    };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int c = threadIdx.x + NT * i;
-            *reinterpret_cast<u32x4*>(&smem[buf][(c / CPR) * PITCH + (c % CPR) * 16]) = st[i];
-        }
-    };
-    auto load_keys = [&](int buf, int sub, u32x4 (&kv)[NC]) {
-        const char* rowp = &smem[buf][(32 * sub + n) * PITCH + 16 * hf];
-#pragma unroll
-        for (int c = 0; c < NC; ++c) kv[c] = *reinterpret_cast<const u32x4*>(rowp + 32 * c);
-    };
-    auto contract = [&](const u32x4 (&kv)[NC], f32x16 (&acc)[MT]) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[mt][e] = 0.f;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) acc[mt] = mfma32_chunk<DT>(qa[mt][c], kv[c], acc[mt]);
-        }
-    };
-    auto key_scale = [&](int kb0) {
-        if constexpr (DT == kFP8) return __uint_as_float(buf_ld4(ksr, hf == 0 ? (kb0 + n) * 4 : kDropOffset));
-        return 1.f;
-    };
-    auto epilogue = [&](int kb0, float ks, const f32x16 (&acc)[MT]) {
-        float v = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            float u = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) u = fmaf(wv[mt][e], fmaxf(acc[mt][e], 0.f), u);
-            v += u;
-        }
-        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-        buf_st4(orow, hf == 0 ? (kb0 + n) * 4 : kDropOffset, __float_as_uint(v * ks));
-    };
-    // Instruction order of a tile.  First stage: both sub-tiles' key reads, then
-    // part of the pending epilogue while they land, then one MFMA and up to three
-    // other vector instructions at a time.  Second stage: one MFMA and up to five.
-    auto order_first = [&]() {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NC, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
-#pragma unroll
-        for (int i = 0; i < NMFMA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-        }
-    };
-    auto order_second = [&]() {
-#pragma unroll
-        for (int i = 0; i < NMFMA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        }
-    };
-
-    f32x16 acc0[MT], acc1[MT];  // sub-tile 0 / 1 of a tile
-    float ks1 = 0.f;            // key scales of the pending sub-tile 1
-    if (ntile > 0) {
-        fetch(0);
-        stash(0);
-    }
-    __syncthreads();
-    for (int it = 0; it < ntile; ++it) {
-        const int buf = it & 1;
-        if (it + 1 < ntile) fetch(it + 1);
-        const int tile0 = it * TK;
-        u32x4 kv0[NC], kv1[NC];
-        load_keys(buf, 0, kv0);
-        load_keys(buf, 1, kv1);
-        const float ks0 = key_scale(tile0);
-        if (it > 0) epilogue(tile0 - 32, ks1, acc1);
-        contract(kv0, acc0);
-        order_first();
-        ks1 = key_scale(tile0 + 32);
-        contract(kv1, acc1);
-        epilogue(tile0, ks0, acc0);
-        order_second();
-        if (it + 1 < ntile) stash(buf ^ 1);
-        __syncthreads();
-    }
-    if (ntile > 0) epilogue((ntile - 1) * TK + 32, ks1, acc1);
-
-    if (a.fill && vq) {
-        float* row = a.scores + b * a.ld_b + (long long)(tq - a.t_begin) * a.ld_t;
-        for (int s = max(pq + 1, 0) + lane; s < a.Lmax; s += 64) row[s] = -INFINITY;
-    }
-}
-
-template <int DT>
-hipError_t launch_prefill32(const IndexerArgs& a, hipStream_t s)
-{
-    dim3 grid((a.t_count + kP32Rows - 1) / kP32Rows, a.B);
-    if (a.H <= 32)
-        indexer_prefill32_kernel<DT, 1><<<grid, 64 * kP32Rows, 0, s>>>(a);
-    else
-        indexer_prefill32_kernel<DT, 2><<<grid, 64 * kP32Rows, 0, s>>>(a);
-    return hipGetLastError();
-}
-
 template <int DT, int D, int HT>
 hipError_t launch_dt(const IndexerArgs& a, hipStream_t s)
 {
@@ -973,12 +758,10 @@ hipError_t launch_dt(const IndexerArgs& a, hipStream_t s)
             dim3 grid(std::max(1, std::min(per_seq, (strips + 3) / 4)), 1, a.B);
             indexer_decode_kernel<DT, D, HT, 2, TPW><<<grid, 256, 0, s>>>(a);
         }
-    } else if constexpr (DT == kF32) {
+    } else {
         constexpr int QPB = 4 * kPrefillQPW;
         dim3 grid((a.t_count + QPB - 1) / QPB, a.B);
         indexer_prefill_kernel<DT, D, HT, false><<<grid, 256, 0, s>>>(a);
-    } else {
-        return launch_prefill32<DT>(a, s);
     }
     return hipGetLastError();
 }

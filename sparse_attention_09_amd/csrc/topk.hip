@@ -49,7 +49,6 @@ struct TopkShared {
     uint32_t keys[kTopkStageMax];
     uint32_t hist[kHistBins];
     uint32_t cand[kLocalCand];
-    int n_cand;
     int cnt_gt[kTopkWaves];
     int cnt_eq[kTopkWaves];
     int base_eq[kTopkWaves];
@@ -158,10 +157,15 @@ __device__ __forceinline__ void block_find_asc(const uint32_t* hist, int nbins, 
     __syncthreads();
 }
 
-struct RowKeys {
+// Key i of the row: from LDS when the row is staged there, else from memory.
+template <bool STAGED> struct RowKeys;
+template <> struct RowKeys<true> {
+    const uint32_t* keys;
+    __device__ __forceinline__ uint32_t operator()(int i) const { return keys[i]; }
+};
+template <> struct RowKeys<false> {
     const float* src;
-    const uint32_t* staged;
-    __device__ __forceinline__ uint32_t operator()(int i) const { return staged ? staged[i] : float_key(src[i]); }
+    __device__ __forceinline__ uint32_t operator()(int i) const { return float_key(src[i]); }
 };
 
 // Whole-row select by one 1024-thread workgroup (n > K): radix select of the
@@ -202,26 +206,53 @@ __device__ __forceinline__ void radix_tail(TopkShared& sh, KeyAt key_at, int n, 
     }
 }
 
-__device__ void block_select(TopkShared& sh, const float* src, int n, int K, int32_t* dst)
+// Stages a row of n <= PER * 1024 keys in LDS with the histogram of their top 12 bits: all
+// of a thread's loads are issued before the first is used (reads past the row are clamped
+// to its last key and ignored).
+template <int PER>
+__device__ __forceinline__ void stage_keys(TopkShared& sh, const float* src, int n)
 {
+    const int tid = threadIdx.x;
+    float v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) v[u] = src[min(u * kTopkThreads + tid, n - 1)];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int i = u * kTopkThreads + tid;
+        if (i < n) {
+            const uint32_t k = float_key(v[u]);
+            sh.keys[i] = k;
+            atomicAdd(&sh.hist[k >> 20], 1u);
+        }
+    }
+}
+
+template <bool STAGED>
+__device__ void block_select_impl(TopkShared& sh, const float* src, int n, int K, int32_t* dst)
+{
+    // keys per thread and batch: reads from LDS need fewer in flight than reads from memory
+    constexpr int kBatch = STAGED ? 4 : ::dsa::kBatch;
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const bool staged = n <= kTopkStageMax;
-    // pass 0 (top 12 key bits) runs on the keys as they are loaded and staged
+    // pass 0 (top 12 key bits) runs on the keys as they are loaded (and staged)
     for (int i = tid; i < kHistBins; i += kTopkThreads) sh.hist[i] = 0;
-    if (tid == 0) sh.n_cand = 0;
     __syncthreads();
-    for (int base = 0; base < n; base += kTopkThreads * kBatch) {
-        float v[kBatch];
+    if constexpr (STAGED) {
+        if (n <= 4 * kTopkThreads)
+            stage_keys<4>(sh, src, n);
+        else if (n <= 8 * kTopkThreads)
+            stage_keys<8>(sh, src, n);
+        else if (n <= 16 * kTopkThreads)
+            stage_keys<16>(sh, src, n);
+        else
+            stage_keys<kTopkStageMax / kTopkThreads>(sh, src, n);
+    } else {
+        for (int base = 0; base < n; base += kTopkThreads * kBatch) {
+            float v[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) v[u] = src[min(base + u * kTopkThreads + tid, n - 1)];
+            for (int u = 0; u < kBatch; ++u) v[u] = src[min(base + u * kTopkThreads + tid, n - 1)];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int i = base + u * kTopkThreads + tid;
-            if (i < n) {
-                const uint32_t k = float_key(v[u]);
-                if (staged) sh.keys[i] = k;
-                atomicAdd(&sh.hist[k >> 20], 1u);
-            }
+            for (int u = 0; u < kBatch; ++u)
+                if (base + u * kTopkThreads + tid < n) atomicAdd(&sh.hist[float_key(v[u]) >> 20], 1u);
         }
     }
     __syncthreads();
@@ -229,22 +260,44 @@ __device__ void block_select(TopkShared& sh, const float* src, int n, int K, int
     int krem = K - sh.sel_above;  // how many still to take among keys matching the prefix
     uint32_t prefix = sh.sel_digit << 20, pmask = 0xFFF00000u;
     const int c0 = (int)sh.hist[sh.sel_digit];  // keys in the threshold bin
-    const RowKeys key_at{src, staged ? sh.keys : nullptr};
+    RowKeys<STAGED> key_at;
+    if constexpr (STAGED)
+        key_at.keys = sh.keys;
+    else
+        key_at.src = src;
 
     // output segments: wave w writes the selected positions of [w * seg, (w + 1) * seg)
     const int seg = ((n + kTopkWaves - 1) / kTopkWaves + 63) & ~63;
     const int s0 = min(n, wave * seg), s1 = min(n, s0 + seg);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t tau;  // key of the K-th largest score; take krem keys equal to it
     if (c0 <= kLocalCand) {
-        // One scan (each wave over its own output segment) gathers the threshold
-        // bin's keys and positions (one append per wave and batch slot; positions go
-        // to hist[256 ..], which the remaining passes leave alone) and counts the
-        // segment's keys of higher bins.
-        if (tid < kTopkWaves) sh.cnt_eq[tid] = 0;
-        __syncthreads();  // (also: every thread has read the threshold bin's count)
+        // The threshold bin's keys and positions are gathered (positions go to hist[256 ..],
+        // which the remaining passes leave alone), each wave over its own output segment:
+        // one scan counts the segment's keys in the bin and above it, a second writes the
+        // bin's keys at the wave's offset (a scan of the counts, no atomics).
         uint32_t* cpos = sh.hist + 256;
         const uint32_t top = prefix | 0x000FFFFFu;  // keys above the threshold bin exceed this
-        int gt = 0;
+        int gt = 0, nin = 0;
+        for (int i0 = s0; i0 < s1; i0 += 64 * kBatch) {
+            uint32_t kk[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) kk[u] = key_at(min(i0 + 64 * u + lane, n - 1));
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int i = i0 + 64 * u + lane;
+                nin += __popcll(__ballot(i < s1 && (kk[u] & pmask) == prefix));
+                gt += __popcll(__ballot(i < s1 && kk[u] > top));
+            }
+        }
+        __syncthreads();  // (every thread has read the threshold bin's count)
+        if (lane == 0) {
+            sh.cnt_gt[wave] = gt;
+            sh.base_eq[wave] = nin;
+        }
+        __syncthreads();
+        int at = 0;
+        for (int v = 0; v < wave; ++v) at += sh.base_eq[v];
         for (int i0 = s0; i0 < s1; i0 += 64 * kBatch) {
             uint32_t kk[kBatch];
 #pragma unroll
@@ -254,20 +307,15 @@ __device__ void block_select(TopkShared& sh, const float* src, int n, int K, int
                 const int i = i0 + 64 * u + lane;
                 const bool in = i < s1 && (kk[u] & pmask) == prefix;
                 const uint64_t m = __ballot(in);
-                if (m) {
-                    int at = 0;
-                    if (lane == 0) at = atomicAdd(&sh.n_cand, __popcll(m));
-                    at = __shfl(at, 0, 64);
-                    if (in) {
-                        const int r = at + __popcll(m & ((1ull << lane) - 1ull));
-                        sh.cand[r] = kk[u];
-                        cpos[r] = (uint32_t)i;
-                    }
+                if (in) {
+                    const int r = at + __popcll(m & below);
+                    sh.cand[r] = kk[u];
+                    cpos[r] = (uint32_t)i;
                 }
-                gt += __popcll(__ballot(i < s1 && kk[u] > top));
+                at += __popcll(m);
             }
         }
-        if (lane == 0) sh.cnt_gt[wave] = gt;
+        if (tid < kTopkWaves) sh.cnt_eq[tid] = 0;
         __syncthreads();
         // key bits 12..19, 6..11, 0..5 over the c0 gathered keys, by wave 0 alone:
         // a wave's LDS operations complete in order, so its passes need no barriers
@@ -278,9 +326,14 @@ __device__ void block_select(TopkShared& sh, const float* src, int n, int K, int
                 const int nbins = pass == 0 ? 256 : 64;
                 const int per = nbins / 64;  // bins per lane: lane l holds [l * per, (l + 1) * per)
                 for (int bin = lane; bin < nbins; bin += 64) sh.hist[bin] = 0;
-                for (int c = lane; c < c0; c += 64) {
-                    const uint32_t k = sh.cand[c];
-                    if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & (nbins - 1)], 1u);
+                for (int cb = 0; cb < c0; cb += 64 * kBatch) {
+                    uint32_t kk[kBatch];
+#pragma unroll
+                    for (int u = 0; u < kBatch; ++u) kk[u] = sh.cand[min(cb + 64 * u + lane, c0 - 1)];
+#pragma unroll
+                    for (int u = 0; u < kBatch; ++u)
+                        if (cb + 64 * u + lane < c0 && (kk[u] & pmask) == prefix)
+                            atomicAdd(&sh.hist[(kk[u] >> shift) & (nbins - 1)], 1u);
                 }
                 uint32_t hv[4], sum = 0;
 #pragma unroll
@@ -308,8 +361,8 @@ __device__ void block_select(TopkShared& sh, const float* src, int n, int K, int
                     }
                 }
                 const int fl = __ffsll((unsigned long long)__ballot(mine)) - 1;
-                digit = __shfl(digit, fl, 64);
-                above = __shfl(above, fl, 64);
+                digit = __builtin_amdgcn_readlane(digit, fl);
+                above = __builtin_amdgcn_readlane(above, fl);
                 krem -= (int)above;
                 prefix |= (uint32_t)digit << shift;
                 pmask |= (uint32_t)(nbins - 1) << shift;
@@ -365,7 +418,6 @@ __device__ void block_select(TopkShared& sh, const float* src, int n, int K, int
     }
     __syncthreads();
     int run_eq = sh.base_eq[wave], run_sel = sh.base_sel[wave];
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int i0 = s0; i0 < s1; i0 += 64 * kBatch) {
         uint32_t kk[kBatch];
 #pragma unroll
@@ -384,6 +436,14 @@ __device__ void block_select(TopkShared& sh, const float* src, int n, int K, int
             run_sel += __popcll(msel);
         }
     }
+}
+
+__device__ __forceinline__ void block_select(TopkShared& sh, const float* src, int n, int K, int32_t* dst)
+{
+    if (n <= kTopkStageMax)
+        block_select_impl<true>(sh, src, n, K, dst);
+    else
+        block_select_impl<false>(sh, src, n, K, dst);
 }
 
 __device__ __forceinline__ void row_of(const TopkArgs& a, int r, int& b, int& t, int& n)

@@ -4,7 +4,9 @@ Integer-valued inputs make every score exact on both sides, so the selection mus
 equal the oracle's top-k (score descending, position ascending) entry for entry,
 ties included; candidate lists much shorter than the rows force repeated cuts.
 Gaussian inputs at the prefill_4k shape are held to the top-k tie band on sampled
-rows.  The entry point is called through the C ABI.
+rows against the oracle, and, for every dtype and for prefill and decode shapes, must
+select exactly what dsa_index_scores followed by dsa_topk select (the header's
+bit-for-bit promise).  The entry point is called through the C ABI.
 """
 import numpy as np
 import pytest
@@ -123,3 +125,44 @@ def test_index_topk_prefill_4k_sampled(dsa, orc):
         assert msg is None, f"row {r}: {msg}"
         same += int(set(row[row >= 0].tolist()) == set(want[i][want[i] >= 0].tolist()))
     assert same >= len(rows) - 1
+
+
+CONSISTENCY_CASES = [
+    # dt, D, H, B, T, Lmax, lens, K
+    ("bf16", 128, 64, 1, 4096, 4096, [4096], 2048),                  # the prefill_4k shape
+    ("bf16", 128, 64, 6, 1, 32768, [32768, 30000, 5000, 1, 0, 20000], 2048),  # decode, one query
+    ("bf16", 128, 64, 4, 2, 20000, [20000, 15000, 3, 2], 512),        # decode, two queries
+    ("fp8", 128, 64, 2, 300, 8192, [8192, 4000], 1024),               # fp8 prefill
+    ("fp8", 128, 64, 4, 1, 40000, [40000, 1000, 39000, 7], 2048),     # fp8 decode
+    ("f32", 64, 16, 2, 2, 5000, [5000, 4000], 300),
+]
+
+
+@pytest.mark.parametrize("case", CONSISTENCY_CASES)
+def test_index_topk_equals_scores_then_topk(dsa, case):
+    """On Gaussian inputs dsa_index_topk selects exactly what dsa_index_scores followed by
+    dsa_topk select, bit for bit: the fused pass and the score rows (the decode tiling
+    included) compute every score in the same order."""
+    dt, D, H, B, T, Lmax, lens, K = case
+    announce(f"index_topk == index_scores + topk {case}")
+    g = torch.Generator().manual_seed(7 * Lmax + T)
+    q = torch.randn(B, T, H, D, generator=g)
+    k = torch.randn(B, Lmax, D, generator=g)
+    w = torch.randn(B, T, H, generator=g)
+    kl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    s = shape_of(dsa, batch=B, n_q=T, max_kv=Lmax, idx_heads=H, idx_dim=D, topk=K, idx_dtype=dt)
+    w = w.to(DEV)
+    if dt == "fp8":
+        qc, qs = dsa.rotate_quant_fp8(q.to(DEV, torch.bfloat16))
+        kc, ks = dsa.rotate_quant_fp8(k.to(DEV, torch.bfloat16))
+        kw = dict(q_scale=qs, k_scale=ks)
+        args = (qc, w, kc, kl)
+    else:
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        kw = {}
+        args = (q.to(DEV, tdt), w, k.to(DEV, tdt), kl)
+    scores = dsa.index_scores(s, *args, **kw)
+    ref = dsa.topk(s, scores, kl)
+    got = dsa.index_topk(s, *args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)

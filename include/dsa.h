@@ -258,8 +258,8 @@ dsa_status dsa_sparse_mla_bwd(const dsa_shape* shape, const void* q, const void*
  *   ceil(T / 2^k) queries whose buffers fit.  When not even one query's score
  *   rows fit, each chunk's scores and top-k run fused as in dsa_index_topk
  *   (8 * cap bytes per query row instead of 4 * L_max, cap as there); the
- *   selection is the same (scores equal to the last bit give the same set;
- *   otherwise the top-k tie band applies). */
+ *   selection, and so out and lse, are the same bit for bit (both paths compute
+ *   every score in the same order). */
 size_t dsa_forward_workspace_size(const dsa_shape* shape);
 size_t dsa_forward_min_workspace_size(const dsa_shape* shape);
 dsa_status dsa_forward(const dsa_shape* shape, const void* q_idx, const float* w,

@@ -141,23 +141,26 @@ def test_forward_prefill_4k_chunked_matches_single_pass(dsa):
     assert d <= 2e-2 * out1.float().abs().max().item()
 
 
-def test_forward_streaming_fallback_matches_score_rows(dsa):
+@pytest.mark.parametrize("operands", ["integer", "gaussian"])
+def test_forward_streaming_fallback_matches_score_rows(dsa, operands):
     """Four decode sequences of 256K keys in their smallest workspace: one query's
     score rows (4 x 1 MiB, with the split top-k's scratch) do not fit, the fused
     scores + top-k (64 KiB of candidate list per row) does, so dsa_forward streams.
-    With integer-valued indexer operands every score is exact on both paths (many
-    ties, broken by position on both), so the selection, the outputs and the lse
-    equal those of the one-pass score-row run bit for bit."""
+    Both paths compute every score in the same order, so the selection, the outputs
+    and the lse equal those of the one-pass score-row run bit for bit: on integer-valued
+    indexer operands (exact scores, many ties broken by position on both) and on the
+    workload's Gaussian ones."""
     wl = get("decode_32k").replace(batch=4, max_kv=1 << 18, kv_len=1 << 18)
     inp = make_inputs(wl, device=DEV)
-    g = torch.Generator(device=DEV).manual_seed(5)
-    inp["q_idx"] = torch.randint(-3, 4, inp["q_idx"].shape, generator=g, device=DEV).to(torch.bfloat16)
-    inp["k_idx"] = torch.randint(-3, 4, inp["k_idx"].shape, generator=g, device=DEV).to(torch.bfloat16)
-    inp["w"] = torch.randint(-4, 5, inp["w"].shape, generator=g, device=DEV).float()
+    if operands == "integer":
+        g = torch.Generator(device=DEV).manual_seed(5)
+        inp["q_idx"] = torch.randint(-3, 4, inp["q_idx"].shape, generator=g, device=DEV).to(torch.bfloat16)
+        inp["k_idx"] = torch.randint(-3, 4, inp["k_idx"].shape, generator=g, device=DEV).to(torch.bfloat16)
+        inp["w"] = torch.randint(-4, 5, inp["w"].shape, generator=g, device=DEV).float()
     s = dsa.DsaShape.of(wl)
     small = dsa.forward_min_workspace_size(s)
     assert small < dsa.forward_workspace_size(s)  # T = 1: the score-row path has no smaller layout
-    announce("forward streaming fallback vs score rows, 4 x 256K decode")
+    announce(f"forward streaming fallback vs score rows, 4 x 256K decode, {operands} operands")
     idx1, out1, lse1, _, _, _ = _run(dsa, wl, inp)
     idx2, out2, lse2, _, _, _ = _run(dsa, wl, inp, workspace_bytes=small)
     assert torch.equal(idx1, idx2)

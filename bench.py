@@ -2,7 +2,8 @@
 
     python bench.py [--steps K] [--warmup W] [--workload decode_32k|prefill_32k|decode_128k_fp8|...] [--single]
     python bench.py --sweep-context     (stage times of bf16 decode, batch 16, context 4K..128K)
-    python bench.py --mfma-ceiling      (sustained bf16 MFMA rate, constant and random operands)
+    python bench.py --mfma-ceiling      (sustained bf16 MFMA rate, constant and random operands;
+                                         streaming-read bandwidth)
 
 A step is one dsa_forward call (fp8 workloads: q rotation + quantisation,
 index scores, top-k, sparse MLA) over one batch of synthetic inputs already
@@ -25,7 +26,11 @@ cores, and on one thread over a smaller sample (CPU model named).
 
 The default run measures the three points of the metric in one process:
 decode_32k (the line's value), prefill_32k and decode_128k_fp8, each with its
-own roofline, stage fractions and oracle timing under "points".
+own roofline, stage fractions and oracle timing under "points".  It ends by
+measuring this GPU's own ceilings ("box_ceilings": a streaming read and the
+sustained bf16 MFMA rate from mfma_ceiling.hip, and the vendor GEMM rate for
+context), and each roofline adds "frac_of_box", the achieved rate over the ceiling
+of its kind, beside "frac" against the published peak.
 
 Prints one JSON line.
 """
@@ -631,6 +636,46 @@ def run_point(args, name: str, with_bwd: bool, cpu_budget: float) -> dict:
     return res
 
 
+def box_ceilings(torch) -> dict:
+    """This GPU's own ceilings, measured live beside the published peaks: a plain
+    streaming read of 1 GiB and the sustained bf16 MFMA rate on random operands (both
+    from mfma_ceiling.hip), and, for context, the bf16 GEMM rate of the vendor library
+    (torch.matmul, 8192^3, contiguous operands)."""
+    probe = mfma_ceiling()
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(n, n, generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, generator=g, device="cuda").to(torch.bfloat16).contiguous()
+    torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    mm_tf = 2 * n ** 3 / (e0.elapsed_time(e1) * 1e-3 / 10) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    mf = probe["results"]["32x32x16_random"]
+    return {"hbm_read": {"achieved": probe["stream_read"]["GBs"], "unit": "GB/s",
+                         "how": "grid-stride 16-byte reads of 1 GiB (mfma_ceiling.hip)"},
+            "bf16_mfma": {"achieved": mf["tflops"], "unit": "TFLOP/s",
+                          "how": "back-to-back v_mfma_f32_32x32x16_bf16 on random operands (mfma_ceiling.hip)"},
+            "bf16_gemm": {"achieved": round(mm_tf, 1), "unit": "TFLOP/s",
+                          "how": "torch.matmul 8192 x 8192 x 8192 bf16 (hipBLASLt), for context"}}
+
+
+def add_box_fraction(roof: dict, box: dict) -> None:
+    """roofline["frac_of_box"]: achieved over this box's own measured ceiling of the same kind."""
+    if not roof:
+        return
+    if roof.get("bound") == "hbm":
+        roof["frac_of_box"] = round(roof["achieved"] / box["hbm_read"]["achieved"], 4)
+    elif roof.get("bound") == "mfma" and roof.get("peak") == PEAK_TFLOPS["bf16"]:
+        roof["frac_of_box"] = round(roof["achieved"] / box["bf16_mfma"]["achieved"], 4)
+
+
 def run(args) -> dict:
     head = run_point(args, args.workload, True, CPU_BUDGET_S)
     res = {"metric": METRIC, "value": head["value"], "unit": "queries/s", "n_gpus": 1, "steps": head["steps"],
@@ -651,6 +696,13 @@ def run(args) -> dict:
             pts[name] = {k: p[k] for k in keep if k in p}
             pts[name]["unit"] = "queries/s"
         res["points"] = pts
+    import torch
+
+    box = box_ceilings(torch)
+    res["box_ceilings"] = box
+    add_box_fraction(res.get("roofline"), box)
+    for p in res.get("points", {}).values():
+        add_box_fraction(p.get("roofline"), box)
     return res
 
 

@@ -1,5 +1,6 @@
-// mfma_ceiling.hip -- sustained bf16 MFMA throughput of this GPU, for the
-// roofline figures that bench.py reports against the published peak.
+// mfma_ceiling.hip -- sustained bf16 MFMA throughput and streaming-read bandwidth
+// of this GPU, for the roofline figures that bench.py reports beside the
+// published peaks.
 //
 // Each wave issues back-to-back independent MFMAs (v_mfma_f32_32x32x16_bf16 or
 // v_mfma_f32_16x16x32_bf16) for a fixed number of iterations, at two waves per
@@ -9,7 +10,11 @@
 // the instruction count.  The "vmix" cases follow every MFMA with n independent
 // fma instructions (on small structured operands, in a fixed MFMA / VALU issue
 // order) to measure how many other vector instructions an MFMA hides.  Only each
-// thread's final sum is stored.  Prints one JSON line.
+// thread's final sum is stored.  The "stream_read" cases read 1 GiB with a
+// grid-stride loop of 16-byte loads (2048, 8192 or 32768 workgroups; 4 or 8 loads
+// in flight per thread) and store one sum per thread; the best of them is the plain
+// streaming ceiling that the HBM-bound kernels are held to.
+// Prints one JSON line.
 //
 // Build and run (bench.py --mfma-ceiling does both):
 //   hipcc --offload-arch=gfx950 -O3 -mllvm -amdgpu-mfma-vgpr-form=1 \
@@ -165,6 +170,28 @@ __global__ __launch_bounds__(256, 2) void vmix32_kernel(const bf16x8* ops, float
     out[blockIdx.x * 256 + threadIdx.x] = r;
 }
 
+// Sum of a 16-byte-aligned buffer of n4 float4 elements, U loads in flight per thread
+// per iteration; one partial sum per thread.
+template <int U>
+__global__ __launch_bounds__(256) void stream_read_kernel(const float4* p, size_t n4, float* out)
+{
+    const size_t stride = (size_t)gridDim.x * 256;
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    float acc = 0.f;
+    for (; i + (U - 1) * stride < n4; i += U * stride) {
+        float4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+    }
+    for (; i < n4; i += stride) {
+        const float4 a = p[i];
+        acc += a.x + a.y + a.z + a.w;
+    }
+    out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 #define CHECK(x)                                                                          \
     do {                                                                                  \
         hipError_t e_ = (x);                                                              \
@@ -214,7 +241,7 @@ int main()
         {"vmix_32x32x16_n6", vmix32_kernel<6>, 2.0 * 32 * 32 * 16 * 2},
         {"vmix_32x32x16_n9", vmix32_kernel<9>, 2.0 * 32 * 32 * 16 * 2},
     };
-    printf("{\"probe\": \"sustained bf16 MFMA\", \"blocks\": %d, \"waves_per_simd\": 2, \"iters\": %d, \"results\": {",
+    printf("{\"probe\": \"sustained bf16 MFMA, streaming read\", \"blocks\": %d, \"waves_per_simd\": 2, \"iters\": %d, \"results\": {",
            blocks, iters);
     const int ncase = (int)(sizeof(cases) / sizeof(cases[0]));
     for (int c = 0; c < ncase; ++c) {
@@ -231,7 +258,41 @@ int main()
         printf("%s\"%s\": {\"ms\": %.3f, \"tflops\": %.1f, \"of_2516_tflops\": %.4f}", c ? ", " : "", cases[c].name,
                ms, tflops, tflops / 2516.6);
     }
-    printf("}}\n");
+    // streaming read of 1 GiB: grid sizes and loads in flight swept, the best is the ceiling
+    const size_t n4 = (size_t)1 << 26;
+    const int grids[3] = {2048, 8192, 32768};
+    float4* big = nullptr;
+    float* sums = nullptr;
+    CHECK(hipMalloc(&big, n4 * sizeof(float4)));
+    CHECK(hipMalloc(&sums, (size_t)grids[2] * 256 * sizeof(float)));
+    CHECK(hipMemset(big, 0, n4 * sizeof(float4)));
+    double best = 0.0;
+    printf("}, \"stream_read\": {\"bytes\": %zu, \"cases\": {", n4 * sizeof(float4));
+    for (int gi = 0; gi < 3; ++gi)
+        for (int uu = 0; uu < 2; ++uu) {
+            auto launch = [&]() {
+                if (uu == 0)
+                    stream_read_kernel<4><<<grids[gi], 256>>>(big, n4, sums);
+                else
+                    stream_read_kernel<8><<<grids[gi], 256>>>(big, n4, sums);
+            };
+            launch();  // warm-up launch
+            CHECK(hipDeviceSynchronize());
+            CHECK(hipEventRecord(e0));
+            for (int r = 0; r < 10; ++r) launch();
+            CHECK(hipEventRecord(e1));
+            CHECK(hipEventSynchronize(e1));
+            float ms = 0.f;
+            CHECK(hipEventElapsedTime(&ms, e0, e1));
+            ms /= 10;
+            const double gbs = n4 * sizeof(float4) / (ms * 1e-3) / 1e9;
+            best = gbs > best ? gbs : best;
+            printf("%s\"grid%d_u%d\": {\"ms\": %.4f, \"GBs\": %.1f}", gi + uu ? ", " : "", grids[gi], uu ? 8 : 4,
+                   ms, gbs);
+        }
+    printf("}, \"GBs\": %.1f}}\n", best);
+    CHECK(hipFree(sums));
+    CHECK(hipFree(big));
     CHECK(hipFree(ops));
     CHECK(hipFree(out));
     return 0;

@@ -212,6 +212,9 @@ TOPK_CASES = [
     (2, 1, 70000, [70000, 5000], 4096),   # the largest K
     (5, 4, 9000, [9000, 8200, 4000, 100, 8999], 512),  # 20 rows: three ticket groups, ragged
     (1, 1, 140000, [140000], 2048),       # over 32 chunks: the three-launch split path
+    # many long rows: one workgroup per row, 16 and 32 staged keys per thread
+    (1, 260, 12000, [12000], 1000),
+    (2, 150, 20000, [20000, 19000], 2048),
 ]
 
 

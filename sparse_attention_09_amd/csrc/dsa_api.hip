@@ -644,18 +644,31 @@ dsa_status forward_run(const dsa_shape* s, const void* q_idx, const float* w, co
     void* part = ws + lay.part;
     const void* qi = q_idx;
     const float* qsc = nullptr;
-    if (s->idx_dtype == DSA_FP8_E4M3) {
-        uint8_t* qc = (uint8_t*)(ws + lay.qcodes);
-        float* qs = (float*)(ws + lay.qscale);
-        const int64_t rows = (int64_t)s->batch * s->n_q * s->idx_heads;
-        hipError_t e = dsa::launch_rotate_quant(rows, s->idx_dim, q_idx, DSA_BF16, qc, qs, stream);
-        if (e != hipSuccess) return DSA_ERR_HIP;
-        qi = qc;
-        qsc = qs;
-    }
     const void* qm = q;
     const float* qms = nullptr;
-    if (s->mla_dtype == DSA_FP8_E4M3) {
+    const bool fp8_idx = s->idx_dtype == DSA_FP8_E4M3, fp8_mla = s->mla_dtype == DSA_FP8_E4M3;
+    const int64_t idx_rows = (int64_t)s->batch * s->n_q * s->idx_heads;
+    if (fp8_idx && fp8_mla) {  // both query preparations in one launch
+        uint8_t* qc = (uint8_t*)(ws + lay.qcodes);
+        float* qs = (float*)(ws + lay.qscale);
+        uint8_t* mqc = (uint8_t*)(ws + lay.mqcodes);
+        float* mqs = (float*)(ws + lay.mqscale);
+        const int64_t mla_rows = (int64_t)s->batch * s->n_q * s->heads;
+        if (dsa::launch_fp8_queries(idx_rows, s->idx_dim, q_idx, qc, qs, mla_rows, s->qk_dim, q, mqc, mqs, stream) !=
+            hipSuccess)
+            return DSA_ERR_HIP;
+        qi = qc;
+        qsc = qs;
+        qm = mqc;
+        qms = mqs;
+    } else if (fp8_idx) {
+        uint8_t* qc = (uint8_t*)(ws + lay.qcodes);
+        float* qs = (float*)(ws + lay.qscale);
+        if (dsa::launch_rotate_quant(idx_rows, s->idx_dim, q_idx, DSA_BF16, qc, qs, stream) != hipSuccess)
+            return DSA_ERR_HIP;
+        qi = qc;
+        qsc = qs;
+    } else if (fp8_mla) {
         uint8_t* qc = (uint8_t*)(ws + lay.mqcodes);
         float* qs = (float*)(ws + lay.mqscale);
         if (quant_mla_queries(s, q, qc, qs, stream) != hipSuccess) return DSA_ERR_HIP;

@@ -112,6 +112,10 @@ hipError_t launch_rotate_quant(int64_t rows, int dim, const void* x, int x_dtype
 // 16 bytes after the codes (fp32 scale, 12 zero bytes).
 hipError_t launch_quant_rows(int64_t rows, int dim, const void* x, int x_dtype, uint8_t* codes, int64_t cpitch,
                              float* scales, int tail, hipStream_t s);
+// The index queries' rotate + quantise (rows x dim, bf16) and the MLA queries'
+// quantisation (mrows x mdim, bf16) in one launch, with the results of the two.
+hipError_t launch_fp8_queries(int64_t rows, int dim, const void* x, uint8_t* codes, float* scales, int64_t mrows,
+                              int mdim, const void* mx, uint8_t* mcodes, float* mscales, hipStream_t s);
 // Rotate + quantise rows [B, t_new, dim] into cache rows kv_len[b] - t_new + t of [B, max_kv, dim].
 hipError_t launch_cache_append(int batch, int t_new, int max_kv, int dim, const void* x, int x_dtype,
                                const int32_t* kv_len, uint8_t* codes, float* scales, hipStream_t s);

@@ -66,16 +66,17 @@ struct RowMap {
 // the stages h >= 8 pair lanes li and li ^ (h / 8) of the same row.  Stages run
 // in increasing h with the same pairing and signs whatever the layout, so every
 // element goes through the same fp64 operations as in the plain transform.
+// Blocks blk of nblk (of the launch's 256-thread blocks) share the rows.
 template <int DIM, int XT>
-__global__ __launch_bounds__(256) void rotate_quant_kernel(int64_t rows, const void* x, uint8_t* codes,
-                                                           float* scales, double inv_sqrt_dim, RowMap map)
+__device__ __forceinline__ void rotate_quant_rows(int64_t rows, const void* x, uint8_t* codes, float* scales,
+                                                  double inv_sqrt_dim, RowMap map, int blk, int nblk)
 {
     constexpr int LPR = DIM / 8;   // lanes per row
     constexpr int RPW = 64 / LPR;  // rows per wave
     static_assert(DIM % 8 == 0 && LPR >= 1 && LPR <= 64, "dim");
     const int lane = lane_id(), li = lane % LPR, grp = lane / LPR;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t n_waves = (int64_t)gridDim.x * 4;
+    const int64_t wave = (int64_t)blk * 4 + (threadIdx.x >> 6);
+    const int64_t n_waves = (int64_t)nblk * 4;
     for (int64_t row0 = wave * RPW; row0 < rows; row0 += n_waves * RPW) {
         const int64_t row = row0 + grp;
         const int64_t orow = row < rows ? map(row) : -1;
@@ -139,18 +140,25 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(int64_t rows, const v
     }
 }
 
+template <int DIM, int XT>
+__global__ __launch_bounds__(256) void rotate_quant_kernel(int64_t rows, const void* x, uint8_t* codes,
+                                                           float* scales, double inv_sqrt_dim, RowMap map)
+{
+    rotate_quant_rows<DIM, XT>(rows, x, codes, scales, inv_sqrt_dim, map, blockIdx.x, gridDim.x);
+}
+
 // Per-row e4m3 quantisation without rotation (the codec above on the rows as
 // they are).  One wave per row; lane li holds the 8-element chunks li and li + 64
 // (rows of up to 1024 elements).  Codes go to codes + row * cpitch; the row scale
 // to scales[row], or with `tail` into the 16 bytes after the row's codes (fp32
 // scale, then 12 zero bytes: the fp8 latent-cache row layout).
 template <int XT>
-__global__ __launch_bounds__(256) void quant_rows_kernel(int64_t rows, int dim, const void* x, uint8_t* codes,
-                                                         int64_t cpitch, float* scales, int tail)
+__device__ __forceinline__ void quant_rows_body(int64_t rows, int dim, const void* x, uint8_t* codes, int64_t cpitch,
+                                                float* scales, int tail, int blk, int nblk)
 {
     const int lane = lane_id(), nch = dim / 8;
-    const int64_t n_waves = (int64_t)gridDim.x * 4;
-    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += n_waves) {
+    const int64_t n_waves = (int64_t)nblk * 4;
+    for (int64_t row = (int64_t)blk * 4 + (threadIdx.x >> 6); row < rows; row += n_waves) {
         float xf[2][8];
         float amax = 0.f;
 #pragma unroll
@@ -204,6 +212,27 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(int64_t rows, int dim, 
     }
 }
 
+template <int XT>
+__global__ __launch_bounds__(256) void quant_rows_kernel(int64_t rows, int dim, const void* x, uint8_t* codes,
+                                                         int64_t cpitch, float* scales, int tail)
+{
+    quant_rows_body<XT>(rows, dim, x, codes, cpitch, scales, tail, blockIdx.x, gridDim.x);
+}
+
+// The two query preparations of an fp8 indexer with an fp8 MLA in one launch: blocks
+// [0, g1) rotate and quantise the index queries, blocks [g1, grid) quantise the MLA
+// queries (bf16 rows of mdim elements, codes packed, scales apart).
+template <int DIM>
+__global__ __launch_bounds__(256) void fp8_queries_kernel(int64_t rows, const void* x, uint8_t* codes, float* scales,
+                                                          double inv_sqrt_dim, int g1, int64_t mrows, int mdim,
+                                                          const void* mx, uint8_t* mcodes, float* mscales)
+{
+    if ((int)blockIdx.x < g1)
+        rotate_quant_rows<DIM, kBF16>(rows, x, codes, scales, inv_sqrt_dim, RowMap{nullptr, 0, 0}, blockIdx.x, g1);
+    else
+        quant_rows_body<kBF16>(mrows, mdim, mx, mcodes, mdim, mscales, 0, blockIdx.x - g1, gridDim.x - g1);
+}
+
 template <int DIM>
 hipError_t launch_dim(int64_t rows, const void* x, int xt, uint8_t* codes, float* scales, RowMap map, hipStream_t s)
 {
@@ -249,6 +278,21 @@ hipError_t launch_quant_rows(int64_t rows, int dim, const void* x, int x_dtype, 
         quant_rows_kernel<kBF16><<<grid, 256, 0, s>>>(rows, dim, x, codes, cpitch, scales, tail);
     else
         quant_rows_kernel<kF32><<<grid, 256, 0, s>>>(rows, dim, x, codes, cpitch, scales, tail);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_queries(int64_t rows, int dim, const void* x, uint8_t* codes, float* scales, int64_t mrows,
+                              int mdim, const void* mx, uint8_t* mcodes, float* mscales, hipStream_t s)
+{
+    if (dim != 128 || mdim <= 0 || mdim % 16 != 0 || mdim > 1024 || rows <= 0 || mrows <= 0) {
+        const hipError_t e = launch_rotate_quant(rows, dim, x, kBF16, codes, scales, s);
+        return e != hipSuccess ? e : launch_quant_rows(mrows, mdim, mx, kBF16, mcodes, mdim, mscales, 0, s);
+    }
+    constexpr int RPB = 4 * (64 / (128 / 8));  // index-query rows per block pass
+    const int g1 = (int)std::min<int64_t>((rows + RPB - 1) / RPB, 8192);
+    const int g2 = (int)std::min<int64_t>((mrows + 3) / 4, 8192);
+    fp8_queries_kernel<128><<<dim3((unsigned)(g1 + g2)), 256, 0, s>>>(rows, x, codes, scales, 1.0 / sqrt(128.0), g1,
+                                                                       mrows, mdim, mx, mcodes, mscales);
     return hipGetLastError();
 }
 

@@ -660,6 +660,10 @@ def box_ceilings(torch) -> dict:
     mf = probe["results"]["32x32x16_random"]
     return {"hbm_read": {"achieved": probe["stream_read"]["GBs"], "unit": "GB/s",
                          "how": "grid-stride 16-byte reads of 1 GiB (mfma_ceiling.hip)"},
+            "row_gather": {"achieved": probe["row_gather"]["GBs"], "unit": "GB/s",
+                           "how": "random 1152-byte rows, 2048 of 32768 per sequence, 64 sequences, "
+                                  "best of register and direct-to-LDS loads (mfma_ceiling.hip)",
+                           "cases": probe["row_gather"]["cases"]},
             "bf16_mfma": {"achieved": mf["tflops"], "unit": "TFLOP/s",
                           "how": "back-to-back v_mfma_f32_32x32x16_bf16 on random operands (mfma_ceiling.hip)"},
             "bf16_gemm": {"achieved": round(mm_tf, 1), "unit": "TFLOP/s",
@@ -674,6 +678,24 @@ def add_box_fraction(roof: dict, box: dict) -> None:
         roof["frac_of_box"] = round(roof["achieved"] / box["hbm_read"]["achieved"], 4)
     elif roof.get("bound") == "mfma" and roof.get("peak") == PEAK_TFLOPS["bf16"]:
         roof["frac_of_box"] = round(roof["achieved"] / box["bf16_mfma"]["achieved"], 4)
+
+
+def add_stage_box_fractions(wl_name: str, fr: dict, box: dict) -> None:
+    """stages_frac[...]["frac_of_box"]: each stage's rate over this box's measured ceiling
+    of its kind.  The decode sparse MLA reads random latent rows, so its HBM figure is
+    held to the measured random-row gather rate rather than to the streaming read."""
+    from workloads import get
+    if not fr:
+        return
+    decode = get(wl_name).n_q == 1
+    for name, f in fr.items():
+        if f["bound"] == "hbm":
+            ceil = box["row_gather"] if (name == "mla" and decode) else box["hbm_read"]
+            f["frac_of_box"] = round(f["frac"] * PEAK_HBM_GBS / ceil["achieved"], 4)
+            if name == "mla" and decode:
+                f["box_ceiling"] = "row_gather"
+        elif f["bound"] == "mfma" and mfma_peak(get(wl_name), name) == PEAK_TFLOPS["bf16"]:
+            f["frac_of_box"] = round(f["frac"] * PEAK_TFLOPS["bf16"] / box["bf16_mfma"]["achieved"], 4)
 
 
 def run(args) -> dict:
@@ -701,8 +723,11 @@ def run(args) -> dict:
     box = box_ceilings(torch)
     res["box_ceilings"] = box
     add_box_fraction(res.get("roofline"), box)
-    for p in res.get("points", {}).values():
+    add_stage_box_fractions(args.workload, res.get("stages_frac"), box)
+    for name, p in res.get("points", {}).items():
         add_box_fraction(p.get("roofline"), box)
+        if name != args.workload:
+            add_stage_box_fractions(name, p.get("stages_frac"), box)
     return res
 
 

@@ -1,5 +1,5 @@
-// mfma_ceiling.hip -- sustained bf16 MFMA throughput and streaming-read bandwidth
-// of this GPU, for the roofline figures that bench.py reports beside the
+// mfma_ceiling.hip -- sustained bf16 MFMA throughput, streaming-read bandwidth and
+// random-row gather bandwidth of this GPU, for the roofline figures that bench.py reports beside the
 // published peaks.
 //
 // Each wave issues back-to-back independent MFMAs (v_mfma_f32_32x32x16_bf16 or
@@ -13,7 +13,15 @@
 // thread's final sum is stored.  The "stream_read" cases read 1 GiB with a
 // grid-stride loop of 16-byte loads (2048, 8192 or 32768 workgroups; 4 or 8 loads
 // in flight per thread) and store one sum per thread; the best of them is the plain
-// streaming ceiling that the HBM-bound kernels are held to.
+// streaming ceiling that the HBM-bound kernels are held to.  The "row_gather" cases
+// read what the decode sparse MLA reads: rows of 1152 bytes (576 bf16) picked at
+// random, without repetition, from each of 64 sequences of 32768 rows (a 2.4 GB
+// latent cache), 2048 rows per sequence, 32 rows per tile, one 256-thread
+// workgroup per (sequence, share of its rows), each 16-byte chunk loaded once,
+// either into registers (two tiles in flight) or straight into LDS
+// (global_load_lds_dwordx4, three tile buffers, two tiles in flight); three
+// different row sets are rotated so that no launch finds the previous one's rows
+// in the caches.  The best of them is the random-row gather ceiling.
 // Prints one JSON line.
 //
 // Build and run (bench.py --mfma-ceiling does both):
@@ -25,6 +33,7 @@
 #include <cstdio>
 #include <cstring>
 #include <random>
+#include <utility>
 #include <vector>
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -192,6 +201,84 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const float4* p, size_
     out[blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// Random-row gather (the access pattern of the decode sparse MLA).  Block w takes
+// sequence w / nsplit and its share w % nsplit of the sequence's row list; a tile
+// is 32 rows x 72 chunks of 16 bytes, chunk c = tid + 256 k (k < 9) being row
+// c / 72, chunk c % 72.  Row offsets are 32-bit byte offsets from the sequence base.
+constexpr int kGSeq = 64, kGRows = 32768, kGSel = 2048, kGRowB = 1152, kGCh = kGRowB / 16;
+constexpr int kGTile = 32, kGTileCh = kGTile * kGCh, kGLoads = kGTileCh / 256;
+static_assert(kGTileCh % 256 == 0, "tile chunks");
+
+__global__ __launch_bounds__(256) void gather_reg_kernel(const char* cache, const int* rows, int nsplit,
+                                                         unsigned* out)
+{
+    __shared__ unsigned roff[kGSel];
+    const int seq = blockIdx.x / nsplit, part = blockIdx.x % nsplit;
+    const int per = kGSel / nsplit, ntiles = per / kGTile;
+    const char* base = cache + (size_t)seq * kGRows * kGRowB;
+    for (int i = threadIdx.x; i < per; i += 256) roff[i] = (unsigned)rows[seq * kGSel + part * per + i] * kGRowB;
+    __syncthreads();
+    unsigned acc = 0;
+    uint4 cur[kGLoads], nxt[kGLoads];
+    auto load = [&](uint4(&d)[kGLoads], int t) {
+#pragma unroll
+        for (int k = 0; k < kGLoads; ++k) {
+            const int c = threadIdx.x + 256 * k;
+            d[k] = *reinterpret_cast<const uint4*>(base + roff[t * kGTile + c / kGCh] + (c % kGCh) * 16);
+        }
+    };
+    load(cur, 0);
+    for (int t = 0; t < ntiles; ++t) {
+        load(nxt, t + 1 < ntiles ? t + 1 : t);  // unconditional: the wait covers this tile only
+#pragma unroll
+        for (int k = 0; k < kGLoads; ++k) {
+            acc ^= cur[k].x ^ cur[k].y ^ cur[k].z ^ cur[k].w;
+            cur[k] = nxt[k];
+        }
+    }
+    out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void gather_lds_kernel(const char* cache, const int* rows, int nsplit,
+                                                         unsigned* out)
+{
+    __shared__ __attribute__((aligned(16))) uint4 buf[3 * kGTileCh];
+    __shared__ unsigned roff[kGSel];
+    const int seq = blockIdx.x / nsplit, part = blockIdx.x % nsplit;
+    const int per = kGSel / nsplit, ntiles = per / kGTile;
+    const char* base = cache + (size_t)seq * kGRows * kGRowB;
+    for (int i = threadIdx.x; i < per; i += 256) roff[i] = (unsigned)rows[seq * kGSel + part * per + i] * kGRowB;
+    __syncthreads();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    auto issue = [&](int t) {
+        uint4* dst = buf + (t % 3) * kGTileCh;
+#pragma unroll
+        for (int k = 0; k < kGLoads; ++k) {
+            const int c = threadIdx.x + 256 * k;
+            const unsigned off = roff[t * kGTile + c / kGCh] + (c % kGCh) * 16;
+            const unsigned lds = (unsigned)reinterpret_cast<uintptr_t>(
+                (__attribute__((address_space(3))) uint4*)(dst + wave * 64 + 256 * k));
+            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+        }
+    };
+    unsigned acc = 0;
+    issue(0);
+    if (ntiles > 1) issue(1);
+    for (int t = 0; t < ntiles; ++t) {
+        // tile t has landed for every wave, and every wave is done with the buffer that
+        // tile t + 2 refills
+        if (t + 1 < ntiles)
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(kGLoads) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+        if (t + 2 < ntiles) issue(t + 2);
+        const uint4 v = buf[(t % 3) * kGTileCh + threadIdx.x];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+    }
+    out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 #define CHECK(x)                                                                          \
     do {                                                                                  \
         hipError_t e_ = (x);                                                              \
@@ -290,9 +377,64 @@ int main()
             printf("%s\"grid%d_u%d\": {\"ms\": %.4f, \"GBs\": %.1f}", gi + uu ? ", " : "", grids[gi], uu ? 8 : 4,
                    ms, gbs);
         }
-    printf("}, \"GBs\": %.1f}}\n", best);
+    printf("}, \"GBs\": %.1f}", best);
     CHECK(hipFree(sums));
     CHECK(hipFree(big));
+
+    // random-row gather: three row sets, each 64 x 2048 distinct rows of 32768
+    const size_t cache_bytes = (size_t)kGSeq * kGRows * kGRowB;
+    char* cache = nullptr;
+    int* rowsets = nullptr;
+    unsigned* gout = nullptr;
+    CHECK(hipMalloc(&cache, cache_bytes));
+    CHECK(hipMemset(cache, 1, cache_bytes));
+    CHECK(hipMalloc(&rowsets, 3 * (size_t)kGSeq * kGSel * sizeof(int)));
+    CHECK(hipMalloc(&gout, (size_t)kGSeq * 16 * 256 * sizeof(unsigned)));
+    {
+        std::vector<int> perm(kGRows), h(3 * (size_t)kGSeq * kGSel);
+        for (size_t sq = 0; sq < 3 * (size_t)kGSeq; ++sq) {
+            for (int i = 0; i < kGRows; ++i) perm[i] = i;
+            for (int i = 0; i < kGSel; ++i) {  // partial Fisher-Yates: the first kGSel of a random permutation
+                const int j = i + (int)(rng() % (unsigned)(kGRows - i));
+                std::swap(perm[i], perm[j]);
+                h[sq * kGSel + i] = perm[i];
+            }
+        }
+        CHECK(hipMemcpy(rowsets, h.data(), h.size() * sizeof(int), hipMemcpyHostToDevice));
+    }
+    const double gbytes = (double)kGSeq * kGSel * kGRowB;
+    const int splits[2] = {4, 16};
+    double gbest = 0.0;
+    printf(", \"row_gather\": {\"bytes\": %.0f, \"row_bytes\": %d, \"cases\": {", gbytes, kGRowB);
+    for (int path = 0; path < 2; ++path)
+        for (int si = 0; si < 2; ++si) {
+            const int ns = splits[si];
+            auto launch = [&](int set) {
+                const int* rs = rowsets + (size_t)set * kGSeq * kGSel;
+                if (path == 0)
+                    gather_reg_kernel<<<kGSeq * ns, 256>>>(cache, rs, ns, gout);
+                else
+                    gather_lds_kernel<<<kGSeq * ns, 256>>>(cache, rs, ns, gout);
+            };
+            launch(0);  // warm-up launch
+            CHECK(hipDeviceSynchronize());
+            const int reps = 30;
+            CHECK(hipEventRecord(e0));
+            for (int r = 0; r < reps; ++r) launch(r % 3);
+            CHECK(hipEventRecord(e1));
+            CHECK(hipEventSynchronize(e1));
+            float ms = 0.f;
+            CHECK(hipEventElapsedTime(&ms, e0, e1));
+            ms /= reps;
+            const double gbs = gbytes / (ms * 1e-3) / 1e9;
+            gbest = gbs > gbest ? gbs : gbest;
+            printf("%s\"%s_%dblocks\": {\"us\": %.2f, \"GBs\": %.1f}", path + si ? ", " : "",
+                   path ? "lds" : "registers", kGSeq * ns, ms * 1e3, gbs);
+        }
+    printf("}, \"GBs\": %.1f}}\n", gbest);
+    CHECK(hipFree(gout));
+    CHECK(hipFree(rowsets));
+    CHECK(hipFree(cache));
     CHECK(hipFree(ops));
     CHECK(hipFree(out));
     return 0;

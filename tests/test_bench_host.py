@@ -83,3 +83,21 @@ def test_default_run_covers_the_metric_points():
     ctx = {get(n).kv_len for n in bench.POINTS}
     assert ctx == {32768, 131072}
     assert bench.SWEEP_CONTEXTS[0] <= 4096 and bench.SWEEP_CONTEXTS[-1] >= 131072
+
+
+def test_stage_fractions_against_the_box_ceilings():
+    box = {"hbm_read": {"achieved": 5000.0}, "row_gather": {"achieved": 4000.0}, "bf16_mfma": {"achieved": 1250.0}}
+    # decode: the sparse MLA is held to the random-row gather ceiling, the others to the streaming read
+    fr = {"indexer": {"bound": "hbm", "frac": 0.5}, "topk": {"bound": "hbm", "frac": 0.05},
+          "mla": {"bound": "hbm", "frac": 0.25}}
+    bench.add_stage_box_fractions("decode_32k", fr, box)
+    assert fr["indexer"]["frac_of_box"] == pytest.approx(0.5 * 8000 / 5000)
+    assert fr["topk"]["frac_of_box"] == pytest.approx(0.05 * 8000 / 5000)
+    assert fr["mla"]["frac_of_box"] == pytest.approx(0.25 * 8000 / 4000)
+    assert fr["mla"]["box_ceiling"] == "row_gather"
+    # prefill: MFMA-bound stages against the sustained bf16 MFMA rate
+    fr = {"indexer": {"bound": "mfma", "frac": 0.5}, "mla": {"bound": "mfma", "frac": 0.4}}
+    bench.add_stage_box_fractions("prefill_32k", fr, box)
+    assert fr["indexer"]["frac_of_box"] == pytest.approx(0.5 * 2500 / 1250)
+    assert fr["mla"]["frac_of_box"] == pytest.approx(0.4 * 2500 / 1250)
+    assert "box_ceiling" not in fr["mla"]

@@ -705,18 +705,36 @@ __device__ __forceinline__ void mla_write_rows_wide(const MlaArgs& a, const Wide
         *reinterpret_cast<f32x4*>(rowp + P::vbytes) = f32x4{st.m_run, l_tot, 0.f, 0.f};
 }
 
+// Queries of the wide kernel staged through LDS: wave w's 32 query rows are
+// contiguous in memory, so they are loaded 1 KiB per instruction straight into
+// LDS in the tiles' padded layout (32 rows of PCH chunks, the pad chunk a copy of
+// chunk 0), and each lane then reads its MFMA operand the way it reads the keys.
+// The staging area overlays the tile buffers and the index list, which are
+// filled only after every wave has read its queries.
+template <class C>
+struct WideQStage {
+    static constexpr int ROW_CH = kTileKeys * C::PCH;                   // 32 rows, padded pitch
+    static constexpr int LOADS = (ROW_CH + 63) / 64;                    // 1 KiB loads per wave
+    static constexpr int WAVE_CH = LOADS * 64;                          // a wave's staging chunks
+    static constexpr int CH = C::NW * WAVE_CH;
+};
+
 template <int DQK, int DV>
 __global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
 {
     using C = WideCfg<DQK, DV>;
-    __shared__ __attribute__((aligned(16))) u32x4 tiles[C::NBUF * C::BUF_CH];
-    __shared__ uint32_t lrow[kMaxListLen];
-    __shared__ uint32_t tmask[kMaxListLen / kTileKeys];
+    using QS_ = WideQStage<C>;
+    constexpr int kTileCh = C::NBUF * C::BUF_CH;
+    constexpr int kListWords = kMaxListLen + kMaxListLen / kTileKeys + 2;
+    constexpr int kMainCh = kTileCh + (kListWords + 3) / 4;
+    __shared__ __attribute__((aligned(16))) u32x4 lds[QS_::CH > kMainCh ? QS_::CH : kMainCh];
+    u32x4* tiles = lds;
+    uint32_t* lrow = reinterpret_cast<uint32_t*>(lds + kTileCh);
+    uint32_t* tmask = lrow + kMaxListLen;
     // restart requests: a wave raising one during tile `it` writes slot it & 1,
     // which every wave reads after the next barrier (before anyone can write that
     // slot again, two tiles later)
-    __shared__ int restart_flags[2];
-    volatile int* restart = restart_flags;
+    volatile int* restart = reinterpret_cast<volatile int*>(tmask + kMaxListLen / kTileKeys);
 
     const int HB = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
     const int n_units = a.B * a.t_count * a.n_split * HB;
@@ -731,7 +749,6 @@ __global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
     const int L = min(a.kv_len[b], a.Lmax);
 
     const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-    if (tid < 2) restart[tid] = 0;
     const int col = lane & 31, kb = lane >> 5;
     const int head = hb * kHeadsPerBlock + w * 32 + col;
     const bool head_ok = head < a.H;
@@ -750,11 +767,41 @@ __global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
     int raw[kListPer];
 #pragma unroll
     for (int r = 0; r < kListPer; ++r) raw[r] = idxr[min(j_begin + tid + C::NT * r, j_last)];
-    // Q^T operand: lane (col, kb) holds dims [HQ * kb + 8 s, + 8) of head `col` at step s
-    const uint16_t* qsrc = (const uint16_t*)a.q + (row * a.H + (head_ok ? head : 0)) * DQK + C::HQ * kb;
-    u32x4 qb[C::QS];
+    // Q^T operand: lane (col, kb) holds dims [HQ * kb + 8 s, + 8) of head `col` at step s.
+    // Staging position p of wave w is row p / PCH (head 32 w + p / PCH, rows past the
+    // wave's 32 and heads past H read head H - 1), chunk p % PCH (the pad chunk reads
+    // chunk 0); load k covers positions 64 k .. 64 k + 63.
+    {
+        const char* qbase = (const char*)a.q + row * (size_t)a.H * C::ROWB;
+        const int wu = __builtin_amdgcn_readfirstlane(w);
+        const int h0 = hb * kHeadsPerBlock + wu * 32;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        int hr = 0, ch = ln;  // 64 < PCH: lane l starts at row 0, chunk l
 #pragma unroll
-    for (int s = 0; s < C::QS; ++s) qb[s] = ld16(qsrc + 8 * s);
+        for (int k = 0; k < QS_::LOADS; ++k) {
+            const int hh = min(h0 + min(hr, kTileKeys - 1), a.H - 1);
+            const uint32_t off = (uint32_t)hh * C::ROWB + (ch >= C::CPR ? 0u : (uint32_t)ch * 16u);
+            const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(
+                (__attribute__((address_space(3))) u32x4*)(lds + wu * QS_::WAVE_CH + 64 * k));
+            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(qbase), "{m0}"(dst)
+                         : "memory");
+            ch += 64;
+            if (ch >= C::PCH) {
+                ch -= C::PCH;
+                ++hr;
+            }
+        }
+    }
+    barrier_lds_vm();  // this wave's staged queries have landed (and everyone's)
+    u32x4 qb[C::QS];
+    {
+        const char* qr = reinterpret_cast<const char*>(lds + w * QS_::WAVE_CH) + col * C::PITCH + C::HQ * kb * 2;
+#pragma unroll
+        for (int s = 0; s < C::QS; ++s) qb[s] = *reinterpret_cast<const u32x4*>(qr + 16 * s);
+    }
+    barrier_lds();  // every wave has its queries: the staging area is free
+    if (tid < 2) restart[tid] = 0;
 #pragma unroll
     for (int r = 0; r < kListPer; ++r) {
         const int j = tid + C::NT * r;

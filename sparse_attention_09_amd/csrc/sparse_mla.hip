@@ -83,6 +83,7 @@ struct Bf16Cfg {
     static constexpr int TILE_CH = kTileKeys * PCH;
     static constexpr int DMA_PER_WAVE = (TILE_CH + 511) / 512;  // 1 KiB direct loads per wave per tile
     static constexpr int BUF_CH = DMA_PER_WAVE * 512;           // buffer size in chunks (dummy tail)
+    static constexpr int NT = 512, NW = 8, DMA = DMA_PER_WAVE;   // for the asm gather
     static constexpr int HALF = DQK / 2;          // contraction share of a wave
     static constexpr int SHARE = DQK / 4;         // share of one 32-lane k-block
     static constexpr int QS = SHARE / 8;          // 32x32x16 steps over a half
@@ -129,6 +130,50 @@ __device__ __forceinline__ void gather_tile(const char* kvb, const uint32_t* lro
     for (int k = 0; k < C::DMA_PER_WAVE; ++k)
         __builtin_amdgcn_global_load_lds(kvb + (roff[k] + coff[k]),
                                          (__attribute__((address_space(3))) void*)(dst + (wu + 8 * k) * 64), 16, 0, 0);
+}
+
+// Direct loads of index-list tile [j0, j0 + 32) into LDS, as gather_tile but for
+// NT threads and issued from asm: gather_offsets reads the row offsets of this
+// lane's DMA loads from LDS, gather_issue issues load k (M0 holds the wave's LDS
+// destination).
+template <class C>
+__device__ __forceinline__ void gather_offsets(const uint32_t* lrow, int j0, int w, int lane, uint32_t (&off)[C::DMA])
+{
+    constexpr int DR = C::NT / C::PCH, DCH = C::NT % C::PCH;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    int r = (wu * 64 + ln) / C::PCH;
+    int c = wu * 64 + ln - r * C::PCH;
+#pragma unroll
+    for (int k = 0; k < C::DMA; ++k) {
+        off[k] = lrow[j0 + min(r, kTileKeys - 1)] + (c == C::CPR ? 0u : (uint32_t)c * 16u);
+        r += DR;
+        c += DCH;
+        if (c >= C::PCH) {
+            c -= C::PCH;
+            ++r;
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void gather_issue(const char* kvb, uint32_t off, u32x4* dst, int w, int k)
+{
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) u32x4*)(dst + (wu + C::NW * k) * 64));
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(kvb), "{m0}"(lds) : "memory");
+}
+
+template <class C>
+__device__ __forceinline__ void gather_tile_asm(const char* kvb, const uint32_t* lrow, int j0, int w, int lane,
+                                                u32x4* dst)
+{
+    uint32_t off[C::DMA];
+    gather_offsets<C>(lrow, j0, w, lane, off);
+#pragma unroll
+    for (int k = 0; k < C::DMA; ++k) gather_issue<C>(kvb, off[k], dst, w, k);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads (whose vmcnt(0)
@@ -296,11 +341,20 @@ template <int DQK, int DV>
 __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
 {
     using C = Bf16Cfg<DQK, DV>;
-    __shared__ __attribute__((aligned(16))) u32x4 tA[C::BUF_CH];
-    __shared__ __attribute__((aligned(16))) u32x4 tB[C::BUF_CH];
-    __shared__ float xbuf[8][16][64];
-    __shared__ uint32_t lrow[kMaxListLen];
-    __shared__ uint32_t tmask[kMaxListLen / kTileKeys];
+    // the queries of wave pair p are staged in region p (see the prologue), which
+    // overlays the tile buffers, the logit exchange and the index list
+    constexpr int kStageCh = (kTileKeys * C::PCH + 63) / 64 * 64;  // one pair's 32 padded rows
+    constexpr int kStageLoads = kStageCh / 64;
+    constexpr int kXbufCh = 8 * 16 * 64 / 4;
+    constexpr int kListWords = kMaxListLen + kMaxListLen / kTileKeys;
+    constexpr int kMainCh = 2 * C::BUF_CH + kXbufCh + (kListWords + 3) / 4;
+    constexpr int kLdsCh = 4 * kStageCh > kMainCh ? 4 * kStageCh : kMainCh;
+    __shared__ __attribute__((aligned(16))) u32x4 lds[kLdsCh];
+    u32x4* tA = lds;
+    u32x4* tB = lds + C::BUF_CH;
+    float (*xbuf)[16][64] = reinterpret_cast<float (*)[16][64]>(lds + 2 * C::BUF_CH);
+    uint32_t* lrow = reinterpret_cast<uint32_t*>(lds + 2 * C::BUF_CH + kXbufCh);
+    uint32_t* tmask = lrow + kMaxListLen;
 
     const int HB = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
     const int n_units = a.B * a.t_count * a.n_split * HB;
@@ -339,16 +393,50 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
     int raw[kListPer];
 #pragma unroll
     for (int r = 0; r < kListPer; ++r) raw[r] = idxr[min(j_begin + tid + 512 * r, j_last)];
-    // Q^T operand: head `head`, contraction d in [HALF*half + SHARE*kb, + SHARE).  A
-    // column past the last head loads head 0 (finite values whose results are never
-    // written), so the loads are unconditional too.
+    // Q^T operand: head `head`, contraction d in [HALF*half + SHARE*kb, + SHARE).  The
+    // pair's 32 query rows are contiguous in memory and are staged in LDS by direct
+    // 1 KiB loads in the tiles' padded layout (position P: row P / PCH, chunk P % PCH,
+    // the pad chunk a copy of chunk 0; half h of the pair issues loads h, h + 2, ...).
+    // A row past the last head reads head H - 1 (finite values whose results are never
+    // written), so every load is unconditional.
+    {
+        const char* qbase = (const char*)a.q + row * (size_t)a.H * C::ROWB;
+        const int pu = __builtin_amdgcn_readfirstlane(pair), hu = __builtin_amdgcn_readfirstlane(half);
+        const int h0 = hb * kHeadsPerBlock + pu * 32;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        int hr = 0, ch = ln + 64 * hu;  // position of load hu: 64 hu + lane
+        while (ch >= C::PCH) {
+            ch -= C::PCH;
+            ++hr;
+        }
+#pragma unroll
+        for (int k = 0; k < (kStageLoads + 1) / 2; ++k) {
+            const int kk = 2 * k + hu;
+            if (kk < kStageLoads) {
+                const int hh = min(h0 + min(hr, kTileKeys - 1), a.H - 1);
+                const uint32_t off = (uint32_t)hh * C::ROWB + (ch >= C::CPR ? 0u : (uint32_t)ch * 16u);
+                const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(
+                    (__attribute__((address_space(3))) u32x4*)(lds + pu * kStageCh + 64 * kk));
+                asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(qbase), "{m0}"(dst)
+                             : "memory");
+            }
+            ch += 128;  // two loads further on
+            while (ch >= C::PCH) {
+                ch -= C::PCH;
+                ++hr;
+            }
+        }
+    }
+    barrier_lds_vm();  // the pair's staged queries have landed
     u32x4 qb[C::QS];
     {
-        const char* src = (const char*)a.q + ((row * a.H + (head_ok ? head : 0)) * DQK) * 2 +
-                          (C::HALF * half + C::SHARE * kb) * 2;
+        const char* qr = reinterpret_cast<const char*>(lds + pair * kStageCh) + col * C::PITCH +
+                         (C::HALF * half + C::SHARE * kb) * 2;
 #pragma unroll
-        for (int s = 0; s < C::QS; ++s) qb[s] = ld16(src + 16 * s);
+        for (int s = 0; s < C::QS; ++s) qb[s] = *reinterpret_cast<const u32x4*>(qr + 16 * s);
     }
+    barrier_lds();  // every wave has its queries: the staging area is free
     // the list sanitised (skipped entries fetch row 0) and padded to whole tiles,
     // plus a validity mask per tile; every slot is filled (the ones past the list
     // as skipped), without branches, so the compiler keeps the early loads
@@ -376,19 +464,19 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
     const float zc = a.sm_scale * kLog2e;
 
     // tile `it` lives in buffer it % 2; each step issues tile it + 1 into the other buffer
-    if (n_tiles > 0) gather_tile<C>(kvb, lrow, 0, w, lane, tA);
+    if (n_tiles > 0) gather_tile_asm<C>(kvb, lrow, 0, w, lane, tA);
 #pragma unroll 1
     for (int it = 0; it < n_tiles; it += 2) {
         barrier_lds_vm();
         // the tile's mask is read together with the next tile's row offsets
         const uint32_t vmA = tmask[it];
-        if (it + 1 < n_tiles) gather_tile<C>(kvb, lrow, (it + 1) * kTileKeys, w, lane, tB);
+        if (it + 1 < n_tiles) gather_tile_asm<C>(kvb, lrow, (it + 1) * kTileKeys, w, lane, tB);
         __builtin_amdgcn_sched_barrier(0);
         tile_compute<DQK, DV>(tA, vmA, qb, st, zc, xbuf, w, lane);
         if (it + 1 >= n_tiles) break;
         barrier_lds_vm();
         const uint32_t vmB = tmask[it + 1];
-        if (it + 2 < n_tiles) gather_tile<C>(kvb, lrow, (it + 2) * kTileKeys, w, lane, tA);
+        if (it + 2 < n_tiles) gather_tile_asm<C>(kvb, lrow, (it + 2) * kTileKeys, w, lane, tA);
         __builtin_amdgcn_sched_barrier(0);
         tile_compute<DQK, DV>(tB, vmB, qb, st, zc, xbuf, w, lane);
     }
@@ -460,50 +548,6 @@ struct WideState {
     f32x16 o[WideCfg<DQK, DV>::VT];
     float m_run, l_run;
 };
-
-// Direct loads of index-list tile [j0, j0 + 32) into LDS, as gather_tile but for
-// NT threads and issued from asm: gather_offsets reads the row offsets of this
-// lane's DMA loads from LDS, gather_issue issues load k (M0 holds the wave's LDS
-// destination).
-template <class C>
-__device__ __forceinline__ void gather_offsets(const uint32_t* lrow, int j0, int w, int lane, uint32_t (&off)[C::DMA])
-{
-    constexpr int DR = C::NT / C::PCH, DCH = C::NT % C::PCH;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int wu = __builtin_amdgcn_readfirstlane(w);
-    int r = (wu * 64 + ln) / C::PCH;
-    int c = wu * 64 + ln - r * C::PCH;
-#pragma unroll
-    for (int k = 0; k < C::DMA; ++k) {
-        off[k] = lrow[j0 + min(r, kTileKeys - 1)] + (c == C::CPR ? 0u : (uint32_t)c * 16u);
-        r += DR;
-        c += DCH;
-        if (c >= C::PCH) {
-            c -= C::PCH;
-            ++r;
-        }
-    }
-}
-
-template <class C>
-__device__ __forceinline__ void gather_issue(const char* kvb, uint32_t off, u32x4* dst, int w, int k)
-{
-    const int wu = __builtin_amdgcn_readfirstlane(w);
-    const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(
-        (__attribute__((address_space(3))) u32x4*)(dst + (wu + C::NW * k) * 64));
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(kvb), "{m0}"(lds) : "memory");
-}
-
-template <class C>
-__device__ __forceinline__ void gather_tile_asm(const char* kvb, const uint32_t* lrow, int j0, int w, int lane,
-                                                u32x4* dst)
-{
-    uint32_t off[C::DMA];
-    gather_offsets<C>(lrow, j0, w, lane, off);
-#pragma unroll
-    for (int k = 0; k < C::DMA; ++k) gather_issue<C>(kvb, off[k], dst, w, k);
-}
 
 // A gather carried out by the tile computation: its loads are issued one at a
 // time between the logit MFMAs, so that they queue behind no other wave's burst
@@ -777,7 +821,11 @@ __global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
         const int h0 = hb * kHeadsPerBlock + wu * 32;
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        int hr = 0, ch = ln;  // 64 < PCH: lane l starts at row 0, chunk l
+        int hr = 0, ch = ln;  // position of load 0: lane
+        while (ch >= C::PCH) {
+            ch -= C::PCH;
+            ++hr;
+        }
 #pragma unroll
         for (int k = 0; k < QS_::LOADS; ++k) {
             const int hh = min(h0 + min(hr, kTileKeys - 1), a.H - 1);
@@ -787,7 +835,7 @@ __global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
             asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(qbase), "{m0}"(dst)
                          : "memory");
             ch += 64;
-            if (ch >= C::PCH) {
+            while (ch >= C::PCH) {
                 ch -= C::PCH;
                 ++hr;
             }

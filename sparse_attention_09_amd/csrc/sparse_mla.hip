@@ -749,6 +749,49 @@ __device__ __forceinline__ void mla_write_rows_wide(const MlaArgs& a, const Wide
         *reinterpret_cast<f32x4*>(rowp + P::vbytes) = f32x4{st.m_run, l_tot, 0.f, 0.f};
 }
 
+// Epilogue of the bf16 wide kernel, staged through LDS: the workgroup's rows
+// (one per head: the normalised value row in bf16, or a split's partial row
+// followed by its fp32 m, l) are one contiguous block in memory, so every wave
+// first writes its 32 rows into `stage` (pitch PartRow::bytes, conflict-free for
+// the 8-byte writes) and the whole block then leaves in 1 KiB stores.  A lane
+// holds dims 32*v + 8*i + 4*kb + jj (register 4*i + jj) of head `col`.
+template <int DQK, int DV, class C>
+__device__ __forceinline__ void mla_write_rows_wide_staged(const MlaArgs& a, const WideState<DQK, DV>& st,
+                                                           size_t row, int rq, int split, int hb, int head,
+                                                           bool head_ok, int w, int col, int kb, int tid,
+                                                           char* stage)
+{
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (a.n_split == 1 && a.lse && head_ok && kb == 0)
+        a.lse[row * a.H + head] = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    using P = PartRow<kBF16, DV>;
+    constexpr int SP = P::bytes;  // staged row pitch
+    const bool part_out = a.n_split > 1;
+    const int hb0 = hb * kHeadsPerBlock;
+    const int heads_here = min(kHeadsPerBlock, a.H - hb0);
+    char* gbase = part_out ? (char*)a.part + (((size_t)rq * a.n_split + split) * a.H + hb0) * P::bytes
+                           : (char*)a.out + (row * a.H + hb0) * (size_t)(DV * 2);
+    const int rch = part_out ? P::bytes / 16 : DV / 8;  // 16-byte chunks of a row in memory
+    barrier_lds();  // every wave is done with the tiles (and the restart flags)
+    char* sb = stage + (w * 32 + col) * SP + 8 * kb;
+#pragma unroll
+    for (int v = 0; v < C::VT; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x2*>(sb + 2 * (32 * v + 8 * i)) =
+                u32x2{pack_bf16x2(st.o[v][4 * i] * inv, st.o[v][4 * i + 1] * inv),
+                      pack_bf16x2(st.o[v][4 * i + 2] * inv, st.o[v][4 * i + 3] * inv)};
+    if (kb == 0)
+        *reinterpret_cast<f32x4*>(stage + (w * 32 + col) * SP + P::vbytes) = f32x4{st.m_run, l_tot, 0.f, 0.f};
+    barrier_lds();
+    const int n = heads_here * rch;
+    for (int c = tid; c < n; c += C::NT) {
+        const int r = c / rch, k = c - r * rch;
+        st16(gbase + 16 * (size_t)c, *reinterpret_cast<const u32x4*>(stage + r * SP + 16 * k));
+    }
+}
+
 // Queries of the wide kernel staged through LDS: wave w's 32 query rows are
 // contiguous in memory, so they are loaded 1 KiB per instruction straight into
 // LDS in the tiles' padded layout (32 rows of PCH chunks, the pad chunk a copy of
@@ -914,7 +957,9 @@ __global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
             for (int e = 0; e < 16; ++e) st.o[v][e] = 0.f;
         st.l_run = 0.f;
     }
-    mla_write_rows_wide<DQK, DV, C>(a, st, row, rq, split, head, head_ok, kb);
+    static_assert(kHeadsPerBlock * PartRow<kBF16, DV>::bytes <= (int)sizeof(lds), "output staging");
+    mla_write_rows_wide_staged<DQK, DV, C>(a, st, row, rq, split, hb, head, head_ok, w, col, kb, tid,
+                                           reinterpret_cast<char*>(lds));
 }
 
 // ================================================================ wide fp8 kernel

@@ -277,7 +277,7 @@ __device__ __forceinline__ void tile_compute(const u32x4* tile, uint32_t vmask, 
     }
 }
 
-// Epilogue shared by the bf16 and fp8 kernels.  One row per head: the
+// Epilogue of the two-waves-per-SIMD fp8 kernel.  One row per head: the
 // normalised value row in bf16 (the output row, or a split's partial row followed
 // by its fp32 m, l).  Rows are staged in the free tile buffers and written out
 // whole, 16 contiguous bytes per lane: two rounds of 64 heads, the pair p of a
@@ -329,6 +329,46 @@ __device__ __forceinline__ void mla_write_rows(const MlaArgs& a, const Bf16State
             st16(gbase + (size_t)(h0 + r) * grow + 16 * k, *reinterpret_cast<const u32x4*>(sb));
         }
         if (round == 0) barrier_lds();
+    }
+}
+
+// Epilogue of the bf16 kernels, staged through LDS: a workgroup's rows (one per
+// head: the normalised value row in bf16, or a split's partial row followed by its
+// fp32 m, l) are one contiguous block in memory, so each wave first writes its
+// share into `stage` (row pitch PartRow::bytes, conflict-free for the 8-byte
+// writes) and the whole block then leaves in 1 KiB stores.  The caller's lane holds
+// value dims d0 + 32*v + 8*i + 4*kb + jj (register 4*i + jj) of staging row `srow`
+// (head hb * 128 + srow); `ml` marks the one lane per row that writes m and l;
+// `l_tot` is the row's softmax sum.
+template <int DV, int VT, int NT>
+__device__ __forceinline__ void mla_write_rows_staged(const MlaArgs& a, const f32x16 (&o)[VT], float m_run,
+                                                      float l_tot, size_t row, int rq, int split, int hb, int srow,
+                                                      int d0, int kb, bool ml, int tid, char* stage)
+{
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    using P = PartRow<kBF16, DV>;
+    constexpr int SP = P::bytes;  // staged row pitch
+    const bool part_out = a.n_split > 1;
+    const int hb0 = hb * kHeadsPerBlock;
+    const int heads_here = min(kHeadsPerBlock, a.H - hb0);
+    char* gbase = part_out ? (char*)a.part + (((size_t)rq * a.n_split + split) * a.H + hb0) * P::bytes
+                           : (char*)a.out + (row * a.H + hb0) * (size_t)(DV * 2);
+    const int rch = part_out ? P::bytes / 16 : DV / 8;  // 16-byte chunks of a row in memory
+    barrier_lds();  // every wave is done with the tiles (and any flags read after the loop)
+    char* sb = stage + srow * SP + 2 * d0 + 8 * kb;
+#pragma unroll
+    for (int v = 0; v < VT; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x2*>(sb + 2 * (32 * v + 8 * i)) =
+                u32x2{pack_bf16x2(o[v][4 * i] * inv, o[v][4 * i + 1] * inv),
+                      pack_bf16x2(o[v][4 * i + 2] * inv, o[v][4 * i + 3] * inv)};
+    if (ml) *reinterpret_cast<f32x4*>(stage + srow * SP + P::vbytes) = f32x4{m_run, l_tot, 0.f, 0.f};
+    barrier_lds();
+    const int n = heads_here * rch;
+    for (int c = tid; c < n; c += NT) {
+        const int r = c / rch, k = c - r * rch;
+        st16(gbase + 16 * (size_t)c, *reinterpret_cast<const u32x4*>(stage + r * SP + 16 * k));
     }
 }
 
@@ -481,7 +521,15 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
         tile_compute<DQK, DV>(tB, vmB, qb, st, zc, xbuf, w, lane);
     }
 
-    mla_write_rows<DQK, DV, C>(a, st, tA, tB, hb, row, rq, split, head, head_ok, pair, half, col, kb, tid);
+    static_assert(kHeadsPerBlock * PartRow<kBF16, DV>::bytes <= (int)sizeof(lds), "output staging");
+    {
+        const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
+        if (a.n_split == 1 && a.lse && head_ok && half == 0 && kb == 0)
+            a.lse[row * a.H + head] = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+        mla_write_rows_staged<DV, C::VT, C::NT>(a, st.o, st.m_run, l_tot, row, rq, split, hb, pair * 32 + col,
+                                                C::VH * half, kb, half == 0 && kb == 0, tid,
+                                                reinterpret_cast<char*>(lds));
+    }
 }
 
 // ================================================================ wide bf16 kernel
@@ -749,49 +797,6 @@ __device__ __forceinline__ void mla_write_rows_wide(const MlaArgs& a, const Wide
         *reinterpret_cast<f32x4*>(rowp + P::vbytes) = f32x4{st.m_run, l_tot, 0.f, 0.f};
 }
 
-// Epilogue of the bf16 wide kernel, staged through LDS: the workgroup's rows
-// (one per head: the normalised value row in bf16, or a split's partial row
-// followed by its fp32 m, l) are one contiguous block in memory, so every wave
-// first writes its 32 rows into `stage` (pitch PartRow::bytes, conflict-free for
-// the 8-byte writes) and the whole block then leaves in 1 KiB stores.  A lane
-// holds dims 32*v + 8*i + 4*kb + jj (register 4*i + jj) of head `col`.
-template <int DQK, int DV, class C>
-__device__ __forceinline__ void mla_write_rows_wide_staged(const MlaArgs& a, const WideState<DQK, DV>& st,
-                                                           size_t row, int rq, int split, int hb, int head,
-                                                           bool head_ok, int w, int col, int kb, int tid,
-                                                           char* stage)
-{
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (a.n_split == 1 && a.lse && head_ok && kb == 0)
-        a.lse[row * a.H + head] = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-    using P = PartRow<kBF16, DV>;
-    constexpr int SP = P::bytes;  // staged row pitch
-    const bool part_out = a.n_split > 1;
-    const int hb0 = hb * kHeadsPerBlock;
-    const int heads_here = min(kHeadsPerBlock, a.H - hb0);
-    char* gbase = part_out ? (char*)a.part + (((size_t)rq * a.n_split + split) * a.H + hb0) * P::bytes
-                           : (char*)a.out + (row * a.H + hb0) * (size_t)(DV * 2);
-    const int rch = part_out ? P::bytes / 16 : DV / 8;  // 16-byte chunks of a row in memory
-    barrier_lds();  // every wave is done with the tiles (and the restart flags)
-    char* sb = stage + (w * 32 + col) * SP + 8 * kb;
-#pragma unroll
-    for (int v = 0; v < C::VT; ++v)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x2*>(sb + 2 * (32 * v + 8 * i)) =
-                u32x2{pack_bf16x2(st.o[v][4 * i] * inv, st.o[v][4 * i + 1] * inv),
-                      pack_bf16x2(st.o[v][4 * i + 2] * inv, st.o[v][4 * i + 3] * inv)};
-    if (kb == 0)
-        *reinterpret_cast<f32x4*>(stage + (w * 32 + col) * SP + P::vbytes) = f32x4{st.m_run, l_tot, 0.f, 0.f};
-    barrier_lds();
-    const int n = heads_here * rch;
-    for (int c = tid; c < n; c += C::NT) {
-        const int r = c / rch, k = c - r * rch;
-        st16(gbase + 16 * (size_t)c, *reinterpret_cast<const u32x4*>(stage + r * SP + 16 * k));
-    }
-}
-
 // Queries of the wide kernel staged through LDS: wave w's 32 query rows are
 // contiguous in memory, so they are loaded 1 KiB per instruction straight into
 // LDS in the tiles' padded layout (32 rows of PCH chunks, the pad chunk a copy of
@@ -958,8 +963,13 @@ __global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
         st.l_run = 0.f;
     }
     static_assert(kHeadsPerBlock * PartRow<kBF16, DV>::bytes <= (int)sizeof(lds), "output staging");
-    mla_write_rows_wide_staged<DQK, DV, C>(a, st, row, rq, split, hb, head, head_ok, w, col, kb, tid,
-                                           reinterpret_cast<char*>(lds));
+    {
+        const float l_tot = st.l_run + __shfl_xor(st.l_run, 32, 64);
+        if (a.n_split == 1 && a.lse && head_ok && kb == 0)
+            a.lse[row * a.H + head] = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+        mla_write_rows_staged<DV, C::VT, C::NT>(a, st.o, st.m_run, l_tot, row, rq, split, hb, w * 32 + col, 0, kb,
+                                                kb == 0, tid, reinterpret_cast<char*>(lds));
+    }
 }
 
 // ================================================================ wide fp8 kernel

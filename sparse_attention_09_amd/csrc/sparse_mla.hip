@@ -1639,7 +1639,9 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a)
     constexpr int NCK = P::vbytes / 16;       // chunks per value row
     constexpr int CPL = (NCK + 63) / 64;      // chunks per lane
     constexpr int kBatch = 4;
-    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // blocks go to the XCDs in contiguous eighths, as the MLA units do, so a query's
+    // partials are read on the XCD whose L2 received them
+    const int wid = xcd_unit(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
     const int lane = lane_id();
     if (wid >= a.B * a.t_count * a.H) return;
     const int head = wid % a.H, rq = wid / a.H;
@@ -1724,7 +1726,8 @@ hipError_t launch_combine(const MlaArgs& a, hipStream_t s)
 {
     if (a.n_split == 1) return hipSuccess;
     const long long waves = (long long)a.B * a.t_count * a.H;
-    mla_combine_kernel<DT, DV><<<dim3((unsigned)((waves + 3) / 4)), 256, 0, s>>>(a);
+    const long long blocks = (waves + 3) / 4;
+    mla_combine_kernel<DT, DV><<<dim3((unsigned)(8 * ((blocks + 7) / 8))), 256, 0, s>>>(a);
     return hipGetLastError();
 }
 

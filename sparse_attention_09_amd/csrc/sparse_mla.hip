@@ -1752,8 +1752,8 @@ hipError_t launch_wide(const MlaArgs& a, hipStream_t s)
 }
 
 // Tiles of one split's index list.  The wide kernels win on long lists; on the
-// short lists of split decode their one-wave-per-SIMD prologue (twice the q
-// loads per wave) costs more than they save.
+// 4-tile lists of a 16-way split (16 decode queries at K = 2048) the bf16 wide
+// kernel measured 31.1 us against 29.4-29.8 us for the two-waves-per-SIMD one.
 int split_tiles(const MlaArgs& a)
 {
     const int per = (a.K + a.n_split - 1) / a.n_split;

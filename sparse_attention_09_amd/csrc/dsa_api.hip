@@ -79,7 +79,7 @@ dsa::IndexerArgs indexer_args(const dsa_shape* s, const void* q, const float* qs
                               const float* ks, const int32_t* kv_len, float* scores, int t_begin, int t_count,
                               int fill)
 {
-    dsa::IndexerArgs a;
+    dsa::IndexerArgs a{};
     a.B = s->batch;
     a.T = s->n_q;
     a.Lmax = s->max_kv;
@@ -99,6 +99,8 @@ dsa::IndexerArgs indexer_args(const dsa_shape* s, const void* q, const float* qs
     a.fill = fill;
     a.zero = nullptr;
     a.zero_words = 0;
+    a.hist = nullptr;
+    a.coarse = nullptr;
     a.sel_cand = nullptr;
     a.sel_cap = 0;
     a.sel_k = 0;
@@ -609,16 +611,41 @@ dsa_status check_forward_args(const dsa_shape* s, const void* q_idx, const float
     return DSA_OK;
 }
 
-// One chunk's index scores and top-k through the score rows.
+// The top-k counters of a query chunk that a launch before the indexer may clear
+// (0 when the chunk's top-k needs none).  A decode chunk (the indexer's decode
+// tiling, at most 2 queries) on the split top-k also gets its row histograms
+// from the indexer, so its counters must be zero before the indexer starts.
+size_t fused_hist_zero_words(const dsa_shape* s, const float* scores, const int32_t* kv_len, int32_t* idx,
+                             void* part, int t0, int cnt)
+{
+    if (cnt > 2) return 0;
+    return dsa::topk_zero_words(topk_args(s, scores, kv_len, idx, part, t0, cnt));
+}
+
+// One chunk's index scores and top-k through the score rows.  `cleared`: a
+// launch before this one cleared the chunk's top-k counters
+// (fused_hist_zero_words words at `part`).
 hipError_t forward_scores_topk(const dsa_shape* s, const void* qi, const float* qsc, const float* w, const void* k_idx,
                                const float* k_scale, const int32_t* kv_len, float* scores, int32_t* idx, void* part,
-                               int t0, int cnt, hipStream_t stream)
+                               int t0, int cnt, bool cleared, hipStream_t stream)
 {
     dsa::IndexerArgs ia = indexer_args(s, qi, qsc, w, k_idx, k_scale, kv_len, scores, t0, cnt, 0);
     dsa::TopkArgs ta = topk_args(s, scores, kv_len, idx, part, t0, cnt);
-    // the indexer clears the top-k's counters, which saves the top-k a launch
     const size_t zw = dsa::topk_zero_words(ta);
-    if (zw > 0) {
+    if (zw > 0 && cnt <= 2) {
+        // decode: the indexer builds the row histograms as it writes the scores,
+        // which saves the top-k its histogram pass over the score rows
+        if (!cleared) {
+            const hipError_t e = dsa::launch_topk_zero(ta, stream);
+            if (e != hipSuccess) return e;
+        }
+        const dsa::TopkHist th = dsa::topk_split_hist(ta);
+        ia.hist = th.hist;
+        ia.coarse = th.coarse;
+        ta.pre_zeroed = 1;
+        ta.hist_done = 1;
+    } else if (zw > 0) {
+        // the indexer clears the top-k's counters, which saves the top-k a launch
         ia.zero = (uint32_t*)part;
         ia.zero_words = (long long)zw;
         ta.pre_zeroed = 1;
@@ -648,14 +675,19 @@ dsa_status forward_run(const dsa_shape* s, const void* q_idx, const float* w, co
     const float* qms = nullptr;
     const bool fp8_idx = s->idx_dtype == DSA_FP8_E4M3, fp8_mla = s->mla_dtype == DSA_FP8_E4M3;
     const int64_t idx_rows = (int64_t)s->batch * s->n_q * s->idx_heads;
+    // the fp8 index queries' preparation also clears the first chunk's top-k counters
+    // when that chunk's indexer builds the top-k histograms
+    const size_t zw0 =
+        (fp8_idx && !lay.stream) ? fused_hist_zero_words(s, scores, kv_len, idx, part, 0, tc < s->n_q ? tc : s->n_q) : 0;
+    uint32_t* const zp0 = zw0 > 0 ? (uint32_t*)part : nullptr;
     if (fp8_idx && fp8_mla) {  // both query preparations in one launch
         uint8_t* qc = (uint8_t*)(ws + lay.qcodes);
         float* qs = (float*)(ws + lay.qscale);
         uint8_t* mqc = (uint8_t*)(ws + lay.mqcodes);
         float* mqs = (float*)(ws + lay.mqscale);
         const int64_t mla_rows = (int64_t)s->batch * s->n_q * s->heads;
-        if (dsa::launch_fp8_queries(idx_rows, s->idx_dim, q_idx, qc, qs, mla_rows, s->qk_dim, q, mqc, mqs, stream) !=
-            hipSuccess)
+        if (dsa::launch_fp8_queries(idx_rows, s->idx_dim, q_idx, qc, qs, mla_rows, s->qk_dim, q, mqc, mqs, stream, zp0,
+                                    (long long)zw0) != hipSuccess)
             return DSA_ERR_HIP;
         qi = qc;
         qsc = qs;
@@ -664,7 +696,8 @@ dsa_status forward_run(const dsa_shape* s, const void* q_idx, const float* w, co
     } else if (fp8_idx) {
         uint8_t* qc = (uint8_t*)(ws + lay.qcodes);
         float* qs = (float*)(ws + lay.qscale);
-        if (dsa::launch_rotate_quant(idx_rows, s->idx_dim, q_idx, DSA_BF16, qc, qs, stream) != hipSuccess)
+        if (dsa::launch_rotate_quant(idx_rows, s->idx_dim, q_idx, DSA_BF16, qc, qs, stream, zp0, (long long)zw0) !=
+            hipSuccess)
             return DSA_ERR_HIP;
         qi = qc;
         qsc = qs;
@@ -685,8 +718,8 @@ dsa_status forward_run(const dsa_shape* s, const void* q_idx, const float* w, co
             ia.sel_idx = idx;
             if (dsa::launch_index_topk(s->idx_dtype, ia, stream) != hipSuccess) return DSA_ERR_HIP;
         } else {
-            if (forward_scores_topk(s, qi, qsc, w, k_idx, k_scale, kv_len, scores, idx, part, t0, cnt, stream) !=
-                hipSuccess)
+            if (forward_scores_topk(s, qi, qsc, w, k_idx, k_scale, kv_len, scores, idx, part, t0, cnt,
+                                    t0 == 0 && zw0 > 0, stream) != hipSuccess)
                 return DSA_ERR_HIP;
         }
         const int ns = dsa::mla_split_count(s->batch, cnt, s->heads, s->topk);

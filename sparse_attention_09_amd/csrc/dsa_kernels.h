@@ -24,6 +24,12 @@ struct IndexerArgs {
     int fill;               // write -inf for every s > p(t)
     uint32_t* zero;         // optional: words [0, zero_words) are cleared by the launch
     long long zero_words;   //   (a following top-k's counters, see topk_zero_words)
+    // optional (decode tiling, t_count <= 2): the split top-k's row histograms
+    // (topk_split_hist), already zero, receive the counts of the scores written:
+    // per row r = b * t_count + (t - t_begin), hist[r * 4096 + (key >> 20)] and
+    // coarse[r * 64 + (key >> 26)] for key = float_key(score) of positions 0 .. p(t)
+    uint32_t* hist;
+    uint32_t* coarse;
     // streaming top-k (launch_index_topk): per chunk row a list of sel_cap
     // (key, position) pairs in place of the score row; the top sel_k positions of
     // row (b, t) go to sel_idx[(b * T + t) * sel_k ..]
@@ -43,6 +49,7 @@ struct TopkArgs {
     int32_t* idx;
     void* ws;               // topk_workspace_bytes(B, t_count, Lmax, K) bytes, 16-byte aligned
     int pre_zeroed;         // the first topk_zero_words(*this) words of ws are already zero
+    int hist_done;          // split path: the row histograms were built with the scores
 };
 
 // Sparse absorbed MLA for queries [t_begin, t_begin + t_count).
@@ -73,6 +80,15 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 // Words at the start of the workspace that the launch clears first (0 when none);
 // a preceding kernel on the same stream may clear them instead (pre_zeroed).
 size_t topk_zero_words(const TopkArgs& a);
+// The split path's row histograms inside the workspace (null when the launch does
+// not take the split path); a launch that fills them sets hist_done.
+struct TopkHist {
+    uint32_t* hist;    // [B * t_count][4096]
+    uint32_t* coarse;  // [B * t_count][64]
+};
+TopkHist topk_split_hist(const TopkArgs& a);
+// Clears the topk_zero_words(a) words at the start of a.ws.
+hipError_t launch_topk_zero(const TopkArgs& a, hipStream_t s);
 
 // Sparse MLA backward for queries [t_begin, t_begin + t_count) of every
 // sequence.  Chunk rows are r = b * t_count + (t - t_begin); Hp = H rounded up
@@ -105,8 +121,10 @@ int mla_split_count(int B, int t_count, int H, int K);
 size_t mla_partial_bytes(int dtype, int B, int t_count, int H, int Dv, int n_split);
 hipError_t launch_mla(int dtype, const MlaArgs& a, hipStream_t s);
 
+// zero / zero_words: optional words that the launch also clears (a following
+// top-k's counters).
 hipError_t launch_rotate_quant(int64_t rows, int dim, const void* x, int x_dtype, uint8_t* codes, float* scales,
-                               hipStream_t s);
+                               hipStream_t s, uint32_t* zero = nullptr, long long zero_words = 0);
 // Per-row e4m3 quantisation without rotation (dim a multiple of 16, at most 1024):
 // codes at codes + row * cpitch; the scale to scales[row], or with tail into the
 // 16 bytes after the codes (fp32 scale, 12 zero bytes).
@@ -115,7 +133,8 @@ hipError_t launch_quant_rows(int64_t rows, int dim, const void* x, int x_dtype, 
 // The index queries' rotate + quantise (rows x dim, bf16) and the MLA queries'
 // quantisation (mrows x mdim, bf16) in one launch, with the results of the two.
 hipError_t launch_fp8_queries(int64_t rows, int dim, const void* x, uint8_t* codes, float* scales, int64_t mrows,
-                              int mdim, const void* mx, uint8_t* mcodes, float* mscales, hipStream_t s);
+                              int mdim, const void* mx, uint8_t* mcodes, float* mscales, hipStream_t s,
+                              uint32_t* zero = nullptr, long long zero_words = 0);
 // Rotate + quantise rows [B, t_new, dim] into cache rows kv_len[b] - t_new + t of [B, max_kv, dim].
 hipError_t launch_cache_append(int batch, int t_new, int max_kv, int dim, const void* x, int x_dtype,
                                const int32_t* kv_len, uint8_t* codes, float* scales, hipStream_t s);

@@ -160,13 +160,19 @@ __device__ __forceinline__ void load_strip(const IndexerArgs& a, int b, int stri
     }
 }
 
+// Row histograms of the split top-k built beside the decode scores: one LDS
+// histogram of the top 12 key bits per query row of the workgroup, added to the
+// row's global histograms (fine and 64-bin coarse) when the workgroup ends.
+constexpr int kIdxHistBins = 4096;
+
 template <int DT, int D, int HT, int QPW, int TPW>
 __device__ __forceinline__ void score_strip(const IndexerArgs& a, int b, int strip,
                                             const u32x4 (&kb)[TPW][Share<DT, D>::nch],
                                             const float (&ks)[StripOut<TPW>::n],
                                             const u32x4 (&qa)[QPW][HT][Share<DT, D>::nch],
                                             const float (&wv)[QPW][HT][4], const int (&tq)[QPW],
-                                            const int (&pq)[QPW], const bool (&vq)[QPW], int kend)
+                                            const int (&pq)[QPW], const bool (&vq)[QPW], int kend,
+                                            uint32_t (*lh)[kIdxHistBins])
 {
     constexpr int NCH = Share<DT, D>::nch;
     constexpr int NO = StripOut<TPW>::n;
@@ -192,10 +198,13 @@ __device__ __forceinline__ void score_strip(const IndexerArgs& a, int b, int str
             const int tile = (strip * TPW + 4 * j + g) * 16;
             const int key = tile + n;
             if (4 * j + g < TPW && tile < kend && key < a.Lmax) {
-                if (key <= pq[q])
-                    row[key] = v * ks[j];
-                else if (a.fill)
+                if (key <= pq[q]) {
+                    const float sv = v * ks[j];
+                    row[key] = sv;
+                    if (a.hist) atomicAdd(&lh[q][float_key(sv) >> 20], 1u);
+                } else if (a.fill) {
                     row[key] = -INFINITY;
+                }
             }
         }
     }
@@ -211,7 +220,12 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a)
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int b = blockIdx.z;
+    __shared__ uint32_t lh[QPW][kIdxHistBins];
     clear_words(a);
+    if (a.hist) {
+        for (int i = threadIdx.x; i < QPW * kIdxHistBins; i += 256) (&lh[0][0])[i] = 0u;
+        __syncthreads();
+    }
     const int L = seq_len(a, b);
 
     int tq[QPW], pq[QPW];
@@ -243,11 +257,11 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a)
         for (int s0 = w0;; s0 += 2 * W) {
             const int s1 = s0 + W;
             load_strip<DT, D, TPW>(a, b, s1 < n_load ? s1 : s0, kend, kB, sB);
-            score_strip<DT, D, HT, QPW, TPW>(a, b, s0, kA, sA, qa, wv, tq, pq, vq, kend);
+            score_strip<DT, D, HT, QPW, TPW>(a, b, s0, kA, sA, qa, wv, tq, pq, vq, kend, lh);
             if (s1 >= n_load) break;
             const int s2 = s1 + W;
             load_strip<DT, D, TPW>(a, b, s2 < n_load ? s2 : s1, kend, kA, sA);
-            score_strip<DT, D, HT, QPW, TPW>(a, b, s1, kB, sB, qa, wv, tq, pq, vq, kend);
+            score_strip<DT, D, HT, QPW, TPW>(a, b, s1, kB, sB, qa, wv, tq, pq, vq, kend, lh);
             if (s2 >= n_load) break;
         }
     }
@@ -257,6 +271,28 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs a)
 #pragma unroll
             for (int q = 0; q < QPW; ++q)
                 if (vq[q]) a.scores[b * a.ld_b + (long long)(tq[q] - a.t_begin) * a.ld_t + s] = -INFINITY;
+    }
+    if (a.hist) {
+        // this workgroup's counts join the rows' histograms: the non-zero fine bins,
+        // and the coarse bins (thread t sums fine bins [16 t, 16 t + 16), four
+        // threads per coarse bin)
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < QPW; ++q) {
+            if (!vq[q]) continue;
+            const size_t r = (size_t)b * a.t_count + (tq[q] - a.t_begin);
+            uint32_t* gh = a.hist + r * kIdxHistBins;
+            for (int i = threadIdx.x; i < kIdxHistBins; i += 256) {
+                const uint32_t c = lh[q][i];
+                if (c) atomicAdd(&gh[i], c);
+            }
+            uint32_t cs = 0;
+#pragma unroll
+            for (int j = 0; j < kIdxHistBins / 256; ++j) cs += lh[q][threadIdx.x * (kIdxHistBins / 256) + j];
+            cs += __shfl_xor(cs, 1, 64);
+            cs += __shfl_xor(cs, 2, 64);
+            if ((threadIdx.x & 3) == 0 && cs) atomicAdd(&a.coarse[r * 64 + threadIdx.x / 4], cs);
+        }
     }
 }
 

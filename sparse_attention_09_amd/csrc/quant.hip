@@ -140,10 +140,25 @@ __device__ __forceinline__ void rotate_quant_rows(int64_t rows, const void* x, u
     }
 }
 
+// Optional words cleared by a launch beside its own work (a following top-k's
+// counters): a grid-stride loop over the launch's threads.
+struct ClearWords {
+    uint32_t* p;
+    long long n;
+    __device__ __forceinline__ void run() const
+    {
+        if (p == nullptr) return;
+        const long long nthreads = (long long)gridDim.x * blockDim.x;
+        for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += nthreads) p[i] = 0u;
+    }
+};
+
 template <int DIM, int XT>
 __global__ __launch_bounds__(256) void rotate_quant_kernel(int64_t rows, const void* x, uint8_t* codes,
-                                                           float* scales, double inv_sqrt_dim, RowMap map)
+                                                           float* scales, double inv_sqrt_dim, RowMap map,
+                                                           ClearWords clear)
 {
+    clear.run();
     rotate_quant_rows<DIM, XT>(rows, x, codes, scales, inv_sqrt_dim, map, blockIdx.x, gridDim.x);
 }
 
@@ -225,8 +240,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(int64_t rows, int dim, 
 template <int DIM>
 __global__ __launch_bounds__(256) void fp8_queries_kernel(int64_t rows, const void* x, uint8_t* codes, float* scales,
                                                           double inv_sqrt_dim, int g1, int64_t mrows, int mdim,
-                                                          const void* mx, uint8_t* mcodes, float* mscales)
+                                                          const void* mx, uint8_t* mcodes, float* mscales,
+                                                          ClearWords clear)
 {
+    clear.run();
     if ((int)blockIdx.x < g1)
         rotate_quant_rows<DIM, kBF16>(rows, x, codes, scales, inv_sqrt_dim, RowMap{nullptr, 0, 0}, blockIdx.x, g1);
     else
@@ -234,28 +251,29 @@ __global__ __launch_bounds__(256) void fp8_queries_kernel(int64_t rows, const vo
 }
 
 template <int DIM>
-hipError_t launch_dim(int64_t rows, const void* x, int xt, uint8_t* codes, float* scales, RowMap map, hipStream_t s)
+hipError_t launch_dim(int64_t rows, const void* x, int xt, uint8_t* codes, float* scales, RowMap map, hipStream_t s,
+                      ClearWords clear)
 {
     const double inv = 1.0 / sqrt((double)DIM);
     constexpr int RPB = 4 * (64 / (DIM / 8));  // rows per block pass
     const dim3 grid((unsigned)std::min<int64_t>((rows + RPB - 1) / RPB, 8192));
     if (xt == kBF16)
-        rotate_quant_kernel<DIM, kBF16><<<grid, 256, 0, s>>>(rows, x, codes, scales, inv, map);
+        rotate_quant_kernel<DIM, kBF16><<<grid, 256, 0, s>>>(rows, x, codes, scales, inv, map, clear);
     else
-        rotate_quant_kernel<DIM, kF32><<<grid, 256, 0, s>>>(rows, x, codes, scales, inv, map);
+        rotate_quant_kernel<DIM, kF32><<<grid, 256, 0, s>>>(rows, x, codes, scales, inv, map, clear);
     return hipGetLastError();
 }
 
 hipError_t launch_map(int64_t rows, int dim, const void* x, int x_dtype, uint8_t* codes, float* scales, RowMap map,
-                      hipStream_t s)
+                      hipStream_t s, ClearWords clear = ClearWords{nullptr, 0})
 {
     if (rows <= 0) return hipSuccess;
     switch (dim) {
-        case 16: return launch_dim<16>(rows, x, x_dtype, codes, scales, map, s);
-        case 32: return launch_dim<32>(rows, x, x_dtype, codes, scales, map, s);
-        case 64: return launch_dim<64>(rows, x, x_dtype, codes, scales, map, s);
-        case 128: return launch_dim<128>(rows, x, x_dtype, codes, scales, map, s);
-        case 256: return launch_dim<256>(rows, x, x_dtype, codes, scales, map, s);
+        case 16: return launch_dim<16>(rows, x, x_dtype, codes, scales, map, s, clear);
+        case 32: return launch_dim<32>(rows, x, x_dtype, codes, scales, map, s, clear);
+        case 64: return launch_dim<64>(rows, x, x_dtype, codes, scales, map, s, clear);
+        case 128: return launch_dim<128>(rows, x, x_dtype, codes, scales, map, s, clear);
+        case 256: return launch_dim<256>(rows, x, x_dtype, codes, scales, map, s, clear);
         default: return hipErrorInvalidValue;
     }
 }
@@ -263,9 +281,9 @@ hipError_t launch_map(int64_t rows, int dim, const void* x, int x_dtype, uint8_t
 }  // namespace
 
 hipError_t launch_rotate_quant(int64_t rows, int dim, const void* x, int x_dtype, uint8_t* codes, float* scales,
-                               hipStream_t s)
+                               hipStream_t s, uint32_t* zero, long long zero_words)
 {
-    return launch_map(rows, dim, x, x_dtype, codes, scales, RowMap{nullptr, 0, 0}, s);
+    return launch_map(rows, dim, x, x_dtype, codes, scales, RowMap{nullptr, 0, 0}, s, ClearWords{zero, zero_words});
 }
 
 hipError_t launch_quant_rows(int64_t rows, int dim, const void* x, int x_dtype, uint8_t* codes, int64_t cpitch,
@@ -282,17 +300,19 @@ hipError_t launch_quant_rows(int64_t rows, int dim, const void* x, int x_dtype, 
 }
 
 hipError_t launch_fp8_queries(int64_t rows, int dim, const void* x, uint8_t* codes, float* scales, int64_t mrows,
-                              int mdim, const void* mx, uint8_t* mcodes, float* mscales, hipStream_t s)
+                              int mdim, const void* mx, uint8_t* mcodes, float* mscales, hipStream_t s,
+                              uint32_t* zero, long long zero_words)
 {
     if (dim != 128 || mdim <= 0 || mdim % 16 != 0 || mdim > 1024 || rows <= 0 || mrows <= 0) {
-        const hipError_t e = launch_rotate_quant(rows, dim, x, kBF16, codes, scales, s);
+        const hipError_t e = launch_rotate_quant(rows, dim, x, kBF16, codes, scales, s, zero, zero_words);
         return e != hipSuccess ? e : launch_quant_rows(mrows, mdim, mx, kBF16, mcodes, mdim, mscales, 0, s);
     }
     constexpr int RPB = 4 * (64 / (128 / 8));  // index-query rows per block pass
     const int g1 = (int)std::min<int64_t>((rows + RPB - 1) / RPB, 8192);
     const int g2 = (int)std::min<int64_t>((mrows + 3) / 4, 8192);
     fp8_queries_kernel<128><<<dim3((unsigned)(g1 + g2)), 256, 0, s>>>(rows, x, codes, scales, 1.0 / sqrt(128.0), g1,
-                                                                       mrows, mdim, mx, mcodes, mscales);
+                                                                       mrows, mdim, mx, mcodes, mscales,
+                                                                       ClearWords{zero, zero_words});
     return hipGetLastError();
 }
 

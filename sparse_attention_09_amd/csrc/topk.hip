@@ -804,6 +804,22 @@ size_t topk_zero_words(const TopkArgs& a)
     return (a.t_count > 0 && a.B > 0 && use_split(a)) ? split_zero_words((size_t)a.B * a.t_count) : 0;
 }
 
+TopkHist topk_split_hist(const TopkArgs& a)
+{
+    if (topk_zero_words(a) == 0) return TopkHist{nullptr, nullptr};
+    const size_t rows = (size_t)a.B * a.t_count;
+    uint32_t* p = (uint32_t*)a.ws;  // the layout of split_ws
+    return TopkHist{p, p + rows * kHistBins};
+}
+
+hipError_t launch_topk_zero(const TopkArgs& a, hipStream_t s)
+{
+    const size_t zw = topk_zero_words(a);
+    if (zw == 0) return hipSuccess;
+    topk_zero_kernel<<<dim3((unsigned)std::min<size_t>((zw + 255) / 256, 1024)), 256, 0, s>>>((uint32_t*)a.ws, zw);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s)
 {
     if (a.t_count <= 0 || a.B <= 0) return hipSuccess;
@@ -816,7 +832,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s)
     if (!a.pre_zeroed)
         topk_zero_kernel<<<dim3((unsigned)std::min<size_t>((zw + 255) / 256, 1024)), 256, 0, s>>>((uint32_t*)a.ws, zw);
     const dim3 grid((a.Lmax + kChunk - 1) / kChunk, rows);
-    topk_hist_kernel<<<grid, 256, 0, s>>>(a);
+    if (!a.hist_done) topk_hist_kernel<<<grid, 256, 0, s>>>(a);
     topk_filter_kernel<<<grid, 256, 0, s>>>(a);
     topk_finish_kernel<<<dim3(rows), kTopkThreads, 0, s>>>(a);
     return hipGetLastError();

@@ -239,6 +239,53 @@ def test_forward_is_deterministic_and_stateless(dsa):
     assert not torch.equal(ra[1], rb[1])
 
 
+DECODE_SELECTION_CASES = [
+    # idx dtype, B, T, Lmax, lens, K, chunked workspace
+    ("bf16", 6, 1, 32768, [32768, 30000, 5000, 1, 0, 20000], 2048, False),
+    ("bf16", 4, 2, 20000, [20000, 15000, 3, 2], 512, False),
+    ("bf16", 3, 2, 16384, [16384, 9000, 2], 1024, True),
+    ("fp8", 4, 1, 40000, [40000, 1000, 39000, 7], 2048, False),
+    ("fp8", 3, 2, 16384, [16384, 9000, 2], 1024, True),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SELECTION_CASES)
+def test_forward_decode_selection_equals_stage_path(dsa, case):
+    """At decode shapes dsa_forward builds the split top-k's row histograms inside the
+    indexer launch (the counters cleared by the fp8 query preparation or a fill launch);
+    its selection must equal dsa_index_scores followed by dsa_topk bit for bit, for
+    ragged, empty and shorter-than-K sequences, one or two queries per sequence, and a
+    workspace small enough to run the queries one at a time."""
+    dt, B, T, Lmax, lens, K, chunked = case
+    announce(f"forward decode selection == index_scores + topk {case}")
+    H, D, heads, dqk, dv = 64, 128, 16, 192, 128
+    s = dsa.DsaShape(batch=B, n_q=T, max_kv=Lmax, idx_heads=H, idx_dim=D, topk=K, heads=heads, qk_dim=dqk,
+                     v_dim=dv, sm_scale=dqk ** -0.5, idx_dtype=dt, mla_dtype="bf16")
+    g = torch.Generator().manual_seed(11 * Lmax + T)
+    q_idx = torch.randn(B, T, H, D, generator=g).to(DEV, torch.bfloat16)
+    k_idx = torch.randn(B, Lmax, D, generator=g).to(DEV, torch.bfloat16)
+    w = torch.randn(B, T, H, generator=g).to(DEV)
+    q = (torch.randn(B, T, heads, dqk, generator=g) * dqk ** -0.5).to(DEV, torch.bfloat16)
+    kv = (torch.randn(B, Lmax, dqk, generator=g) * dqk ** -0.5).to(DEV, torch.bfloat16)
+    kl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    if dt == "fp8":
+        kc, ks = dsa.rotate_quant_fp8(k_idx)
+        qc, qs = dsa.rotate_quant_fp8(q_idx)
+        scores = dsa.index_scores(s, qc, w, kc, kl, q_scale=qs, k_scale=ks)
+        k_fwd, ks_fwd = kc, ks
+    else:
+        scores = dsa.index_scores(s, q_idx, w, k_idx, kl)
+        k_fwd, ks_fwd = k_idx, None
+    ref = dsa.topk(s, scores, kl)
+    ws = None
+    if chunked:
+        ws = torch.empty(dsa.forward_min_workspace_size(s), dtype=torch.uint8, device=DEV)
+    for _ in range(2):  # a second call on the same workspace starts from what the first left there
+        idx, _, _ = dsa.forward(s, q_idx, w, k_fwd, q, kv, kl, k_scale=ks_fwd, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref)
+
+
 def test_forward_ragged_lengths(dsa, orc):
     wl = get("decode_32k").replace(batch=4, n_q=3, max_kv=5000, kv_len=5000)
     lens = [5000, 2049, 1000, 3]

@@ -166,14 +166,27 @@ __device__ __forceinline__ void gather_issue(const char* kvb, uint32_t off, u32x
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(kvb), "{m0}"(lds) : "memory");
 }
 
+// Direct loads of wave w that touch the tile (the others would fill only the
+// dummy tail past it): the wave's loads k cover 64-chunk groups w + NW * k.
 template <class C>
+__device__ __forceinline__ int tile_loads(int w)
+{
+    constexpr int G = (C::TILE_CH + 63) / 64;
+    return (G - w + C::NW - 1) / C::NW;
+}
+
+// SKIP_TAIL: leave out the loads that fill only the dummy tail; the caller's waits
+// then count tile_loads(w) loads per tile for wave w.
+template <class C, bool SKIP_TAIL = false>
 __device__ __forceinline__ void gather_tile_asm(const char* kvb, const uint32_t* lrow, int j0, int w, int lane,
                                                 u32x4* dst)
 {
     uint32_t off[C::DMA];
     gather_offsets<C>(lrow, j0, w, lane, off);
+    const int n = SKIP_TAIL ? tile_loads<C>(__builtin_amdgcn_readfirstlane(w)) : C::DMA;
 #pragma unroll
-    for (int k = 0; k < C::DMA; ++k) gather_issue<C>(kvb, off[k], dst, w, k);
+    for (int k = 0; k < C::DMA; ++k)
+        if (k < n) gather_issue<C>(kvb, off[k], dst, w, k);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads (whose vmcnt(0)
@@ -504,19 +517,19 @@ __global__ __launch_bounds__(512) void mla_bf16_kernel(MlaArgs a)
     const float zc = a.sm_scale * kLog2e;
 
     // tile `it` lives in buffer it % 2; each step issues tile it + 1 into the other buffer
-    if (n_tiles > 0) gather_tile_asm<C>(kvb, lrow, 0, w, lane, tA);
+    if (n_tiles > 0) gather_tile_asm<C, true>(kvb, lrow, 0, w, lane, tA);
 #pragma unroll 1
     for (int it = 0; it < n_tiles; it += 2) {
         barrier_lds_vm();
         // the tile's mask is read together with the next tile's row offsets
         const uint32_t vmA = tmask[it];
-        if (it + 1 < n_tiles) gather_tile_asm<C>(kvb, lrow, (it + 1) * kTileKeys, w, lane, tB);
+        if (it + 1 < n_tiles) gather_tile_asm<C, true>(kvb, lrow, (it + 1) * kTileKeys, w, lane, tB);
         __builtin_amdgcn_sched_barrier(0);
         tile_compute<DQK, DV>(tA, vmA, qb, st, zc, xbuf, w, lane);
         if (it + 1 >= n_tiles) break;
         barrier_lds_vm();
         const uint32_t vmB = tmask[it + 1];
-        if (it + 2 < n_tiles) gather_tile_asm<C>(kvb, lrow, (it + 2) * kTileKeys, w, lane, tA);
+        if (it + 2 < n_tiles) gather_tile_asm<C, true>(kvb, lrow, (it + 2) * kTileKeys, w, lane, tA);
         __builtin_amdgcn_sched_barrier(0);
         tile_compute<DQK, DV>(tB, vmB, qb, st, zc, xbuf, w, lane);
     }
@@ -609,6 +622,7 @@ struct PendingGather {
     const uint32_t* lrow;  // entry j0 of the tile's list
     int r, c;
     bool active;
+    int nload = C::DMA;    // loads this wave issues (tile_loads when the tail is skipped)
     __device__ __forceinline__ void start(int w, int lane)
     {
         int ln = lane;
@@ -673,7 +687,7 @@ __device__ __forceinline__ bool tile_compute_wide(const u32x4* tile, uint32_t vm
             else
                 mfma32_bf16_vacc(ka, qb[st_], sacc);
             if (st_ % GAP == 0 && st_ / GAP < C::DMA) goff = pg.next_offset();
-            if (st_ % GAP == GAP - 1 && st_ / GAP < C::DMA && pg.active)
+            if (st_ % GAP == GAP - 1 && st_ / GAP < C::DMA && st_ / GAP < pg.nload && pg.active)
                 gather_issue<C>(pg.kvb, goff, pg.dst, w, st_ / GAP);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -924,20 +938,27 @@ __global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
     st.m_run = -INFINITY;
     st.l_run = 0.f;
     const float zc = a.sm_scale * kLog2e;
+    const int nload = tile_loads<C>(__builtin_amdgcn_readfirstlane(w));  // C::DMA or C::DMA - 1
+    static_assert((((C::TILE_CH + 63) / 64) / C::NW) >= C::DMA - 1, "per-wave load counts");
 
 #pragma unroll 1
     for (;;) {
-        if (n_tiles > 0) gather_tile_asm<C>(kvb, lrow, 0, w, lane, tiles);
-        if (n_tiles > 1) gather_tile_asm<C>(kvb, lrow, kTileKeys, w, lane, tiles + C::BUF_CH);
+        if (n_tiles > 0) gather_tile_asm<C, true>(kvb, lrow, 0, w, lane, tiles);
+        if (n_tiles > 1) gather_tile_asm<C, true>(kvb, lrow, kTileKeys, w, lane, tiles + C::BUF_CH);
         int cur = 0;
 #pragma unroll 1
         for (int it = 0; it < n_tiles; ++it) {
             // tile `it` has landed everywhere and every wave is done with the buffer
-            // it computed two tiles ago, which the gather below refills
-            if (it + 1 < n_tiles)
-                barrier_vm<C::DMA>();
-            else
+            // it computed two tiles ago, which the gather below refills (a wave's
+            // loads retire in order: at most the next tile's may still be in flight)
+            if (it + 1 < n_tiles) {
+                if (nload == C::DMA)
+                    barrier_vm<C::DMA>();
+                else
+                    barrier_vm<C::DMA - 1>();
+            } else {
                 barrier_vm<0>();
+            }
             if (it > 0 && restart[(it - 1) & 1]) break;  // read after the barrier: the same for every wave
             const uint32_t vm = tmask[it];
             const int nxt = cur == 0 ? 2 : cur - 1;  // (cur + 2) % 3
@@ -946,6 +967,7 @@ __global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
             pg.dst = tiles + nxt * C::BUF_CH;
             pg.lrow = lrow + min(it + 2, n_tiles - 1) * kTileKeys;
             pg.active = it + 2 < n_tiles;
+            pg.nload = nload;
             pg.start(w, lane);
             if (tile_compute_wide<DQK, DV>(tiles + cur * C::BUF_CH, vm, qb, st, zc, lane, w, pg) && lane == 0)
                 restart[it & 1] = 1;

@@ -63,7 +63,11 @@ typedef enum {
     DSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required             */
     DSA_ERR_UNSUPPORTED = -6, /* valid but not built (a head width, a head count)    */
     DSA_ERR_HIP = -7,         /* the HIP runtime reported an error on launch         */
-    DSA_ERR_SCRATCH = -8      /* dsa_forward_noalloc: needs more than its scratch    */
+    DSA_ERR_SCRATCH = -8,     /* dsa_forward_noalloc: needs more than its scratch    */
+    /* Not statuses: they give the type the range of int32_t, so that any int a
+     * caller passes to dsa_status_string is a valid value of the type. */
+    DSA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    DSA_STATUS_RANGE_MAX_ = 2147483647
 } dsa_status;
 
 /* Problem description.  Dtype fields hold dsa_dtype values. */
@@ -89,6 +93,8 @@ typedef struct {
  *   MLA      (mla_dtype, qk_dim, v_dim) in {(F32, 80, 64), (BF16, 576, 512),
  *            (BF16, 192, 128), (FP8_E4M3, 576, 512)}; any heads >= 1.
  *   top-k    topk <= 4096, max_kv <= 1 << 20.
+ *   all      batch <= 65535; batch * n_q <= 2^30; with an MLA,
+ *            batch * n_q * heads <= 2^30.
  */
 
 /* Lightning-indexer scores.

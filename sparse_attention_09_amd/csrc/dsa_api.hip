@@ -20,6 +20,11 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxTopk = 4096;
 constexpr int kMaxMlaSplit = 16;  // most list splits of one query (mla_split_count)
 constexpr int kMaxKv = 1 << 20;
+// Launch-size limits: batch is a grid dimension (at most 65535); query rows
+// B * T and query-head rows B * T * H stay below 2^30, so every launch size and
+// every row or unit index the kernels form fits an int.
+constexpr int kMaxBatch = 65535;
+constexpr int64_t kMaxRows = int64_t{1} << 30;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -31,6 +36,7 @@ dsa_status check_common(const dsa_shape* s)
     if (s->batch <= 0 || s->n_q <= 0 || s->max_kv <= 0) return DSA_ERR_SHAPE;
     if (s->n_q > s->max_kv) return DSA_ERR_SHAPE;
     if (s->max_kv > kMaxKv) return DSA_ERR_UNSUPPORTED;
+    if (s->batch > kMaxBatch || (int64_t)s->batch * s->n_q > kMaxRows) return DSA_ERR_UNSUPPORTED;
     return DSA_OK;
 }
 
@@ -57,6 +63,7 @@ dsa_status check_mla_shape(const dsa_shape* s)
     if (s->mla_dtype != DSA_F32 && s->mla_dtype != DSA_BF16 && s->mla_dtype != DSA_FP8_E4M3) return DSA_ERR_DTYPE;
     if (s->topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
     if (!dsa::mla_supported(s->mla_dtype, s->qk_dim, s->v_dim)) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)s->batch * s->n_q * s->heads > kMaxRows) return DSA_ERR_UNSUPPORTED;
     return DSA_OK;
 }
 
@@ -341,6 +348,7 @@ DSA_EXPORT const char* dsa_status_string(dsa_status st)
         case DSA_ERR_UNSUPPORTED: return "sizes valid but not supported by the built kernels";
         case DSA_ERR_HIP: return "HIP runtime error on launch";
         case DSA_ERR_SCRATCH: return "shape needs more than the library's static scratch (dsa_forward_noalloc)";
+        default: break;
     }
     return "unknown status";
 }

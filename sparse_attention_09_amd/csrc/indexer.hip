@@ -782,7 +782,7 @@ hipError_t launch_dt(const IndexerArgs& a, hipStream_t s)
         // per byte); 8 KB strips keep the window of rows in flight small (measured
         // best among 4, 8 and 16 KB)
         const int waves = DT == kFP8 ? 4096 : 2048;
-        const int per_seq = (waves + 4 * a.B - 1) / (4 * a.B);
+        const int per_seq = (int)((waves + 4LL * a.B - 1) / (4LL * a.B));
         if (a.t_count == 1) {
             constexpr int TPW = NCH >= 8 ? 1 : 8 / NCH;
             const int strips = (a.Lmax + TPW * 16 - 1) / (TPW * 16);

@@ -668,6 +668,63 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp)
     return base + incl - v;
 }
 
+// Threshold among the candidates of a row's threshold bin (keys ckey, positions
+// cidx, n_cand of them; the top 12 key bits are equal): the krem-th largest low
+// 20 bits tau_low (radix select on bits 19..10, then 9..0) and, among candidates
+// equal to it, the largest position that is still taken (iota; all of them:
+// 0xFFFFFFFF).  A candidate is taken iff its low bits exceed tau_low, or equal it
+// at a position <= iota.  Block-wide (every thread calls it); hist is 1024 words.
+__device__ __forceinline__ void resolve_candidates(const uint32_t* ckey, const int32_t* cidx, int n_cand, int krem,
+                                                   uint32_t* hist, uint32_t* scan_tmp, uint32_t* sel_digit,
+                                                   int* sel_above, uint32_t& tau_low, uint32_t& iota)
+{
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, pmask = 0;
+    int need = krem;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = pass == 0 ? 10 : 0;
+        for (int i = tid; i < 1024; i += kTopkThreads) hist[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < n_cand; i += kTopkThreads) {
+            const uint32_t k = ckey[i];
+            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 1023u], 1u);
+        }
+        __syncthreads();
+        block_find_desc<kTopkThreads>(hist, 1024, (uint32_t)need, scan_tmp, sel_digit, sel_above);
+        need -= *sel_above;
+        prefix |= *sel_digit << shift;
+        pmask |= 1023u << shift;
+        __syncthreads();
+    }
+    tau_low = prefix;  // low 20 bits of the threshold key
+    const int count_eq = (int)hist[tau_low & 1023u];
+    __syncthreads();  // every thread has read the histogram before it is cleared again
+    // among keys equal to the threshold, keep the `need` smallest positions
+    iota = 0xFFFFFFFFu;
+    if (need < count_eq) {
+        uint32_t ip = 0, im = 0;
+        int k2 = need;
+#pragma unroll 1
+        for (int pass = 0; pass < 2; ++pass) {
+            const int shift = pass == 0 ? 10 : 0;
+            for (int i = tid; i < 1024; i += kTopkThreads) hist[i] = 0;
+            __syncthreads();
+            for (int i = tid; i < n_cand; i += kTopkThreads) {
+                const uint32_t p = (uint32_t)cidx[i];
+                if ((ckey[i] & 0xFFFFFu) == tau_low && (p & im) == ip) atomicAdd(&hist[(p >> shift) & 1023u], 1u);
+            }
+            __syncthreads();
+            block_find_asc<kTopkThreads>(hist, 1024, (uint32_t)k2, scan_tmp, sel_digit, sel_above);
+            k2 -= *sel_above;
+            ip |= *sel_digit << shift;
+            im |= 1023u << shift;
+            __syncthreads();
+        }
+        iota = ip;
+    }
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_finish_kernel(TopkArgs a)
 {
     __shared__ TopkUnion u;
@@ -696,51 +753,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_finish_kernel(TopkArgs a)
         f.cidx[i] = (int32_t)c.y;
     }
     const int krem = K - n_sel;  // candidates to take, 1 <= krem <= n_cand
-    // radix select of the krem-th largest candidate key on bits 19..10 then 9..0
-    uint32_t prefix = 0, pmask = 0;
-    int need = krem;
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-        const int shift = pass == 0 ? 10 : 0;
-        for (int i = tid; i < 1024; i += kTopkThreads) f.hist[i] = 0;
-        __syncthreads();
-        for (int i = tid; i < n_cand; i += kTopkThreads) {
-            const uint32_t k = f.ckey[i];
-            if ((k & pmask) == prefix) atomicAdd(&f.hist[(k >> shift) & 1023u], 1u);
-        }
-        __syncthreads();
-        block_find_desc<kTopkThreads>(f.hist, 1024, (uint32_t)need, f.scan_tmp, &f.sel_digit, &f.sel_above);
-        need -= f.sel_above;
-        prefix |= f.sel_digit << shift;
-        pmask |= 1023u << shift;
-        __syncthreads();
-    }
-    const uint32_t tau_low = prefix;  // low 20 bits of the threshold key
-    const int count_eq = (int)f.hist[tau_low & 1023u];
-    __syncthreads();  // every thread has read the histogram before it is cleared again
-    // among keys equal to the threshold, keep the `need` smallest positions
-    uint32_t iota = 0xFFFFFFFFu;
-    if (need < count_eq) {
-        uint32_t ip = 0, im = 0;
-        int k2 = need;
-#pragma unroll 1
-        for (int pass = 0; pass < 2; ++pass) {
-            const int shift = pass == 0 ? 10 : 0;
-            for (int i = tid; i < 1024; i += kTopkThreads) f.hist[i] = 0;
-            __syncthreads();
-            for (int i = tid; i < n_cand; i += kTopkThreads) {
-                const uint32_t p = (uint32_t)f.cidx[i];
-                if ((f.ckey[i] & 0xFFFFFu) == tau_low && (p & im) == ip) atomicAdd(&f.hist[(p >> shift) & 1023u], 1u);
-            }
-            __syncthreads();
-            block_find_asc<kTopkThreads>(f.hist, 1024, (uint32_t)k2, f.scan_tmp, &f.sel_digit, &f.sel_above);
-            k2 -= f.sel_above;
-            ip |= f.sel_digit << shift;
-            im |= 1023u << shift;
-            __syncthreads();
-        }
-        iota = ip;
-    }
+    uint32_t tau_low, iota;
+    resolve_candidates(f.ckey, f.cidx, n_cand, krem, f.hist, f.scan_tmp, &f.sel_digit, &f.sel_above, tau_low, iota);
     // the chosen candidates go to `out` before the bitmap reuses the candidate space
     if (tid == 0) f.n_out = 0;
     __syncthreads();

@@ -240,12 +240,16 @@ def test_forward_is_deterministic_and_stateless(dsa):
 
 
 DECODE_SELECTION_CASES = [
-    # idx dtype, B, T, Lmax, lens, K, chunked workspace
-    ("bf16", 6, 1, 32768, [32768, 30000, 5000, 1, 0, 20000], 2048, False),
-    ("bf16", 4, 2, 20000, [20000, 15000, 3, 2], 512, False),
-    ("bf16", 3, 2, 16384, [16384, 9000, 2], 1024, True),
-    ("fp8", 4, 1, 40000, [40000, 1000, 39000, 7], 2048, False),
-    ("fp8", 3, 2, 16384, [16384, 9000, 2], 1024, True),
+    # idx dtype, B, T, Lmax, lens, K, chunked workspace, keys
+    ("bf16", 6, 1, 32768, [32768, 30000, 5000, 1, 0, 20000], 2048, False, "gauss"),
+    ("bf16", 4, 2, 20000, [20000, 15000, 3, 2], 512, False, "gauss"),
+    ("bf16", 3, 2, 16384, [16384, 9000, 2], 1024, True, "gauss"),
+    ("fp8", 4, 1, 40000, [40000, 1000, 39000, 7], 2048, False, "gauss"),
+    ("fp8", 3, 2, 16384, [16384, 9000, 2], 1024, True, "gauss"),
+    # every key of a sequence the same: one threshold bin holds the whole row
+    ("bf16", 2, 1, 12000, [12000, 5000], 2048, False, "equal"),
+    # a narrow band of scores: many keys in the threshold bin
+    ("bf16", 2, 1, 32768, [32768, 25000], 2048, False, "band"),
 ]
 
 
@@ -256,14 +260,19 @@ def test_forward_decode_selection_equals_stage_path(dsa, case):
     its selection must equal dsa_index_scores followed by dsa_topk bit for bit, for
     ragged, empty and shorter-than-K sequences, one or two queries per sequence, and a
     workspace small enough to run the queries one at a time."""
-    dt, B, T, Lmax, lens, K, chunked = case
+    dt, B, T, Lmax, lens, K, chunked, keys = case
     announce(f"forward decode selection == index_scores + topk {case}")
     H, D, heads, dqk, dv = 64, 128, 16, 192, 128
     s = dsa.DsaShape(batch=B, n_q=T, max_kv=Lmax, idx_heads=H, idx_dim=D, topk=K, heads=heads, qk_dim=dqk,
                      v_dim=dv, sm_scale=dqk ** -0.5, idx_dtype=dt, mla_dtype="bf16")
     g = torch.Generator().manual_seed(11 * Lmax + T)
     q_idx = torch.randn(B, T, H, D, generator=g).to(DEV, torch.bfloat16)
-    k_idx = torch.randn(B, Lmax, D, generator=g).to(DEV, torch.bfloat16)
+    k_idx = torch.randn(B, Lmax, D, generator=g)
+    if keys == "equal":
+        k_idx = k_idx[:, :1].expand(B, Lmax, D).contiguous()
+    elif keys == "band":
+        k_idx = k_idx[:, :1] + 1e-3 * k_idx
+    k_idx = k_idx.to(DEV, torch.bfloat16)
     w = torch.randn(B, T, H, generator=g).to(DEV)
     q = (torch.randn(B, T, heads, dqk, generator=g) * dqk ** -0.5).to(DEV, torch.bfloat16)
     kv = (torch.randn(B, Lmax, dqk, generator=g) * dqk ** -0.5).to(DEV, torch.bfloat16)

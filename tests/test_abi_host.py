@@ -216,6 +216,23 @@ def test_forward_workspace_sizes_and_checks(dsa):
     assert dsa.forward_workspace_size(bad) == 0
 
 
+def test_launch_size_limits(dsa):
+    """batch <= 65535, B * T <= 2^30 and B * T * H <= 2^30 keep every launch size and kernel
+    row index inside int; beyond them the host returns DSA_ERR_UNSUPPORTED (-6)."""
+    assert _call_scores(dsa, _shape(dsa, batch=65536, n_q=1)) == -6
+    assert _call_scores(dsa, _shape(dsa, batch=65535, n_q=20000, max_kv=20000)) == -6  # B*T > 2^30
+    assert dsa.forward_workspace_size(_shape(dsa, batch=65536, n_q=1)) == 0
+    # B*T*H beyond 2^30 with an MLA: 4096 x 256 queries x 2048 heads = 2^31
+    big = _shape(dsa, batch=4096, n_q=256, max_kv=256, heads=2048)
+    assert dsa.forward_workspace_size(big) == 0
+    assert dsa.sparse_mla_workspace_size(big) == 0
+    # the same query count with 128 heads is within the limits
+    assert dsa.forward_workspace_size(_shape(dsa, batch=4096, n_q=256, max_kv=256)) > 0
+    L = dsa.lib()
+    for st in (-2147483648, -100, -9, 1, 2147483647):  # any int32 is a valid status value
+        assert L.dsa_status_string(st) == b"unknown status"
+
+
 def test_index_topk_rejects_bad_arguments(dsa):
     L = dsa.lib()
     f = L.dsa_index_topk

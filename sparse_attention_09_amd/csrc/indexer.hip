@@ -133,6 +133,9 @@ __device__ __forceinline__ int seq_len(const IndexerArgs& a, int b)
 // Scores leave a strip four tiles at a time: lane (n, g) stores key n of tile
 // 4 j + g, so one store covers 64 consecutive keys.  The fp8 key scales are
 // loaded with the strip in that store layout, so no load waits behind it.
+// bf16 keys are read once per call, and their loads are marked non-temporal
+// (measured at 32K context and 64 sequences: 105.1 -> 102.0 us); the fp8 indexer
+// measured slower with the hint (60.0 -> 64.2 us at 128K) and loads as usual.
 template <int TPW> struct StripOut { static constexpr int n = (TPW + 3) / 4; };
 
 template <int DT, int D, int TPW>
@@ -148,7 +151,13 @@ __device__ __forceinline__ void load_strip(const IndexerArgs& a, int b, int stri
         const int key = min((strip * TPW + i) * 16 + n, kend - 1);
         const char* src = kbase + (size_t)key * D * EB;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) kb[i][c] = ld16(src + Share<DT, D>::off(g, c));
+        for (int c = 0; c < NCH; ++c) {
+            const void* p = src + Share<DT, D>::off(g, c);
+            if constexpr (DT == kBF16)
+                kb[i][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+            else
+                kb[i][c] = ld16(p);
+        }
     }
 #pragma unroll
     for (int j = 0; j < StripOut<TPW>::n; ++j) {

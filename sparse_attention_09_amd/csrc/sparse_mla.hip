@@ -157,13 +157,18 @@ __device__ __forceinline__ void gather_offsets(const uint32_t* lrow, int j0, int
     }
 }
 
-template <class C>
+// STREAM marks the load non-temporal: for rows that no other query of the call
+// reads (one query per sequence), so they do not displace cached data.
+template <class C, bool STREAM = false>
 __device__ __forceinline__ void gather_issue(const char* kvb, uint32_t off, u32x4* dst, int w, int k)
 {
     const int wu = __builtin_amdgcn_readfirstlane(w);
     const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(
         (__attribute__((address_space(3))) u32x4*)(dst + (wu + C::NW * k) * 64));
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(kvb), "{m0}"(lds) : "memory");
+    if constexpr (STREAM)
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(off), "s"(kvb), "{m0}"(lds) : "memory");
+    else
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(kvb), "{m0}"(lds) : "memory");
 }
 
 // Direct loads of wave w that touch the tile (the others would fill only the
@@ -177,7 +182,7 @@ __device__ __forceinline__ int tile_loads(int w)
 
 // SKIP_TAIL: leave out the loads that fill only the dummy tail; the caller's waits
 // then count tile_loads(w) loads per tile for wave w.
-template <class C, bool SKIP_TAIL = false>
+template <class C, bool SKIP_TAIL = false, bool STREAM = false>
 __device__ __forceinline__ void gather_tile_asm(const char* kvb, const uint32_t* lrow, int j0, int w, int lane,
                                                 u32x4* dst)
 {
@@ -186,7 +191,7 @@ __device__ __forceinline__ void gather_tile_asm(const char* kvb, const uint32_t*
     const int n = SKIP_TAIL ? tile_loads<C>(__builtin_amdgcn_readfirstlane(w)) : C::DMA;
 #pragma unroll
     for (int k = 0; k < C::DMA; ++k)
-        if (k < n) gather_issue<C>(kvb, off[k], dst, w, k);
+        if (k < n) gather_issue<C, STREAM>(kvb, off[k], dst, w, k);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads (whose vmcnt(0)
@@ -657,7 +662,7 @@ __device__ __forceinline__ void barrier_vm()
 // feeding the MFMAs go in groups of four steps, the next group's reads issued
 // before the current group's MFMAs, with a scheduling barrier between groups:
 // without it the compiler hoists every read of the tile and spills the queries.
-template <int DQK, int DV>
+template <int DQK, int DV, bool STREAM>
 __device__ __forceinline__ bool tile_compute_wide(const u32x4* tile, uint32_t vmask,
                                                   const u32x4 (&qb)[WideCfg<DQK, DV>::QS], WideState<DQK, DV>& st,
                                                   float zc, int lane, int w, PendingGather<WideCfg<DQK, DV>>& pg)
@@ -687,7 +692,7 @@ __device__ __forceinline__ bool tile_compute_wide(const u32x4* tile, uint32_t vm
                 mfma32_bf16_vacc(ka, qb[st_], sacc);
             if (st_ % GAP == 0 && st_ / GAP < C::DMA) goff = pg.next_offset();
             if (st_ % GAP == GAP - 1 && st_ / GAP < C::DMA && pg.active)
-                gather_issue<C>(pg.kvb, goff, pg.dst, w, st_ / GAP);
+                gather_issue<C, STREAM>(pg.kvb, goff, pg.dst, w, st_ / GAP);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -824,7 +829,7 @@ struct WideQStage {
     static constexpr int CH = C::NW * WAVE_CH;
 };
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool STREAM>
 __global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
 {
     using C = WideCfg<DQK, DV>;
@@ -940,8 +945,8 @@ __global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
 
 #pragma unroll 1
     for (;;) {
-        if (n_tiles > 0) gather_tile_asm<C>(kvb, lrow, 0, w, lane, tiles);
-        if (n_tiles > 1) gather_tile_asm<C>(kvb, lrow, kTileKeys, w, lane, tiles + C::BUF_CH);
+        if (n_tiles > 0) gather_tile_asm<C, false, STREAM>(kvb, lrow, 0, w, lane, tiles);
+        if (n_tiles > 1) gather_tile_asm<C, false, STREAM>(kvb, lrow, kTileKeys, w, lane, tiles + C::BUF_CH);
         int cur = 0;
 #pragma unroll 1
         for (int it = 0; it < n_tiles; ++it) {
@@ -961,7 +966,7 @@ __global__ __launch_bounds__(256) void mla_wide_kernel(MlaArgs a)
             pg.lrow = lrow + min(it + 2, n_tiles - 1) * kTileKeys;
             pg.active = it + 2 < n_tiles;
             pg.start(w, lane);
-            if (tile_compute_wide<DQK, DV>(tiles + cur * C::BUF_CH, vm, qb, st, zc, lane, w, pg) && lane == 0)
+            if (tile_compute_wide<DQK, DV, STREAM>(tiles + cur * C::BUF_CH, vm, qb, st, zc, lane, w, pg) && lane == 0)
                 restart[it & 1] = 1;
             cur = cur == 2 ? 0 : cur + 1;
         }
@@ -1763,7 +1768,14 @@ hipError_t launch_wide(const MlaArgs& a, hipStream_t s)
 {
     const int HB = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
     const long long units = (long long)a.B * a.t_count * a.n_split * HB;
-    mla_wide_kernel<DQK, DV><<<dim3((unsigned)(8 * ((units + 7) / 8))), 256, 0, s>>>(a);
+    // one query per sequence: every gathered row is read by one workgroup only, and
+    // non-temporal gathers measured faster (decode at 32K context: step 183.4 ->
+    // 179.0 us); prefill queries share rows through L2 (5.7% slower with the hint)
+    const dim3 grid((unsigned)(8 * ((units + 7) / 8)));
+    if (a.t_count == 1)
+        mla_wide_kernel<DQK, DV, true><<<grid, 256, 0, s>>>(a);
+    else
+        mla_wide_kernel<DQK, DV, false><<<grid, 256, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : launch_combine<kBF16, DV>(a, s);
 }

@@ -659,10 +659,11 @@ def box_ceilings(torch) -> dict:
     torch.cuda.empty_cache()
     mf = probe["results"]["32x32x16_random"]
     return {"hbm_read": {"achieved": probe["stream_read"]["GBs"], "unit": "GB/s",
-                         "how": "grid-stride 16-byte reads of 1 GiB (mfma_ceiling.hip)"},
+                         "how": "grid-stride 16-byte reads of 1 GiB, best of plain and non-temporal loads "
+                                "(mfma_ceiling.hip)"},
             "row_gather": {"achieved": probe["row_gather"]["GBs"], "unit": "GB/s",
                            "how": "random 1152-byte rows, 2048 of 32768 per sequence, 64 sequences, "
-                                  "best of register and direct-to-LDS loads (mfma_ceiling.hip)",
+                                  "best of register and direct-to-LDS, plain and non-temporal loads (mfma_ceiling.hip)",
                            "cases": probe["row_gather"]["cases"]},
             "bf16_mfma": {"achieved": mf["tflops"], "unit": "TFLOP/s",
                           "how": "back-to-back v_mfma_f32_32x32x16_bf16 on random operands (mfma_ceiling.hip)"},

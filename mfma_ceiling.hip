@@ -12,14 +12,15 @@
 // order) to measure how many other vector instructions an MFMA hides.  Only each
 // thread's final sum is stored.  The "stream_read" cases read 1 GiB with a
 // grid-stride loop of 16-byte loads (2048, 8192 or 32768 workgroups; 4 or 8 loads
-// in flight per thread) and store one sum per thread; the best of them is the plain
-// streaming ceiling that the HBM-bound kernels are held to.  The "row_gather" cases
+// in flight per thread; plain or non-temporal loads) and store one sum per thread;
+// the best of them is the streaming ceiling that the HBM-bound kernels are held to.  The "row_gather" cases
 // read what the decode sparse MLA reads: rows of 1152 bytes (576 bf16) picked at
 // random, without repetition, from each of 64 sequences of 32768 rows (a 2.4 GB
 // latent cache), 2048 rows per sequence, 32 rows per tile, one 256-thread
 // workgroup per (sequence, share of its rows), each 16-byte chunk loaded once,
 // either into registers (two tiles in flight) or straight into LDS
-// (global_load_lds_dwordx4, three tile buffers, two tiles in flight); three
+// (global_load_lds_dwordx4, three tile buffers, two tiles in flight), with plain
+// or non-temporal loads; three
 // different row sets are rotated so that no launch finds the previous one's rows
 // in the caches.  The best of them is the random-row gather ceiling.
 // Prints one JSON line.
@@ -180,8 +181,22 @@ __global__ __launch_bounds__(256, 2) void vmix32_kernel(const bf16x8* ops, float
 }
 
 // Sum of a 16-byte-aligned buffer of n4 float4 elements, U loads in flight per thread
-// per iteration; one partial sum per thread.
-template <int U>
+// per iteration (non-temporal loads when NT); one partial sum per thread.
+typedef float fv4 __attribute__((ext_vector_type(4)));
+typedef unsigned uv4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ float4 ld_f4(const float4* p)
+{
+    if constexpr (NT) {
+        const fv4 v = __builtin_nontemporal_load(reinterpret_cast<const fv4*>(p));
+        return make_float4(v.x, v.y, v.z, v.w);
+    } else {
+        return *p;
+    }
+}
+
+template <int U, bool NT>
 __global__ __launch_bounds__(256) void stream_read_kernel(const float4* p, size_t n4, float* out)
 {
     const size_t stride = (size_t)gridDim.x * 256;
@@ -190,12 +205,12 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const float4* p, size_
     for (; i + (U - 1) * stride < n4; i += U * stride) {
         float4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = p[i + u * stride];
+        for (int u = 0; u < U; ++u) v[u] = ld_f4<NT>(p + i + u * stride);
 #pragma unroll
         for (int u = 0; u < U; ++u) acc += (v[u].x + v[u].y) + (v[u].z + v[u].w);
     }
     for (; i < n4; i += stride) {
-        const float4 a = p[i];
+        const float4 a = ld_f4<NT>(p + i);
         acc += a.x + a.y + a.z + a.w;
     }
     out[blockIdx.x * 256 + threadIdx.x] = acc;
@@ -209,6 +224,7 @@ constexpr int kGSeq = 64, kGRows = 32768, kGSel = 2048, kGRowB = 1152, kGCh = kG
 constexpr int kGTile = 32, kGTileCh = kGTile * kGCh, kGLoads = kGTileCh / 256;
 static_assert(kGTileCh % 256 == 0, "tile chunks");
 
+template <bool NT>
 __global__ __launch_bounds__(256) void gather_reg_kernel(const char* cache, const int* rows, int nsplit,
                                                          unsigned* out)
 {
@@ -224,7 +240,13 @@ __global__ __launch_bounds__(256) void gather_reg_kernel(const char* cache, cons
 #pragma unroll
         for (int k = 0; k < kGLoads; ++k) {
             const int c = threadIdx.x + 256 * k;
-            d[k] = *reinterpret_cast<const uint4*>(base + roff[t * kGTile + c / kGCh] + (c % kGCh) * 16);
+            const uint4* src = reinterpret_cast<const uint4*>(base + roff[t * kGTile + c / kGCh] + (c % kGCh) * 16);
+            if constexpr (NT) {
+                const uv4 v = __builtin_nontemporal_load(reinterpret_cast<const uv4*>(src));
+                d[k] = make_uint4(v.x, v.y, v.z, v.w);
+            } else {
+                d[k] = *src;
+            }
         }
     };
     load(cur, 0);
@@ -239,6 +261,7 @@ __global__ __launch_bounds__(256) void gather_reg_kernel(const char* cache, cons
     out[blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+template <bool NT>
 __global__ __launch_bounds__(256) void gather_lds_kernel(const char* cache, const int* rows, int nsplit,
                                                          unsigned* out)
 {
@@ -258,7 +281,10 @@ __global__ __launch_bounds__(256) void gather_lds_kernel(const char* cache, cons
             const unsigned off = roff[t * kGTile + c / kGCh] + (c % kGCh) * 16;
             const unsigned lds = (unsigned)reinterpret_cast<uintptr_t>(
                 (__attribute__((address_space(3))) uint4*)(dst + wave * 64 + 256 * k));
-            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+            if constexpr (NT)
+                asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+            else
+                asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
         }
     };
     unsigned acc = 0;
@@ -356,12 +382,14 @@ int main()
     double best = 0.0;
     printf("}, \"stream_read\": {\"bytes\": %zu, \"cases\": {", n4 * sizeof(float4));
     for (int gi = 0; gi < 3; ++gi)
-        for (int uu = 0; uu < 2; ++uu) {
+        for (int uu = 0; uu < 4; ++uu) {  // bit 0: 8 loads in flight instead of 4; bit 1: non-temporal
             auto launch = [&]() {
-                if (uu == 0)
-                    stream_read_kernel<4><<<grids[gi], 256>>>(big, n4, sums);
-                else
-                    stream_read_kernel<8><<<grids[gi], 256>>>(big, n4, sums);
+                switch (uu) {
+                case 0: stream_read_kernel<4, false><<<grids[gi], 256>>>(big, n4, sums); break;
+                case 1: stream_read_kernel<8, false><<<grids[gi], 256>>>(big, n4, sums); break;
+                case 2: stream_read_kernel<4, true><<<grids[gi], 256>>>(big, n4, sums); break;
+                default: stream_read_kernel<8, true><<<grids[gi], 256>>>(big, n4, sums); break;
+                }
             };
             launch();  // warm-up launch
             CHECK(hipDeviceSynchronize());
@@ -374,8 +402,8 @@ int main()
             ms /= 10;
             const double gbs = n4 * sizeof(float4) / (ms * 1e-3) / 1e9;
             best = gbs > best ? gbs : best;
-            printf("%s\"grid%d_u%d\": {\"ms\": %.4f, \"GBs\": %.1f}", gi + uu ? ", " : "", grids[gi], uu ? 8 : 4,
-                   ms, gbs);
+            printf("%s\"grid%d_u%d%s\": {\"ms\": %.4f, \"GBs\": %.1f}", gi + uu ? ", " : "", grids[gi],
+                   (uu & 1) ? 8 : 4, (uu & 2) ? "_nt" : "", ms, gbs);
         }
     printf("}, \"GBs\": %.1f}", best);
     CHECK(hipFree(sums));
@@ -406,15 +434,17 @@ int main()
     const int splits[2] = {4, 16};
     double gbest = 0.0;
     printf(", \"row_gather\": {\"bytes\": %.0f, \"row_bytes\": %d, \"cases\": {", gbytes, kGRowB);
-    for (int path = 0; path < 2; ++path)
+    for (int path = 0; path < 4; ++path)  // bit 0: straight into LDS; bit 1: non-temporal
         for (int si = 0; si < 2; ++si) {
             const int ns = splits[si];
             auto launch = [&](int set) {
                 const int* rs = rowsets + (size_t)set * kGSeq * kGSel;
-                if (path == 0)
-                    gather_reg_kernel<<<kGSeq * ns, 256>>>(cache, rs, ns, gout);
-                else
-                    gather_lds_kernel<<<kGSeq * ns, 256>>>(cache, rs, ns, gout);
+                switch (path) {
+                case 0: gather_reg_kernel<false><<<kGSeq * ns, 256>>>(cache, rs, ns, gout); break;
+                case 1: gather_lds_kernel<false><<<kGSeq * ns, 256>>>(cache, rs, ns, gout); break;
+                case 2: gather_reg_kernel<true><<<kGSeq * ns, 256>>>(cache, rs, ns, gout); break;
+                default: gather_lds_kernel<true><<<kGSeq * ns, 256>>>(cache, rs, ns, gout); break;
+                }
             };
             launch(0);  // warm-up launch
             CHECK(hipDeviceSynchronize());
@@ -428,8 +458,8 @@ int main()
             ms /= reps;
             const double gbs = gbytes / (ms * 1e-3) / 1e9;
             gbest = gbs > gbest ? gbs : gbest;
-            printf("%s\"%s_%dblocks\": {\"us\": %.2f, \"GBs\": %.1f}", path + si ? ", " : "",
-                   path ? "lds" : "registers", kGSeq * ns, ms * 1e3, gbs);
+            printf("%s\"%s%s_%dblocks\": {\"us\": %.2f, \"GBs\": %.1f}", path + si ? ", " : "",
+                   (path & 1) ? "lds" : "registers", (path & 2) ? "_nt" : "", kGSeq * ns, ms * 1e3, gbs);
         }
     printf("}, \"GBs\": %.1f}}\n", gbest);
     CHECK(hipFree(gout));

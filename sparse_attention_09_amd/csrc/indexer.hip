@@ -133,9 +133,9 @@ __device__ __forceinline__ int seq_len(const IndexerArgs& a, int b)
 // Scores leave a strip four tiles at a time: lane (n, g) stores key n of tile
 // 4 j + g, so one store covers 64 consecutive keys.  The fp8 key scales are
 // loaded with the strip in that store layout, so no load waits behind it.
-// bf16 keys are read once per call, and their loads are marked non-temporal
-// (measured at 32K context and 64 sequences: 105.1 -> 102.0 us); the fp8 indexer
-// measured slower with the hint (60.0 -> 64.2 us at 128K) and loads as usual.
+// Keys are read once per call, and bf16 and fp8 key loads are marked
+// non-temporal (whole decode steps, measured: 32K context, 64 sequences, bf16
+// 191.2 -> 183.4 us; 128K context, 16 sequences, fp8 at 3072 waves 120.4 -> 118.5 us).
 template <int TPW> struct StripOut { static constexpr int n = (TPW + 3) / 4; };
 
 template <int DT, int D, int TPW>
@@ -153,7 +153,7 @@ __device__ __forceinline__ void load_strip(const IndexerArgs& a, int b, int stri
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const void* p = src + Share<DT, D>::off(g, c);
-            if constexpr (DT == kBF16)
+            if constexpr (DT == kBF16 || DT == kFP8)
                 kb[i][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
             else
                 kb[i][c] = ld16(p);
@@ -786,11 +786,11 @@ hipError_t launch_dt(const IndexerArgs& a, hipStream_t s)
     if (a.t_count <= 0 || a.B <= 0) return hipSuccess;
     if (a.t_count <= 2) {
         constexpr int NCH = Share<DT, D>::nch;
-        // about 2048 persistent waves over the grid for bf16 keys, 4096 for fp8
-        // (measured: 1024-8192 waves; fp8 64-key strips carry twice the products
-        // per byte); 8 KB strips keep the window of rows in flight small (measured
-        // best among 4, 8 and 16 KB)
-        const int waves = DT == kFP8 ? 4096 : 2048;
+        // about 2048 persistent waves over the grid for bf16 keys, 3072 for fp8
+        // (measured with non-temporal key loads: bf16 1536-4096, fp8 2048-4096
+        // waves; fp8 64-key strips carry twice the products per byte); 8 KB strips
+        // keep the window of rows in flight small (measured best among 4, 8 and 16 KB)
+        const int waves = DT == kFP8 ? 3072 : 2048;
         const int per_seq = (int)((waves + 4LL * a.B - 1) / (4LL * a.B));
         if (a.t_count == 1) {
             constexpr int TPW = NCH >= 8 ? 1 : 8 / NCH;

@@ -52,6 +52,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // 16-byte global load / store through plain vector accesses.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// The same with the non-temporal hint, for data that one access reads or writes once.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p)); }
 
 // Raw buffer accesses (no stride) through a descriptor whose record count bounds
 // them: a load at or past the end returns zero, a store there is dropped, with no

@@ -357,7 +357,8 @@ __device__ __forceinline__ void mla_write_rows(const MlaArgs& a, const Bf16State
 // writes) and the whole block then leaves in 1 KiB stores.  The caller's lane holds
 // value dims d0 + 32*v + 8*i + 4*kb + jj (register 4*i + jj) of staging row `srow`
 // (head hb * 128 + srow); `ml` marks the one lane per row that writes m and l;
-// `l_tot` is the row's softmax sum.
+// `l_tot` is the row's softmax sum.  The block is written once (and partials read
+// once, by the combine), so the stores carry the non-temporal hint.
 template <int DV, int VT, int NT>
 __device__ __forceinline__ void mla_write_rows_staged(const MlaArgs& a, const f32x16 (&o)[VT], float m_run,
                                                       float l_tot, size_t row, int rq, int split, int hb, int srow,
@@ -386,7 +387,7 @@ __device__ __forceinline__ void mla_write_rows_staged(const MlaArgs& a, const f3
     const int n = heads_here * rch;
     for (int c = tid; c < n; c += NT) {
         const int r = c / rch, k = c - r * rch;
-        st16(gbase + 16 * (size_t)c, *reinterpret_cast<const u32x4*>(stage + r * SP + 16 * k));
+        st16_nt(gbase + 16 * (size_t)c, *reinterpret_cast<const u32x4*>(stage + r * SP + 16 * k));
     }
 }
 

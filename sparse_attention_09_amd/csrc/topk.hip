@@ -601,7 +601,8 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a)
     // past the chunk are clamped to its last key and ignored)
     uint32_t key[kFilterPer];
 #pragma unroll
-    for (int j = 0; j < kFilterPer; ++j) key[j] = float_key(src[min(c0 + tid + 256 * j, c1 - 1)]);
+    for (int j = 0; j < kFilterPer; ++j)  // the last read of these scores: non-temporal
+        key[j] = float_key(__builtin_nontemporal_load(src + min(c0 + tid + 256 * j, c1 - 1)));
     // the bin d1 of the K-th largest key: coarse bin first (64 words), then its 64 fine bins
     if (wave == 0) {
         int cb, fb;
